@@ -1,0 +1,226 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module holds no attention arithmetic: it only draws random numbers,
+rounds them to the storage dtype, and decodes stored values back to float64
+exactly.  The oracle and the GPU path both consume what it produces.
+
+Every tensor comes from ``numpy.random.default_rng(SeedSequence([seed, cfg,
+tensor_id]))`` with tensor ids q=0, k=1, v=2, lengths=3, forced index=4,
+sampled rows=5, so a workload is reproducible on any machine with no torch
+RNG involved.  Values are drawn in float32 and rounded to the storage dtype
+with round-to-nearest-even (bf16 rounding is done on the bit pattern).
+
+Workloads (each stands in for a workload printed on the pages):
+
+1. tiny      -- the 2x3x8 ``torch.randn`` example of the PyTorch SDPA tutorial
+                ("Fused implementations" section): B=2, H=1, N=3, d=8, f32.
+2. noncausal -- the tutorial's dispatcher benchmark ("Explicit dispatcher
+                control"): B=32, H=32, N=1024, d=32, f16, ``torch.rand``.
+3. causal    -- the attention core of the tutorial's CausalSelfAttention
+                module (embed 512, 8 heads, head dim 64) with causal masking
+                switched on: B=32, H=8, N=1024, d=64, f16, N(0,1).
+4. varlen    -- the NestedTensor batch recipe ("NestedTensor and dense tensor
+                support"): 32 sequences of length int(512*(1-g)), g~N(0.5,
+                0.01), one random entry forced to 512; H=8, d=64, f16, packed.
+5. long      -- the 64k-token regime of the FlashAttention article's
+                benchmark paragraph on one GPU: B=1, H=16, N=65536, d=64,
+                bf16, causal; checked on 256 sampled query rows per head.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+# tensor ids for SeedSequence
+_TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS = 0, 1, 2, 3, 4, 5
+
+# largest float16 strictly below 1.0; uniform draws are clamped here so that
+# rounding to f16 never produces 1.0 (the pages' torch.rand is [0, 1)).
+_F16_BELOW_ONE = np.float32(0.99951171875)
+
+DTYPES = ("f16", "bf16", "f32")
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even.
+
+    Inputs must be finite (the generator never produces NaN/Inf)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = (bits + 0x7FFF + lsb) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns to float64."""
+    u32 = (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the storage dtype.
+
+    Returns float32 / float16 arrays, or uint16 bit patterns for bf16."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(x32.astype(np.float16))
+    if dtype == "bf16":
+        return round_to_bf16_bits(x32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def storage_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of stored values to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(a)
+    return np.asarray(a).astype(np.float64)
+
+
+def _rng(seed: int, cfg: int, tid: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(seed), int(cfg), int(tid)]))
+
+
+def _draw(rng: np.random.Generator, shape, dist: str) -> np.ndarray:
+    if dist == "normal":
+        return rng.standard_normal(size=shape, dtype=np.float32)
+    if dist == "uniform":
+        u = rng.random(size=shape, dtype=np.float32)
+        return np.minimum(u, _F16_BELOW_ONE)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+@dataclasses.dataclass
+class Workload:
+    """One seeded problem instance.
+
+    Dense: q [B,H,Nq,d], k/v [B,H,Nk,d].  Varlen (cu_seqlens set): q/k/v
+    packed [T,H,d] with sequence s in rows cu_seqlens[s]:cu_seqlens[s+1].
+    ``q``/``k``/``v`` hold the stored values (f32/f16 arrays, or uint16 bf16
+    bit patterns); ``q64`` etc. are their exact float64 values."""
+
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    is_causal: bool
+    scale: np.float32
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_seqlens: Optional[np.ndarray] = None
+    rows: Optional[np.ndarray] = None  # sampled query rows (dense only)
+
+    @property
+    def varlen(self) -> bool:
+        return self.cu_seqlens is not None
+
+    @property
+    def q64(self) -> np.ndarray:
+        return storage_to_f64(self.q, self.dtype)
+
+    @property
+    def k64(self) -> np.ndarray:
+        return storage_to_f64(self.k, self.dtype)
+
+    @property
+    def v64(self) -> np.ndarray:
+        return storage_to_f64(self.v, self.dtype)
+
+    def flops(self) -> float:
+        """Metric FLOPs: 4*B*H*Nq*Nk*d, halved when causal; varlen sums
+        4*H*len^2*d over sequences (halved when causal)."""
+        if self.varlen:
+            lens = np.diff(self.cu_seqlens.astype(np.int64))
+            f = float(np.sum(4.0 * self.H * lens.astype(np.float64) ** 2 * self.d))
+        else:
+            f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.d
+        return f / 2 if self.is_causal else f
+
+
+def default_scale(d: int) -> np.float32:
+    return np.float32(1.0 / math.sqrt(d))
+
+
+def make_dense(B, H, Nq, Nk, d, dtype="f16", dist="normal", is_causal=False,
+               seed=0, cfg=0, scale=None, name="dense") -> Workload:
+    q32 = _draw(_rng(seed, cfg, _TID_Q), (B, H, Nq, d), dist)
+    k32 = _draw(_rng(seed, cfg, _TID_K), (B, H, Nk, d), dist)
+    v32 = _draw(_rng(seed, cfg, _TID_V), (B, H, Nk, d), dist)
+    sc = default_scale(d) if scale is None else np.float32(scale)
+    return Workload(name=name, dtype=dtype, B=B, H=H, Nq=Nq, Nk=Nk, d=d,
+                    is_causal=is_causal, scale=sc,
+                    q=to_storage(q32, dtype), k=to_storage(k32, dtype),
+                    v=to_storage(v32, dtype))
+
+
+def nested_lengths(batch: int, max_len: int, pad_fraction: float, seed=0, cfg=4) -> np.ndarray:
+    """The NestedTensor batch recipe: len_i = int(max_len*(1-g_i)) with
+    g_i ~ N(pad_fraction, 0.01), then one uniformly chosen entry is set to
+    max_len.  Lengths are clamped to [1, max_len]."""
+    g = _rng(seed, cfg, _TID_LEN).normal(loc=pad_fraction, scale=0.01, size=batch)
+    lens = np.array([int(max_len * (1.0 - gi)) for gi in g], dtype=np.int64)
+    forced = int(_rng(seed, cfg, _TID_FORCE).integers(0, batch))
+    lens[forced] = max_len
+    return np.clip(lens, 1, max_len)
+
+
+def cu_seqlens_from_lengths(lens) -> np.ndarray:
+    lens = np.asarray(lens, dtype=np.int64)
+    cu = np.zeros(len(lens) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lens)
+    assert cu[-1] < 2 ** 31
+    return cu.astype(np.int32)
+
+
+def make_varlen(lens, H, d, dtype="f16", dist="normal", is_causal=False, seed=0,
+                cfg=0, scale=None, name="varlen") -> Workload:
+    lens = np.asarray(lens, dtype=np.int64)
+    cu = cu_seqlens_from_lengths(lens)
+    T = int(cu[-1])
+    q32 = _draw(_rng(seed, cfg, _TID_Q), (T, H, d), dist)
+    k32 = _draw(_rng(seed, cfg, _TID_K), (T, H, d), dist)
+    v32 = _draw(_rng(seed, cfg, _TID_V), (T, H, d), dist)
+    sc = default_scale(d) if scale is None else np.float32(scale)
+    mx = int(lens.max()) if len(lens) else 0
+    return Workload(name=name, dtype=dtype, B=len(lens), H=H, Nq=mx, Nk=mx, d=d,
+                    is_causal=is_causal, scale=sc,
+                    q=to_storage(q32, dtype), k=to_storage(k32, dtype),
+                    v=to_storage(v32, dtype), cu_seqlens=cu)
+
+
+def sample_rows(n: int, count: int, seed=0, cfg=5) -> np.ndarray:
+    """``count`` distinct query rows of [0, n), sorted."""
+    rng = _rng(seed, cfg, _TID_ROWS)
+    return np.sort(rng.choice(n, size=min(count, n), replace=False)).astype(np.int64)
+
+
+CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long"}
+
+
+def make_config(i: int, seed: int = 0) -> Workload:
+    """The five workloads (see module docstring)."""
+    if i == 1:
+        return make_dense(2, 1, 3, 3, 8, "f32", "normal", False, seed, 1, name="tiny")
+    if i == 2:
+        return make_dense(32, 32, 1024, 1024, 32, "f16", "uniform", False, seed, 2,
+                          name="noncausal")
+    if i == 3:
+        return make_dense(32, 8, 1024, 1024, 64, "f16", "normal", True, seed, 3,
+                          name="causal")
+    if i == 4:
+        lens = nested_lengths(32, 512, 0.5, seed, 4)
+        return make_varlen(lens, 8, 64, "f16", "normal", False, seed, 4, name="varlen")
+    if i == 5:
+        w = make_dense(1, 16, 65536, 65536, 64, "bf16", "normal", True, seed, 5,
+                       name="long")
+        w.rows = sample_rows(65536, 256, seed, 5)
+        return w
+    raise ValueError(f"no config {i}")
