@@ -1,0 +1,40 @@
+"""ctypes loader for libsdpa.so (the gfx950 HIP library with the C ABI of
+include/sdpa.h).  There is no fallback: if the library is missing, every
+entry point raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so")
+
+SDPA_F16, SDPA_BF16, SDPA_F32, SDPA_SAME = 0, 1, 2, 255
+SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVICE = range(5)
+
+# every symbol include/sdpa.h declares
+EXPORTS = ("sdpa_fwd", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m exact_attention_sdpa_amd.build` "
+            "(the HIP library is required, there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    L.sdpa_fwd.restype = ctypes.c_int
+    L.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                           ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_supports.restype = ctypes.c_int
+    L.sdpa_supports.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
+    L.sdpa_status_str.restype = ctypes.c_char_p
+    L.sdpa_status_str.argtypes = [ctypes.c_int]
+    L.sdpa_abi_version.restype = ctypes.c_int
+    L.sdpa_abi_version.argtypes = []
+    _lib = L
+    return L

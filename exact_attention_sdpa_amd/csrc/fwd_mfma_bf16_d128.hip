@@ -1,0 +1,6 @@
+// Instantiations of the matrix-core forward: bf16 inputs, head dim 128.
+#include "fwd_mfma_launch.h"
+
+namespace sdpa {
+template hipError_t launch_mfma_d<true, 128>(const FwdArgs&);
+}  // namespace sdpa

@@ -1,0 +1,67 @@
+// C-ABI entry points: validation, device check, kernel selection, launch.
+#include <atomic>
+#include <cstring>
+
+#include "sdpa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// per device: 0 = not yet checked, 1 = gfx950, 2 = anything else
+std::atomic<int> g_arch[kMaxDevices];
+
+bool current_device_is_gfx950() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  int st = g_arch[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
+                     sdpa_dtype out_dtype, void* stream) {
+  sdpa::FwdArgs a;
+  const sdpa_status st = sdpa::validate(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal,
+                                        cu_seqlens, dtype, out_dtype, stream, &a);
+  if (st != SDPA_OK) return st;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  hipError_t e;
+  switch (dtype) {
+    case SDPA_F16: e = sdpa::launch_fwd_mfma_f16(a); break;
+    case SDPA_BF16: e = sdpa::launch_fwd_mfma_bf16(a); break;
+    default: e = sdpa::launch_fwd_f32(a); break;
+  }
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+int sdpa_supports(sdpa_dtype dtype, int64_t d, int is_causal, int varlen) {
+  (void)is_causal;
+  (void)varlen;
+  return sdpa::path_for(dtype, d);
+}
+
+const char* sdpa_status_str(sdpa_status s) {
+  switch (s) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_INVALID: return "invalid argument";
+    case SDPA_ERR_UNSUPPORTED: return "not supported";
+    case SDPA_ERR_LAUNCH: return "kernel launch failed";
+    case SDPA_ERR_DEVICE: return "current device is not gfx950";
+  }
+  return "unknown status";
+}
+
+int sdpa_abi_version(void) { return SDPA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sdpa.h"
+
+namespace sdpa {
+
+// Validated arguments of one forward call.  Sizes are already checked to be
+// positive and small enough for the kernels' int32 tile arithmetic.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;               // may be null
+  const int32_t* cu;        // null for dense
+  int64_t B, H, Nq, Nk, d;  // packed: Nq == Nk == max sequence length
+  float scale;
+  bool causal;
+  bool out_f32;             // out element type is f32 (else the input type)
+  sdpa_dtype dtype;         // SDPA_F16, SDPA_BF16 or SDPA_F32
+  hipStream_t stream;       // null = the null stream
+};
+
+// Host-only argument checks (no HIP calls).  Fills `a` on success.
+sdpa_status validate(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
+                     sdpa_dtype out_dtype, void* stream, FwdArgs* a);
+
+// 1 = matrix-core path, 0 = plain f32 path, -1 = unsupported.
+int path_for(sdpa_dtype dtype, int64_t d);
+
+// Kernel launchers: queue the kernel on a.stream and return the launch status.
+hipError_t launch_fwd_mfma_f16(const FwdArgs& a);
+hipError_t launch_fwd_mfma_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+
+}  // namespace sdpa

@@ -1,0 +1,107 @@
+// Host-side argument checks of sdpa_fwd.  Makes no HIP calls, so every
+// error path can be exercised without a GPU.
+#include <cmath>
+#include <cstdint>
+
+#include "sdpa_internal.h"
+
+namespace sdpa {
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int elem_bytes(sdpa_dtype t) { return t == SDPA_F32 ? 4 : 2; }
+
+}  // namespace
+
+int path_for(sdpa_dtype dtype, int64_t d) {
+  if (dtype == SDPA_F16 || dtype == SDPA_BF16) return (d == 32 || d == 64 || d == 128) ? 1 : -1;
+  if (dtype == SDPA_F32) return (d >= 1 && d <= 128) ? 0 : -1;
+  return -1;
+}
+
+sdpa_status validate(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                     int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
+                     sdpa_dtype out_dtype, void* stream, FwdArgs* a) {
+  if (!q || !k || !v || !out) return SDPA_ERR_INVALID;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return SDPA_ERR_INVALID;
+  if (is_causal != 0 && is_causal != 1) return SDPA_ERR_INVALID;
+  if (dtype != SDPA_F16 && dtype != SDPA_BF16 && dtype != SDPA_F32) return SDPA_ERR_INVALID;
+  if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen && Nq != Nk) return SDPA_ERR_INVALID;
+
+  // sizes must fit the kernels' int32 row and tile arithmetic
+  const int64_t lim = (int64_t)1 << 30;
+  if (H > lim || Nq > lim || Nk > lim || B > lim) return SDPA_ERR_INVALID;
+  int64_t rows_q, rows_k, eq, ek, tmp;
+  if (!mul_ok(B, H, &tmp) || !mul_ok(tmp, Nq, &rows_q) || !mul_ok(tmp, Nk, &rows_k) ||
+      !mul_ok(rows_q, d, &eq) || !mul_ok(rows_k, d, &ek) || eq > INT64_MAX / 4 ||
+      ek > INT64_MAX / 4)
+    return SDPA_ERR_INVALID;
+  // one workgroup per (batch, head, 32-row block) at most
+  if (tmp * ((Nq + 31) / 32) > INT32_MAX) return SDPA_ERR_INVALID;
+
+  bool out_f32;
+  if (out_dtype == SDPA_SAME || out_dtype == dtype)
+    out_f32 = dtype == SDPA_F32;
+  else if (out_dtype == SDPA_F32)
+    out_f32 = true;
+  else if (out_dtype == SDPA_F16 || out_dtype == SDPA_BF16)
+    return SDPA_ERR_UNSUPPORTED;
+  else
+    return SDPA_ERR_INVALID;
+
+  const int path = path_for(dtype, d);
+  if (path < 0) return SDPA_ERR_UNSUPPORTED;
+  if (scale < 0.f) return SDPA_ERR_UNSUPPORTED;
+
+  const uintptr_t al = path == 1 ? 16 : 4;
+  if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(out, al))
+    return SDPA_ERR_INVALID;
+  if (lse && !aligned(lse, 4)) return SDPA_ERR_INVALID;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return SDPA_ERR_INVALID;
+
+  if (!varlen) {
+    const int64_t ib = elem_bytes(dtype), ob = out_f32 ? 4 : elem_bytes(dtype);
+    const int64_t obytes = eq * ob;
+    if (overlap(out, obytes, q, eq * ib) || overlap(out, obytes, k, ek * ib) ||
+        overlap(out, obytes, v, ek * ib))
+      return SDPA_ERR_INVALID;
+    if (lse && overlap(out, obytes, lse, rows_q * 4)) return SDPA_ERR_INVALID;
+  }
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->out = out;
+  a->lse = lse;
+  a->cu = cu_seqlens;
+  a->B = B;
+  a->H = H;
+  a->Nq = Nq;
+  a->Nk = Nk;
+  a->d = d;
+  a->scale = scale;
+  a->causal = is_causal != 0;
+  a->out_f32 = out_f32;
+  a->dtype = dtype;
+  a->stream = static_cast<hipStream_t>(stream);
+  return SDPA_OK;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,133 @@
+/*
+ * sdpa.h -- C ABI of the fused, exact scaled dot-product attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every (batch, head) -- or (sequence, head) of a
+ * packed variable-length batch -- and every query row i:
+ *
+ *     s_ij  = scale * <q_i, k_j>                  for j in A_i
+ *     out_i = sum_j softmax_j(s_i.) * v_j
+ *     lse_i = ln sum_{j in A_i} exp(s_ij)
+ *
+ * with A_i = every key, or the keys j <= i when is_causal is set (a
+ * lower-triangular mask aligned at the top-left corner).  This is the
+ * scaled dot-product attention of the PyTorch SDPA tutorial ("Overview";
+ * the example calls in "Fused implementations" and the CausalSelfAttention
+ * block under "Causal self-attention"), computed the FlashAttention way:
+ * tile by tile with a running softmax, so that the N x N score matrix is
+ * never written to device memory (FlashAttention article, method
+ * paragraph and its tiling figure).  The result is exact attention up to
+ * floating-point rounding; there is no approximation.
+ *
+ * Ownership and side effects.  The caller owns every buffer.  The library
+ * never allocates, frees or synchronises, keeps no state between calls and
+ * may be called concurrently from several host threads.  Work is queued on
+ * `stream`; faults during kernel execution surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SDPA_API __attribute__((visibility("default")))
+#else
+#define SDPA_API
+#endif
+
+/* Element types.  SDPA_SAME is only valid as an output type and means
+ * "the input type". */
+typedef enum {
+  SDPA_F16 = 0,
+  SDPA_BF16 = 1,
+  SDPA_F32 = 2,
+  SDPA_SAME = 255
+} sdpa_dtype;
+
+/* Status codes.  Mirrors the tutorial's convention that an unsupported
+ * input raises an error instead of computing ("Explicit dispatcher
+ * control": a backend that cannot serve the input reports "not
+ * supported"). */
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID = 1,     /* malformed arguments (see sdpa_fwd)          */
+  SDPA_ERR_UNSUPPORTED = 2, /* well-formed but outside what is implemented */
+  SDPA_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch          */
+  SDPA_ERR_DEVICE = 4       /* no usable gfx950 device is current          */
+} sdpa_status;
+
+/*
+ * sdpa_fwd -- one attention forward, queued on `stream`.
+ *
+ * q, k, v   device pointers, element type `dtype`.
+ *           Dense (cu_seqlens == NULL): q is [B, H, Nq, d], k and v are
+ *           [B, H, Nk, d], all contiguous row-major.
+ *           Packed (cu_seqlens != NULL): q, k, v are [T, H, d] contiguous,
+ *           where sequence s owns rows cu_seqlens[s] .. cu_seqlens[s+1]-1
+ *           and attends only to itself (the tutorial's NestedTensor batches,
+ *           "NestedTensor and dense tensor support"); T = cu_seqlens[B].
+ * out       device pointer, element type out_dtype (SDPA_SAME -> dtype),
+ *           same shape as q.  Must not overlap q, k, v or lse.
+ * lse       device pointer to float, or NULL to skip.  Natural-log
+ *           logsumexp of the scaled, masked scores of each query row:
+ *           [B, H, Nq] dense, [T, H] packed (the output's shape without d).
+ * B, H      batch (number of sequences when packed) and heads, >= 1.
+ * Nq, Nk    query and key rows per (batch, head), >= 1.  Packed: both must
+ *           equal max_s(len_s); used only to size the launch grid.
+ * d         head dimension, >= 1.
+ * scale     multiplier of <q_i, k_j>; finite and >= 0 (1/sqrt(d) is the
+ *           usual choice).
+ * is_causal 0 or 1.
+ * cu_seqlens device pointer to B+1 int32 offsets, or NULL for dense.  The
+ *           caller guarantees cu_seqlens[0] = 0, non-decreasing entries and
+ *           every length <= Nq; the library cannot check device memory.
+ *           Zero-length sequences are allowed and write nothing.
+ * dtype     SDPA_F16, SDPA_BF16 or SDPA_F32.
+ * out_dtype SDPA_SAME or SDPA_F32.
+ * stream    hipStream_t, or NULL for the null stream.
+ *
+ * Supported: f16 and bf16 with d in {32, 64, 128}; f32 with 1 <= d <= 128.
+ * For bf16 inputs the P.V product runs on the f16 matrix cores with V
+ * converted to f16, which requires |v| <= 65504 (larger values overflow).
+ *
+ * Alignment: q, k, v and out must be 16-byte aligned (f16/bf16 paths).
+ *
+ * Returns SDPA_OK, or
+ *   SDPA_ERR_INVALID     null q/k/v/out, B/H/Nq/Nk/d < 1, non-finite scale,
+ *                        is_causal not 0/1, unknown dtype, SDPA_SAME as
+ *                        dtype, packed with Nq != Nk, misaligned pointers,
+ *                        or element counts overflowing int64;
+ *   SDPA_ERR_UNSUPPORTED d or dtype outside the supported set, negative
+ *                        scale, out_dtype other than SDPA_SAME/SDPA_F32;
+ *   SDPA_ERR_DEVICE      the current device is not gfx950;
+ *   SDPA_ERR_LAUNCH      the kernel launch failed.
+ * Nothing is launched unless SDPA_OK is returned.
+ */
+SDPA_API sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                              float scale, int is_causal, const int32_t* cu_seqlens,
+                              sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
+/* 1 if (dtype, d, is_causal, varlen) is served by the matrix-core path,
+ * 0 if it is served by the plain f32 path, -1 if unsupported.  Pure host
+ * function; touches no device. */
+SDPA_API int sdpa_supports(sdpa_dtype dtype, int64_t d, int is_causal, int varlen);
+
+/* Static string naming a status code; never NULL. */
+SDPA_API const char* sdpa_status_str(sdpa_status s);
+
+/* SDPA_ABI_VERSION of the built library. */
+SDPA_API int sdpa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */
