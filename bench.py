@@ -121,6 +121,22 @@ def cpu_baseline(w, budget_s: float):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration(torch) -> int:
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / 5
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": round(ms, 4), "GBps": round(2 * n / ms / 1e6, 1)}))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +145,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="noncausal", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU work for the oracle baseline (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (5 times), the "
+                         "reference for scaling HBM byte counters")
     a = ap.parse_args(argv)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the path shards by (batch, head) "
@@ -145,6 +164,8 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if a.calibrate_copy:
+        return copy_calibration(torch)
     w = inputs.make_config(WORKLOADS[a.workload])
 
     def up(x):

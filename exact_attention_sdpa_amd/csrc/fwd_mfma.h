@@ -17,22 +17,40 @@
 //            K/V in that XCD's L2.  Causal tiles of a head run heaviest
 //            first.
 //   waves    NW waves; wave w owns NB blocks of 32 query rows.
-//   tile     BN keys per step, staged through double-buffered LDS:
-//            K row-major [BN][D+8], V transposed [D][BN+4] (f16 always).
+//   tile     BN keys per step, read with buffer loads whose range check
+//            returns zeros past the last key, staged through double-buffered
+//            LDS: K row-major [BN][D+8]; V transposed to [D][BN+8] f16 with
+//            keys permuted inside each group of 16, so that a lane's V
+//            fragment is one 16-byte read.  The row padding and the lane to
+//            key-pair assignment of the transposing writes were chosen by
+//            measuring LDS bank conflicts on gfx950: both the fragment reads
+//            and the writes are conflict-free.
 //
 // Register dataflow per 32x32 block (v_mfma_f32_32x32x16, wave64):
 //   S^T = K . Q^T      A = K rows from LDS, B = Q rows held in VGPRs.
 //                      Lane l owns query l%32 and keys 8(r/4)+4(l/32)+r%4,
-//                      r = 0..15, so a row max/sum is 15 in-lane ops plus
-//                      one v_permlane32_swap exchange with lane l^32.
-//   P = exp2(S*c - m)  c = scale*log2(e); running max m and per-lane
-//                      partial row sums l in fp32 registers.
-//   O^T += V^T . P^T   B = P converted to f16 straight from the S^T
-//                      accumulator registers (no LDS round trip); A = V^T
-//                      read from the transposed LDS tile with the matching
-//                      key order.  bf16 inputs: V is converted to f16 when
-//                      it is staged (exact for |v| <= 65504), P is f16.
+//                      r = 0..15, so a row max is 15 in-lane ops plus one
+//                      v_permlane32_swap exchange with lane l^32.
+//   softmax (exp2)     t = s*c - m with c = scale*log2(e) (one fma per score)
+//                      and m a per-row reference; P = exp2(t).  The reference
+//                      is raised only when a row's scores exceed it by more
+//                      than 2^8 (and on the first block), so the output
+//                      rescale is rare and P <= 256 in between.  Row sums
+//                      accumulate the fp32 P.
+//   P                  converted to f16 straight from the accumulator
+//                      registers (no LDS round trip).
+//   O^T += V^T . P^T   A = V^T read from LDS in the key order of P's
+//                      registers.  bf16 inputs: V is converted to f16 when
+//                      staged (exact for |v| <= 65504).
 //   epilogue           O = acc / l, lse = ln2 * (m + log2 l), one store.
+//
+// Step order (KL = how many tiles the K stream runs ahead of V):
+//   KL = 0  step j: S(j) = K(j) Q^T, softmax of tile j, P(j) V(j);
+//   KL = 1  step j: S(j+1) = K(j+1) Q^T is issued first, then the softmax of
+//           tile j (independent of those products, so one wave keeps both
+//           the matrix cores and the vector ALUs busy), then P(j) V(j).
+// Either way LDS holds two K and two V buffers, filled from registers loaded
+// one step earlier, with one barrier per step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,8 +78,13 @@ struct MfmaParams {
   int Nq, Nk;          // dense sizes; packed: max sequence length
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
-  float c;             // scale * log2(e)
+  float c;             // scale * log2(e), at least 1e-30
 };
+
+// Reference raise threshold (log2 units): P = exp2(t) stays <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+// Buffer descriptor word 3 for raw (untyped) 32-bit accesses on gfx9.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -92,105 +115,323 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// bf16 bit pattern -> f16 bit pattern (exact for normal f16 magnitudes).
-__device__ __forceinline__ uint32_t bf16_to_f16_bits(uint32_t b) {
-  _Float16 h = (_Float16)__uint_as_float(b << 16);
-  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+// two bf16 (packed) -> two f16 (packed); exact for normal f16 magnitudes.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
-template <bool BF16, int D, int NB, int NW, bool CAUSAL, bool VARLEN, bool OUTF32>
+// Position of key k (0..BN-1) inside its LDS V^T row: within each group of
+// 16 keys, lane half 0 reads keys {0-3, 8-11} and half 1 keys {4-7, 12-15},
+// each as 8 contiguous elements.
+__host__ __device__ constexpr int vt_key_pos(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <bool BF16, int D, int NB, int NW, int BN, int KL, bool CAUSAL, bool VARLEN, bool OUTF32>
 struct MfmaFwd {
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
-  static constexpr int BN = (D >= 128) ? 32 : 64;  // keys per step
   static constexpr int KB = BN / 32;       // 32-key blocks per step
   static constexpr int DS = D / 16;        // k-steps of S = Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
   static constexpr int NT = NW * 64;
+  static constexpr int NC = D / 8;         // 16-byte chunks per row
   static constexpr int KROW = D + 8;       // LDS K row, elements
-  static constexpr int VROW = BN + 4;      // LDS V^T row, elements
-  static constexpr int KCHUNKS = BN * D / 8;         // 16-byte K chunks per tile
-  static constexpr int VPAIRS = (BN / 2) * (D / 8);  // (2 rows x 16 bytes) V chunks
+  static constexpr int VRW = BN / 2 + 4;   // LDS V^T row, 32-bit words
+  static constexpr int KCHUNKS = BN * NC;        // 16-byte K chunks per tile
+  static constexpr int VPAIRS = (BN / 2) * NC;   // (2 rows x 16 bytes) V chunks
   static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
   static constexpr int VPT = (VPAIRS + NT - 1) / NT;
   static_assert(D % 32 == 0 && D <= 128, "head dim");
+  static_assert(BN % 32 == 0 && BN <= 128, "key block");
 
   struct __attribute__((aligned(16))) Smem {
     uint16_t k[2][BN * KROW];
-    uint16_t vt[2][D * VROW];
+    uint32_t vt[2][D * VRW];
   };
 
-  struct Prefetch {
-    u32x4 k[KPT];
-    u32x4 v0[VPT], v1[VPT];
+  struct KRegs { u32x4 k[KPT]; };
+  struct VRegs { u32x4 v0[VPT], v1[VPT]; };
+
+  // per-thread constant addressing of the staging copies
+  struct Staging {
+    int kg[KPT];   // K chunk: byte offset within the tile
+    int kl[KPT];   // K chunk: element offset in an LDS K buffer
+    int vg[VPT];   // V pair: byte offset of the even row within the tile
+    int vl[VPT];   // V pair: word offset in an LDS V^T buffer (d offset 0)
   };
 
-  // Global -> registers for key tile starting at key kb (rows >= nk read as 0).
-  static __device__ __forceinline__ void load_tile(Prefetch& pf, const uint16_t* kbase,
-                                                   const uint16_t* vbase, int64_t rs, int kb,
-                                                   int nk, int tid) {
+  // per-lane LDS read bases
+  struct Lanes {
+    int kl;      // K fragment, elements
+    int vl[2];   // V^T fragment for hs = 0, 1, words
+  };
+
+  // per-head view used by the staging copies
+  struct Head {
+    const char* k;
+    const char* v;
+    int kv_bytes;   // byte length of the valid key rows
+    int rs_bytes;   // row stride in bytes
+  };
+
+  static __device__ __forceinline__ void setup_staging(Staging& st, int64_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      int c = tid + i * NT;
-      pf.k[i] = u32x4{0, 0, 0, 0};
-      if (KCHUNKS % NT == 0 || c < KCHUNKS) {
-        int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        if (kb + row < nk)
-          pf.k[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kb + row) * rs + col);
-      }
+      const int c = tid + i * NT;
+      const int row = c / NC, col = (c % NC) * 8;
+      st.kg[i] = (int)(((int64_t)row * rs + col) * 2);
+      st.kl[i] = row * KROW + col;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      int c = tid + i * NT;
-      pf.v0[i] = u32x4{0, 0, 0, 0};
-      pf.v1[i] = u32x4{0, 0, 0, 0};
-      if (VPAIRS % NT == 0 || c < VPAIRS) {
-        int pr = c / (D / 8), col = (c % (D / 8)) * 8;
-        int r0 = kb + 2 * pr;
-        if (r0 < nk)
-          pf.v0[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)r0 * rs + col);
-        if (r0 + 1 < nk)
-          pf.v1[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)(r0 + 1) * rs + col);
+      const int c = tid + i * NT;
+      // consecutive lanes take consecutive key pairs of one column chunk
+      const int pr = c % (BN / 2);
+      const int col = (c / (BN / 2)) * 8;
+      st.vg[i] = (int)(((int64_t)(2 * pr) * rs + col) * 2);
+      st.vl[i] = col * VRW + vt_key_pos(2 * pr) / 2;
+    }
+  }
+
+  static __device__ __forceinline__ Lanes setup_lanes(int l32, int hl) {
+    Lanes ln;
+    ln.kl = l32 * KROW + hl * 8;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) ln.vl[hs] = l32 * VRW + hl * 4 + 8 * hs;
+    return ln;
+  }
+
+  // Buffer view of tile `t` of a head: it starts at the tile and ends at the
+  // last valid key row, so rows past it read as zeros (the range check never
+  // relies on the hardware applying an offset register).
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int t,
+                                                                     const Head& hd) {
+    const int toff = t * BN * hd.rs_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + toff), (short)0,
+                                             max(hd.kv_bytes - toff, 0), kBufferWord3);
+  }
+
+  static __device__ __forceinline__ void load_k(KRegs& r, const Staging& st, const Head& hd, int t,
+                                                int tid) {
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(hd.k, t, hd);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS)
+        r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, st.kg[i], 0, 0));
+  }
+
+  static __device__ __forceinline__ void load_v(VRegs& r, const Staging& st, const Head& hd, int t,
+                                                int tid) {
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(hd.v, t, hd);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+        r.v0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, st.vg[i], 0, 0));
+        r.v1[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, st.vg[i] + hd.rs_bytes, 0, 0));
+      }
+  }
+
+  static __device__ __forceinline__ void store_k(Smem& sm, int buf, const KRegs& r,
+                                                 const Staging& st, int tid) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS)
+        *reinterpret_cast<u32x4*>(&sm.k[buf][st.kl[i]]) = r.k[i];
+  }
+
+  // V transposed to [d][key] (f16), keys in vt_key_pos order
+  static __device__ __forceinline__ void store_v(Smem& sm, int buf, const VRegs& r,
+                                                 const Staging& st, int tid) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+        uint32_t* dst = &sm.vt[buf][st.vl[i]];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t a = r.v0[i][w], b = r.v1[i][w];  // (d 2w, d 2w+1) of keys 2pr, 2pr+1
+          if (BF16) {
+            a = bf16x2_to_f16x2(a);
+            b = bf16x2_to_f16x2(b);
+          }
+          dst[(2 * w) * VRW] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+          dst[(2 * w + 1) * VRW] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+        }
+      }
+  }
+
+  // Raw scores S^T = K Q^T of the tile in LDS K buffer `buf`.
+  static __device__ __forceinline__ void scores(f32x16 (&s)[NB][KB], const Smem& sm, int buf,
+                                                const Lanes& ln, const u32x4 (&qf)[NB][DS]) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      u32x4 kf[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kf[ds] = *reinterpret_cast<const u32x4*>(&sm.k[buf][ln.kl + kk * 32 * KROW + ds * 16]);
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          acc = BF16 ? mfma_bf16(kf[ds], qf[qb][ds], acc) : mfma_f16(kf[ds], qf[qb][ds], acc);
+        s[qb][kk] = acc;
       }
     }
   }
 
-  // Registers -> LDS buffer `buf` (K as is, V transposed to [d][key], f16).
-  static __device__ __forceinline__ void store_tile(Smem& sm, int buf, const Prefetch& pf,
-                                                    int tid) {
+  struct State {
+    f32x16 o[NB][DB];
+    float m[NB], l[NB];
+  };
+
+  // Softmax update of one tile from its raw scores, then O += P V with the
+  // tile in LDS V buffer `buf`.  One code path for every tile: the mask and
+  // the reference raise are small branches that rewrite registers in place.
+  static __device__ __forceinline__ void softmax_pv(f32x16 (&s)[NB][KB], const Smem& sm, int buf,
+                                                    int kb, bool first, bool need_mask, int nk,
+                                                    int wq0, int l32, int hl, float c,
+                                                    const Lanes& ln, State& S) {
+    // ---- t = S*c - m
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int c = tid + i * NT;
-      if (KCHUNKS % NT == 0 || c < KCHUNKS) {
-        int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(&sm.k[buf][row * KROW + col]) = pf.k[i];
-      }
+    for (int qb = 0; qb < NB; ++qb) {
+      const float nm = -S.m[qb];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kk][r] = __builtin_fmaf(s[qb][kk][r], c, nm);
     }
+
+    // ---- masking (diagonal and tail tiles only)
+    if (need_mask) {
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      int c = tid + i * NT;
-      if (VPAIRS % NT == 0 || c < VPAIRS) {
-        int pr = c / (D / 8), col = (c % (D / 8)) * 8;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[buf][col * VROW + 2 * pr]);
+      for (int qb = 0; qb < NB; ++qb) {
+        const int qi = wq0 + qb * 32 + l32;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          uint32_t a = (pf.v0[i][t / 2] >> (16 * (t & 1))) & 0xffffu;
-          uint32_t b = (pf.v1[i][t / 2] >> (16 * (t & 1))) & 0xffffu;
-          if (BF16) {
-            a = bf16_to_f16_bits(a);
-            b = bf16_to_f16_bits(b);
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+            const bool ok = key < nk && (!CAUSAL || key <= qi);
+            if (!ok) s[qb][kk][r] = -INFINITY;
           }
-          dst[t * (VROW / 2)] = a | (b << 16);
-        }
       }
     }
+
+    // ---- row maxima (4 independent chains); raise the reference where needed
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      float x[4] = {s[qb][0][0], s[qb][0][1], s[qb][0][2], s[qb][0][3]};
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r & 3] = fmaxf(x[r & 3], s[qb][kk][r]);
+      const float mt = pair_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      // Per lane (exec-masked), so the accumulators are rescaled in place.
+      // First tile: the reference becomes the block maximum (finite: key 0 is
+      // visible to every row); later: only rows that exceeded it by 2^8.
+      if (first || mt > kRescaleSlack) {
+        S.m[qb] += mt;
+        const float alpha = __builtin_amdgcn_exp2f(-mt);
+        S.l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qb][kk][r] -= mt;
+      }
+    }
+
+    // ---- P = exp2(t): fp32 row sums (4 partial sums), f16 B operands
+    u32x4 pf16[NB][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      float rs4[4] = {S.l[qb], 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          uint32_t w[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float e0 = __builtin_amdgcn_exp2f(s[qb][kk][8 * hs + 2 * t]);
+            const float e1 = __builtin_amdgcn_exp2f(s[qb][kk][8 * hs + 2 * t + 1]);
+            rs4[(2 * t) & 3] += e0;
+            rs4[(2 * t + 1) & 3] += e1;
+            w[t] = pack_f16(e0, e1);
+          }
+          pf16[qb][kk][hs] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+      S.l[qb] = (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(
+              &sm.vt[buf][ln.vl[hs] + db * 32 * VRW + 16 * kk]);
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb)
+            S.o[qb][db] = mfma_f16(vf, pf16[qb][kk][hs], S.o[qb][db]);
+        }
+  }
+
+  struct Ctx {
+    Staging st;
+    Lanes ln;
+    Head hd;
+    int ntiles, nk, wq0, l32, hl, tid;
+    bool wave_live;
+    float c;
+  };
+
+  static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
+    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
+  }
+
+  // Step j with KL = 1 (K buffer of tile j+1 is B^1, V buffer of tile j is B):
+  // loads K(j+2), V(j+1); S(j+1) on the matrix cores; softmax and P.V of
+  // tile j; stores K(j+2) -> K buffer B, V(j+1) -> V buffer B^1; barrier.
+  // With KL = 0 (K and V of tile j both in buffer B): loads K(j+1), V(j+1);
+  // S(j), softmax, P.V of tile j; stores tile j+1 -> buffers B^1; barrier.
+  template <int B>
+  static __device__ __forceinline__ void step(Smem& sm, const Ctx& x, State& S,
+                                              const u32x4 (&qf)[NB][DS], f32x16 (&s_cur)[NB][KB],
+                                              f32x16 (&s_nxt)[NB][KB], int j) {
+    KRegs kr;
+    VRegs vr;
+    const bool kn = j + 1 + KL < x.ntiles, vn = j + 1 < x.ntiles;
+    if (kn) load_k(kr, x.st, x.hd, j + 1 + KL, x.tid);
+    if (vn) load_v(vr, x.st, x.hd, j + 1, x.tid);
+    if (KL == 1 && vn && !skip_tile(x, j + 1)) scores(s_nxt, sm, B ^ 1, x.ln, qf);
+    if (!skip_tile(x, j)) {
+      if (KL == 0) scores(s_cur, sm, B, x.ln, qf);
+      const int kb = j * BN;
+      const bool need_mask = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
+      softmax_pv(s_cur, sm, B, kb, j == 0, need_mask, x.nk, x.wq0, x.l32, x.hl, x.c, x.ln, S);
+    }
+    if (kn) store_k(sm, KL == 1 ? B : B ^ 1, kr, x.st, x.tid);
+    if (vn) store_v(sm, B ^ 1, vr, x.st, x.tid);
+    __syncthreads();
   }
 
   static __device__ void run(const MfmaParams& p, Smem& sm) {
-    const int tid = threadIdx.x;
-    const int wave = tid / 64;
-    const int lane = tid % 64;
-    const int hl = lane / 32;
-    const int l32 = lane % 32;
+    Ctx x;
+    x.tid = threadIdx.x;
+    const int wave = x.tid / 64;
+    const int lane = x.tid % 64;
+    x.hl = lane / 32;
+    x.l32 = lane % 32;
+    x.c = p.c;
 
     // ---- which tile: XCD-contiguous ranges, heads' tiles back to back
     int tile = blockIdx.x;
@@ -219,164 +460,85 @@ struct MfmaFwd {
     }
     const int q0 = qt * BM;
     if (q0 >= nq) return;  // whole workgroup: tile past the sequence end
+    x.nk = nk;
 
-    const uint16_t* qbase = p.q + qoff;
-    const uint16_t* kbase = p.k + kvoff;
-    const uint16_t* vbase = p.v + kvoff;
+    x.hd.rs_bytes = (int)(rs * 2);
+    x.hd.kv_bytes = (int)(((int64_t)(nk - 1) * rs + D) * 2);
+    x.hd.k = reinterpret_cast<const char*>(p.k + kvoff);
+    x.hd.v = reinterpret_cast<const char*>(p.v + kvoff);
+    const int q_bytes = (int)(((int64_t)(nq - 1) * rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t qr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qoff), (short)0, q_bytes, kBufferWord3);
+
     const int kend = CAUSAL ? min(nk, q0 + BM) : nk;
-    const int ntiles = (kend + BN - 1) / BN;
-
-    const int wq0 = q0 + wave * NB * 32;   // first query row of this wave
-    const bool wave_live = wq0 < nq;
+    x.ntiles = (kend + BN - 1) / BN;
+    x.wq0 = q0 + wave * NB * 32;   // first query row of this wave
+    x.wave_live = x.wq0 < nq;
 
     // ---- Q rows as the B operand of S^T = K Q^T
     u32x4 qf[NB][DS];
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      const int qi = wq0 + qb * 32 + l32;
+      const int qi = x.wq0 + qb * 32 + x.l32;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        qf[qb][ds] = u32x4{0, 0, 0, 0};
-        if (qi < nq)
-          qf[qb][ds] = *reinterpret_cast<const u32x4*>(qbase + (int64_t)qi * rs + ds * 16 + hl * 8);
-      }
+      for (int ds = 0; ds < DS; ++ds)
+        qf[qb][ds] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qi * x.hd.rs_bytes + (ds * 16 + x.hl * 8) * 2, 0, 0));
     }
 
-    f32x16 o[NB][DB];
-    float m[NB], l[NB];
+    State S;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      m[qb] = -INFINITY;
-      l[qb] = 0.f;
+      S.m[qb] = 0.f;
+      S.l[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+        for (int r = 0; r < 16; ++r) S.o[qb][db][r] = 0.f;
     }
 
-    Prefetch pf;
-    load_tile(pf, kbase, vbase, rs, 0, nk, tid);
-    store_tile(sm, 0, pf, tid);
+    setup_staging(x.st, rs, x.tid);
+    x.ln = setup_lanes(x.l32, x.hl);
+
+    // ---- prologue: K(0) (and K(1) when KL = 1) and V(0) staged; with KL = 1
+    // also S(0), then a barrier before K(0)'s buffer is reused
+    {
+      KRegs k0, k1;
+      VRegs v0;
+      load_k(k0, x.st, x.hd, 0, x.tid);
+      if (KL == 1 && x.ntiles > 1) load_k(k1, x.st, x.hd, 1, x.tid);
+      load_v(v0, x.st, x.hd, 0, x.tid);
+      store_k(sm, 0, k0, x.st, x.tid);
+      if (KL == 1 && x.ntiles > 1) store_k(sm, 1, k1, x.st, x.tid);
+      store_v(sm, 0, v0, x.st, x.tid);
+    }
     __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-      const int buf = j & 1;
-      const int kb = j * BN;
-      const bool has_next = j + 1 < ntiles;
-      if (has_next) load_tile(pf, kbase, vbase, rs, kb + BN, nk, tid);
-
-      const bool skip = !wave_live || (CAUSAL && kb > wq0 + NB * 32 - 1);
-      if (!skip) {
-        const bool need_mask = (kb + BN > nk) || (CAUSAL && kb + BN - 1 > wq0);
-        // ---- S^T = K Q^T
-        f32x16 s[NB][KB];
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk) {
-          u32x4 kf[DS];
-#pragma unroll
-          for (int ds = 0; ds < DS; ++ds)
-            kf[ds] = *reinterpret_cast<const u32x4*>(
-                &sm.k[buf][(kk * 32 + l32) * KROW + ds * 16 + hl * 8]);
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) {
-            f32x16 acc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds)
-              acc = BF16 ? mfma_bf16(kf[ds], qf[qb][ds], acc) : mfma_f16(kf[ds], qf[qb][ds], acc);
-            s[qb][kk] = acc;
-          }
-        }
-
-        // ---- online softmax (exp2 domain)
-        u32x4 pf16[NB][KB][2];
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          const int qi = wq0 + qb * 32 + l32;
-          if (need_mask) {
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = kb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-                const bool ok = key < nk && (!CAUSAL || key <= qi);
-                if (!ok) s[qb][kk][r] = -INFINITY;
-              }
-          }
-          float mt = -INFINITY;
-#pragma unroll
-          for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[qb][kk][r]);
-          mt = pair_max(mt);
-          // scaled tile max; a row with every key masked here keeps its max
-          const float ms = (mt == -INFINITY) ? -INFINITY : mt * p.c;
-          const float mnew = fmaxf(m[qb], ms);
-          const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-          const float alpha = __builtin_amdgcn_exp2f(m[qb] - mref);
-          m[qb] = mnew;
-          const float nm = -mref;
-          float rsum = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < KB; ++kk) {
-            float pv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kk][r], p.c, nm));
-              if (need_mask && s[qb][kk][r] == -INFINITY) e = 0.f;
-              pv[r] = e;
-              rsum += e;
-            }
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs)
-              pf16[qb][kk][hs] = u32x4{pack_f16(pv[8 * hs + 0], pv[8 * hs + 1]),
-                                       pack_f16(pv[8 * hs + 2], pv[8 * hs + 3]),
-                                       pack_f16(pv[8 * hs + 4], pv[8 * hs + 5]),
-                                       pack_f16(pv[8 * hs + 6], pv[8 * hs + 7])};
-          }
-          l[qb] = l[qb] * alpha + rsum;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        }
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const uint16_t* vrow = &sm.vt[buf][(db * 32 + l32) * VROW + kk * 32 + 16 * hs + 4 * hl];
-              const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-              const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-              const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-              for (int qb = 0; qb < NB; ++qb) o[qb][db] = mfma_f16(vf, pf16[qb][kk][hs], o[qb][db]);
-            }
-      }
-
-      if (has_next) store_tile(sm, buf ^ 1, pf, tid);
+    f32x16 sa[NB][KB], sb[NB][KB];
+    if (KL == 1) {
+      if (!skip_tile(x, 0)) scores(sa, sm, 0, x.ln, qf);
       __syncthreads();
     }
 
+    for (int j = 0; j < x.ntiles; j += 2) {
+      step<0>(sm, x, S, qf, sa, sb, j);
+      if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, sb, sa, j + 1);
+    }
+
     // ---- epilogue: normalise, store O and lse once
-    if (!wave_live) return;
+    if (!x.wave_live) return;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      const int qi = wq0 + qb * 32 + l32;
-      const float lt = pair_sum(l[qb]);
+      const int qi = x.wq0 + qb * 32 + x.l32;
+      const float lt = pair_sum(S.l[qb]);
       const float inv = 1.f / lt;
       if (qi < nq) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int dcol = db * 32 + 8 * g + 4 * hl;
-            const float x0 = o[qb][db][4 * g + 0] * inv, x1 = o[qb][db][4 * g + 1] * inv;
-            const float x2 = o[qb][db][4 * g + 2] * inv, x3 = o[qb][db][4 * g + 3] * inv;
+            const int dcol = db * 32 + 8 * g + 4 * x.hl;
+            const float x0 = S.o[qb][db][4 * g + 0] * inv, x1 = S.o[qb][db][4 * g + 1] * inv;
+            const float x2 = S.o[qb][db][4 * g + 2] * inv, x3 = S.o[qb][db][4 * g + 3] * inv;
             const int64_t off = qoff + (int64_t)qi * rs + dcol;
             if (OUTF32) {
               *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + off) =
@@ -387,8 +549,8 @@ struct MfmaFwd {
               *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + off) = w;
             }
           }
-        if (p.lse != nullptr && hl == 0) {
-          const float lse = (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+        if (p.lse != nullptr && x.hl == 0) {
+          const float lse = (S.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
           if (VARLEN)
             p.lse[(int64_t)(p.cu[b] + qi) * p.H + h] = lse;
           else
@@ -399,9 +561,9 @@ struct MfmaFwd {
   }
 };
 
-template <bool BF16, int D, int NB, int NW, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, int NB, int NW, int BN, int KL, bool CAUSAL, bool VARLEN, bool OUTF32>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(MfmaParams p) {
-  using K = MfmaFwd<BF16, D, NB, NW, CAUSAL, VARLEN, OUTF32>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, KL, CAUSAL, VARLEN, OUTF32>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -1,5 +1,6 @@
 // Host-side argument checks of sdpa_fwd.  Makes no HIP calls, so every
 // error path can be exercised without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -69,6 +70,13 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   const int path = path_for(dtype, d);
   if (path < 0) return SDPA_ERR_UNSUPPORTED;
   if (scale < 0.f) return SDPA_ERR_UNSUPPORTED;
+
+  // matrix-core path: one head's rows (plus a query tile of slack) must fit
+  // the 32-bit byte offsets of its buffer loads
+  if (path == 1) {
+    const int64_t row_bytes = (varlen ? H * d : d) * 2;
+    if ((std::max(Nq, Nk) + 256) * row_bytes > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
+  }
 
   const uintptr_t al = path == 1 ? 16 : 4;
   if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(out, al))
