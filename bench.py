@@ -137,6 +137,106 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def _csv_rows(d, name):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{name}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{name} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_kib(d, kernel_match):
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(d, "counter_collection.csv")
+            if kernel_match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no dispatch matching {kernel_match!r} in {d}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize(a) -> int:
+    """Turn rocprofv3 outputs of the commands printed below into the text
+    summary profiles/<kernel>_<workload>.txt and the HBM-traffic record
+    profiles/hbm_traffic.json that the benchmark line reports.
+
+    FETCH_SIZE / WRITE_SIZE are scaled by what the same counters read for a
+    plain copy of 1 GiB (bench.py --calibrate-copy), so that a counter
+    that sees only part of the memory channels still yields bytes."""
+    stats = _csv_rows(a.trace_dir, "kernel_stats.csv")
+    ker = [r for r in stats if "fwd_mfma" in r["Name"] or "fwd_f32" in r["Name"]]
+    if not ker:
+        raise SystemExit("no attention kernel in the kernel trace")
+    k = max(ker, key=lambda r: float(r["TotalDurationNs"]))
+    avg_ns = float(k["AverageNs"])
+    fetch, nf = _counter_kib(a.fetch_dir, "fwd_mfma")
+    write, nw = _counter_kib(a.write_dir, "fwd_mfma")
+    cfetch, _ = _counter_kib(a.copy_fetch_dir, "copyBuffer")
+    cwrite, _ = _counter_kib(a.copy_write_dir, "copyBuffer")
+    gib_kib = float(1 << 20)
+    ffac, wfac = gib_kib / cfetch, gib_kib / cwrite
+    read_b = fetch * ffac * 1024
+    write_b = write * wfac * 1024
+    from exact_attention_sdpa_amd import inputs
+    w = inputs.make_config(WORKLOADS[a.workload])
+    el = 2 if w.dtype != "f32" else 4
+    rows_q = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nq
+    rows_k = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nk
+    out_el = 4 if w.dtype == "bf16" else el
+    alg_read = (rows_q + 2 * rows_k) * w.H * w.d * el
+    alg_write = rows_q * w.H * (w.d * out_el + 4)
+    name = k["Name"].split("(")[0].replace("void ", "").replace("sdpa::", "")
+    tag = f"fwd_mfma_{a.workload}"
+    txt = [
+        f"# {tag}: rocprofv3 summary, workload {describe(w, a.workload)['workload']}",
+        "",
+        "Kernel trace (average over the profiled launches):",
+        f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- "
+        f"python3 bench.py --workload {a.workload} --steps 20 --warmup 3 --cpu-budget 0",
+        f"  kernel:  {k['Name']}",
+        f"  calls {k['Calls']}  average {avg_ns / 1e3:.2f} us  min {float(k['MinNs']) / 1e3:.2f} us"
+        f"  max {float(k['MaxNs']) / 1e3:.2f} us",
+        f"  metric FLOPs per launch {w.flops():.6g} -> {w.flops() / avg_ns / 1e3:.1f} TFLOP/s at the "
+        f"average duration ({100 * w.flops() / avg_ns / 1e3 / PEAK_TFLOPS:.1f}% of {PEAK_TFLOPS:.0f})",
+        "",
+        "HBM traffic (separate counter passes, one counter block each):",
+        f"  commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
+        f"--workload {a.workload} --steps 5 --warmup 1 --cpu-budget 0",
+        "            rocprofv3 --pmc WRITE_SIZE (same program)",
+        "            rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 bench.py --calibrate-copy",
+        f"  copy of 1 GiB reads FETCH_SIZE {cfetch:.0f} KiB, WRITE_SIZE {cwrite:.0f} KiB"
+        f" -> scale factors {ffac:.4f} (fetch), {wfac:.4f} (write)",
+        f"  kernel: FETCH_SIZE {fetch:.0f} KiB/dispatch ({nf} dispatches), WRITE_SIZE {write:.0f} "
+        f"KiB/dispatch ({nw})",
+        f"  -> {read_b / 1e6:.2f} MB read + {write_b / 1e6:.2f} MB written per launch",
+        f"  algorithmic (q,k,v read once; out and lse written once): {alg_read / 1e6:.2f} MB read + "
+        f"{alg_write / 1e6:.2f} MB written",
+        f"  measured / algorithmic: read {read_b / alg_read:.3f}, write {write_b / alg_write:.3f}",
+        f"  achieved HBM rate at the average duration: {(read_b + write_b) / avg_ns:.1f} GB/s",
+        "",
+        f"kernel sources digest: {kernel_sources_digest()}",
+    ]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{tag}.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    rec = {"kernel_sources": kernel_sources_digest(), "workloads": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            old = json.load(f)
+        if old.get("kernel_sources") == rec["kernel_sources"]:
+            rec = old
+    rec["workloads"][a.workload] = {
+        "bytes_per_launch": round(read_b + write_b), "read_bytes": round(read_b),
+        "write_bytes": round(write_b), "algorithmic_bytes": alg_read + alg_write,
+        "avg_kernel_us": round(avg_ns / 1e3, 3), "fetch_scale": round(ffac, 5),
+        "write_scale": round(wfac, 5), "kernel": name}
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print("\n".join(txt))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,7 +248,16 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), the "
                          "reference for scaling HBM byte counters")
+    ap.add_argument("--summarize", action="store_true",
+                    help="summarize rocprofv3 CSV outputs into profiles/ (no GPU needed)")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
     a = ap.parse_args(argv)
+    if a.summarize:
+        return summarize(a)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the path shards by (batch, head) "
               "with no exchange, so --gpus N > 1 is not measured here.", file=sys.stderr)
