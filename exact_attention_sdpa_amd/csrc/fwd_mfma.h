@@ -31,12 +31,16 @@
 //                      Lane l owns query l%32 and keys 8(r/4)+4(l/32)+r%4,
 //                      r = 0..15, so a row max is 15 in-lane ops plus one
 //                      v_permlane32_swap exchange with lane l^32.
-//   softmax (exp2)     t = s*c - m with c = scale*log2(e) (one fma per score)
-//                      and m a per-row reference; P = exp2(t).  The reference
-//                      is raised only when a row's scores exceed it by more
-//                      than 2^8 (and on the first block), so the output
-//                      rescale is rare and P <= 256 in between.  Row sums
-//                      accumulate the fp32 P.
+//   softmax (exp2)     each row keeps a reference mu in raw-score units; the
+//                      S accumulator is seeded with -mu, so the matrix core
+//                      returns s - mu and t = c*(s - mu) is one multiply
+//                      (c = scale*log2(e)); P = exp2(t).  The first tile sets
+//                      mu to the row maximum.  Later tiles do not compute a
+//                      maximum at all: every lane's fp32 sum of its P values
+//                      bounds each of them, and only if a sum exceeds 2^15
+//                      (an f16 P could overflow) is the tile redone with mu
+//                      raised to the new maximum.  Row sums accumulate the
+//                      fp32 P, so the logsumexp is exact to fp32 rounding.
 //   P                  converted to f16 straight from the accumulator
 //                      registers (no LDS round trip).
 //   O^T += V^T . P^T   A = V^T read from LDS in the key order of P's
@@ -44,13 +48,10 @@
 //                      staged (exact for |v| <= 65504).
 //   epilogue           O = acc / l, lse = ln2 * (m + log2 l), one store.
 //
-// Step order (KL = how many tiles the K stream runs ahead of V):
-//   KL = 0  step j: S(j) = K(j) Q^T, softmax of tile j, P(j) V(j);
-//   KL = 1  step j: S(j+1) = K(j+1) Q^T is issued first, then the softmax of
-//           tile j (independent of those products, so one wave keeps both
-//           the matrix cores and the vector ALUs busy), then P(j) V(j).
-// Either way LDS holds two K and two V buffers, filled from registers loaded
-// one step earlier, with one barrier per step.
+// Step j: S(j) = K(j) Q^T, the softmax of tile j, P(j) V(j) (the P.V products
+// of the first 32 keys are issued under the exponentials of the next 32).
+// LDS holds two K and two V buffers, filled from registers loaded one step
+// earlier, with one barrier per step.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -79,10 +80,18 @@ struct MfmaParams {
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
   float c;             // scale * log2(e), at least 1e-30
+  float inv_c;         // 1 / c
 };
 
-// Reference raise threshold (log2 units): P = exp2(t) stays <= 2^8.
-constexpr float kRescaleSlack = 8.0f;
+// Build option: raise the wave priority while it issues matrix-core work
+// (measured a few percent faster on MI355X).
+#ifndef SDPA_SETPRIO
+#define SDPA_SETPRIO 1
+#endif
+
+// A lane whose tile sum of P exceeds this redoes the tile with a raised
+// reference, so no f16 P ever exceeds 2^15 (f16 max 65504).
+constexpr float kLaneSumLimit = 32768.0f;
 // Buffer descriptor word 3 for raw (untyped) 32-bit accesses on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -127,7 +136,7 @@ __host__ __device__ constexpr int vt_key_pos(int k) {
   return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <bool BF16, int D, int NB, int NW, int BN, int KL, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32>
 struct MfmaFwd {
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
   static constexpr int KB = BN / 32;       // 32-key blocks per step
@@ -260,130 +269,33 @@ struct MfmaFwd {
       }
   }
 
-  // Raw scores S^T = K Q^T of the tile in LDS K buffer `buf`.
-  static __device__ __forceinline__ void scores(f32x16 (&s)[NB][KB], const Smem& sm, int buf,
-                                                const Lanes& ln, const u32x4 (&qf)[NB][DS]) {
+  // S^T - mu = K Q^T - mu for key block kk (32 keys) of the tile in LDS K
+  // buffer `buf`; the accumulator starts at -mu, broadcast over the lane's
+  // 16 registers.
+  static __device__ __forceinline__ void scores(f32x16 (&s)[NB], const Smem& sm, int buf, int kk,
+                                                const Lanes& ln, const u32x4 (&qf)[NB][DS],
+                                                const f32x16 (&negmu)[NB]) {
+    u32x4 kf[DS];
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      u32x4 kf[DS];
+    for (int ds = 0; ds < DS; ++ds)
+      kf[ds] = *reinterpret_cast<const u32x4*>(&sm.k[buf][ln.kl + kk * 32 * KROW + ds * 16]);
+    if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      f32x16 acc = negmu[qb];
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
-        kf[ds] = *reinterpret_cast<const u32x4*>(&sm.k[buf][ln.kl + kk * 32 * KROW + ds * 16]);
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-          acc = BF16 ? mfma_bf16(kf[ds], qf[qb][ds], acc) : mfma_f16(kf[ds], qf[qb][ds], acc);
-        s[qb][kk] = acc;
-      }
+        acc = BF16 ? mfma_bf16(kf[ds], qf[qb][ds], acc) : mfma_f16(kf[ds], qf[qb][ds], acc);
+      s[qb] = acc;
     }
+    if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
   }
 
   struct State {
     f32x16 o[NB][DB];
-    float m[NB], l[NB];
+    f32x16 negmu[NB];   // -mu broadcast (seed of the S accumulator)
+    float mu[NB], l[NB];
   };
-
-  // Softmax update of one tile from its raw scores, then O += P V with the
-  // tile in LDS V buffer `buf`.  One code path for every tile: the mask and
-  // the reference raise are small branches that rewrite registers in place.
-  static __device__ __forceinline__ void softmax_pv(f32x16 (&s)[NB][KB], const Smem& sm, int buf,
-                                                    int kb, bool first, bool need_mask, int nk,
-                                                    int wq0, int l32, int hl, float c,
-                                                    const Lanes& ln, State& S) {
-    // ---- t = S*c - m
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      const float nm = -S.m[qb];
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kk][r] = __builtin_fmaf(s[qb][kk][r], c, nm);
-    }
-
-    // ---- masking (diagonal and tail tiles only)
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        const int qi = wq0 + qb * 32 + l32;
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-            const bool ok = key < nk && (!CAUSAL || key <= qi);
-            if (!ok) s[qb][kk][r] = -INFINITY;
-          }
-      }
-    }
-
-    // ---- row maxima (4 independent chains); raise the reference where needed
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      float x[4] = {s[qb][0][0], s[qb][0][1], s[qb][0][2], s[qb][0][3]};
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r & 3] = fmaxf(x[r & 3], s[qb][kk][r]);
-      const float mt = pair_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      // Per lane (exec-masked), so the accumulators are rescaled in place.
-      // First tile: the reference becomes the block maximum (finite: key 0 is
-      // visible to every row); later: only rows that exceeded it by 2^8.
-      if (first || mt > kRescaleSlack) {
-        S.m[qb] += mt;
-        const float alpha = __builtin_amdgcn_exp2f(-mt);
-        S.l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
-#pragma unroll
-        for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][kk][r] -= mt;
-      }
-    }
-
-    // ---- P = exp2(t): fp32 row sums (4 partial sums), f16 B operands
-    u32x4 pf16[NB][KB][2];
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) {
-      float rs4[4] = {S.l[qb], 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          uint32_t w[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float e0 = __builtin_amdgcn_exp2f(s[qb][kk][8 * hs + 2 * t]);
-            const float e1 = __builtin_amdgcn_exp2f(s[qb][kk][8 * hs + 2 * t + 1]);
-            rs4[(2 * t) & 3] += e0;
-            rs4[(2 * t + 1) & 3] += e1;
-            w[t] = pack_f16(e0, e1);
-          }
-          pf16[qb][kk][hs] = u32x4{w[0], w[1], w[2], w[3]};
-        }
-      S.l[qb] = (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(
-              &sm.vt[buf][ln.vl[hs] + db * 32 * VRW + 16 * kk]);
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb)
-            S.o[qb][db] = mfma_f16(vf, pf16[qb][kk][hs], S.o[qb][db]);
-        }
-  }
 
   struct Ctx {
     Staging st;
@@ -391,36 +303,179 @@ struct MfmaFwd {
     Head hd;
     int ntiles, nk, wq0, l32, hl, tid;
     bool wave_live;
-    float c;
+    float c, inv_c;
   };
+
+  // ---- softmax update of one tile, one block of 32 keys at a time
+
+  // Causal / key-tail mask on s - mu of the block at key kb0.
+  static __device__ __forceinline__ void mask_block(f32x16 (&s)[NB], int kb0, int nk, int wq0,
+                                                    int l32, int hl) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const int qi = wq0 + qb * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + 8 * (r / 4) + 4 * hl + (r % 4);
+        const bool ok = key < nk && (!CAUSAL || key <= qi);
+        if (!ok) s[qb][r] = -INFINITY;
+      }
+    }
+  }
+
+  // Row maximum of t over the block (4 chains, then the lane pair l, l^32).
+  static __device__ __forceinline__ float row_max(const f32x16& t) {
+    float x[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r & 3] = fmaxf(x[r & 3], t[r]);
+    return pair_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  }
+
+  // Move row qb's reference up by x (log2 units; per lane, exec-masked so
+  // the accumulators are rescaled in place): mu += x/c; the scaled block t
+  // drops by x and the pending unscaled block sn (s - mu) by x/c (both up
+  // to one rounding of x/c, far below the fp32 error of s itself); with
+  // RESCALE, l and O are scaled by 2^-x (without it they are still zero).
+  template <bool RESCALE, bool PENDING>
+  static __device__ __forceinline__ void raise_by(f32x16& t, f32x16& sn, int qb, float x,
+                                                  float inv_c, State& S) {
+    const float dmu = x * inv_c;
+    S.mu[qb] += dmu;
+    if (RESCALE) {
+      const float alpha = __builtin_amdgcn_exp2f(-x);
+      S.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t[r] -= x;
+    if (PENDING)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[r] -= dmu;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S.negmu[qb][r] = -S.mu[qb];
+  }
+
+  // P = exp2(t) of a block: the lane's fp32 sums (two partial sums per row)
+  // and the f16 B operands of P V.
+  static __device__ __forceinline__ void exp_block(const f32x16 (&t)[NB], float (&bs)[NB][2],
+                                                   u32x4 (&pf)[NB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = __builtin_amdgcn_exp2f(t[qb][8 * hs + 2 * i]);
+          const float e1 = __builtin_amdgcn_exp2f(t[qb][8 * hs + 2 * i + 1]);
+          if (hs == 0 && i == 0) {
+            bs[qb][0] = e0;
+            bs[qb][1] = e1;
+          } else {
+            bs[qb][0] += e0;
+            bs[qb][1] += e1;
+          }
+          w[i] = pack_f16(e0, e1);
+        }
+        pf[qb][hs] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+  }
+
+  // One tile: for each key block kk, the products S(kk+1) are issued before
+  // the softmax of block kk (they do not depend on it) and P V of block kk
+  // after it, so the matrix cores and the vector ALUs of one wave overlap.
+  // Each P is at most its lane's block sum; a lane over the limit (rare)
+  // raises its row to the block maximum (blocks already in O are rescaled
+  // with O and l) and the block's exponentials are redone.  The first block
+  // of the first tile sets the reference to its row maximum (finite: key 0
+  // is visible to every row).
+  static __device__ __forceinline__ void tile(const Smem& sm, int buf, int kb, bool first,
+                                              bool masked, const Ctx& x, const u32x4 (&qf)[NB][DS],
+                                              State& S) {
+    f32x16 sc[NB], sn[NB];
+    scores(sc, sm, buf, 0, x.ln, qf, S.negmu);
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const bool pending = kk + 1 < KB;
+      if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf, S.negmu);
+      if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][r] *= x.c;
+      if (kk == 0 && first) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float m = row_max(sc[qb]);
+          if (KB > 1) raise_by<false, true>(sc[qb], sn[qb], qb, m, x.inv_c, S);
+          else raise_by<false, false>(sc[qb], sn[qb], qb, m, x.inv_c, S);
+        }
+      }
+      float bs[NB][2];
+      u32x4 pf[NB][2];
+      exp_block(sc, bs, pf);
+      bool over = false;
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) over = over || !(bs[qb][0] + bs[qb][1] <= kLaneSumLimit);
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float m = row_max(sc[qb]);
+          if (m > 0.f) {
+            if (pending) raise_by<true, true>(sc[qb], sn[qb], qb, m, x.inv_c, S);
+            else raise_by<true, false>(sc[qb], sn[qb], qb, m, x.inv_c, S);
+          }
+        }
+        exp_block(sc, bs, pf);
+      }
+      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(
+              &sm.vt[buf][x.ln.vl[hs] + db * 32 * VRW + 16 * kk]);
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) S.o[qb][db] = mfma_f16(vf, pf[qb][hs], S.o[qb][db]);
+        }
+      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        S.l[qb] += bs[qb][0] + bs[qb][1];
+        if (pending) sc[qb] = sn[qb];
+      }
+    }
+  }
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
     return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
   }
 
-  // Step j with KL = 1 (K buffer of tile j+1 is B^1, V buffer of tile j is B):
-  // loads K(j+2), V(j+1); S(j+1) on the matrix cores; softmax and P.V of
-  // tile j; stores K(j+2) -> K buffer B, V(j+1) -> V buffer B^1; barrier.
-  // With KL = 0 (K and V of tile j both in buffer B): loads K(j+1), V(j+1);
-  // S(j), softmax, P.V of tile j; stores tile j+1 -> buffers B^1; barrier.
+  // Step j (K and V of tile j in buffers B): loads tile j+1 into registers;
+  // S(j), softmax and P.V of tile j; stores tile j+1 into buffers B^1;
+  // barrier.
   template <int B>
   static __device__ __forceinline__ void step(Smem& sm, const Ctx& x, State& S,
-                                              const u32x4 (&qf)[NB][DS], f32x16 (&s_cur)[NB][KB],
-                                              f32x16 (&s_nxt)[NB][KB], int j) {
+                                              const u32x4 (&qf)[NB][DS], int j) {
     KRegs kr;
     VRegs vr;
-    const bool kn = j + 1 + KL < x.ntiles, vn = j + 1 < x.ntiles;
-    if (kn) load_k(kr, x.st, x.hd, j + 1 + KL, x.tid);
-    if (vn) load_v(vr, x.st, x.hd, j + 1, x.tid);
-    if (KL == 1 && vn && !skip_tile(x, j + 1)) scores(s_nxt, sm, B ^ 1, x.ln, qf);
-    if (!skip_tile(x, j)) {
-      if (KL == 0) scores(s_cur, sm, B, x.ln, qf);
-      const int kb = j * BN;
-      const bool need_mask = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
-      softmax_pv(s_cur, sm, B, kb, j == 0, need_mask, x.nk, x.wq0, x.l32, x.hl, x.c, x.ln, S);
+    const bool nxt = j + 1 < x.ntiles;
+    if (nxt) {
+      load_k(kr, x.st, x.hd, j + 1, x.tid);
+      load_v(vr, x.st, x.hd, j + 1, x.tid);
     }
-    if (kn) store_k(sm, KL == 1 ? B : B ^ 1, kr, x.st, x.tid);
-    if (vn) store_v(sm, B ^ 1, vr, x.st, x.tid);
+    if (!skip_tile(x, j)) {
+      const int kb = j * BN;
+      const bool masked = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
+      tile(sm, B, kb, j == 0, masked, x, qf, S);
+    }
+    if (nxt) {
+      store_k(sm, B ^ 1, kr, x.st, x.tid);
+      store_v(sm, B ^ 1, vr, x.st, x.tid);
+    }
     __syncthreads();
   }
 
@@ -432,6 +487,7 @@ struct MfmaFwd {
     x.hl = lane / 32;
     x.l32 = lane % 32;
     x.c = p.c;
+    x.inv_c = p.inv_c;
 
     // ---- which tile: XCD-contiguous ranges, heads' tiles back to back
     int tile = blockIdx.x;
@@ -489,8 +545,10 @@ struct MfmaFwd {
     State S;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      S.m[qb] = 0.f;
+      S.mu[qb] = 0.f;
       S.l[qb] = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.negmu[qb][r] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -500,28 +558,20 @@ struct MfmaFwd {
     setup_staging(x.st, rs, x.tid);
     x.ln = setup_lanes(x.l32, x.hl);
 
-    // ---- prologue: K(0) (and K(1) when KL = 1) and V(0) staged; with KL = 1
-    // also S(0), then a barrier before K(0)'s buffer is reused
+    // ---- prologue: tile 0 staged
     {
-      KRegs k0, k1;
+      KRegs k0;
       VRegs v0;
       load_k(k0, x.st, x.hd, 0, x.tid);
-      if (KL == 1 && x.ntiles > 1) load_k(k1, x.st, x.hd, 1, x.tid);
       load_v(v0, x.st, x.hd, 0, x.tid);
       store_k(sm, 0, k0, x.st, x.tid);
-      if (KL == 1 && x.ntiles > 1) store_k(sm, 1, k1, x.st, x.tid);
       store_v(sm, 0, v0, x.st, x.tid);
     }
     __syncthreads();
-    f32x16 sa[NB][KB], sb[NB][KB];
-    if (KL == 1) {
-      if (!skip_tile(x, 0)) scores(sa, sm, 0, x.ln, qf);
-      __syncthreads();
-    }
 
     for (int j = 0; j < x.ntiles; j += 2) {
-      step<0>(sm, x, S, qf, sa, sb, j);
-      if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, sb, sa, j + 1);
+      step<0>(sm, x, S, qf, j);
+      if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1);
     }
 
     // ---- epilogue: normalise, store O and lse once
@@ -550,7 +600,7 @@ struct MfmaFwd {
             }
           }
         if (p.lse != nullptr && x.hl == 0) {
-          const float lse = (S.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+          const float lse = (S.mu[qb] * x.c + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
           if (VARLEN)
             p.lse[(int64_t)(p.cu[b] + qi) * p.H + h] = lse;
           else
@@ -561,9 +611,9 @@ struct MfmaFwd {
   }
 };
 
-template <bool BF16, int D, int NB, int NW, int BN, int KL, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(MfmaParams p) {
-  using K = MfmaFwd<BF16, D, NB, NW, BN, KL, CAUSAL, VARLEN, OUTF32>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -8,18 +8,17 @@ namespace sdpa {
 
 // Tile shape per head dimension: NB blocks of 32 query rows per wave, NW
 // waves, BN keys per step (overridable at build time for tuning sweeps).
-// Fourth field: KL, how far the K stream runs ahead of V (0 or 1).
 #ifndef SDPA_SHAPE_D32
-#define SDPA_SHAPE_D32 1, 4, 64, 0
+#define SDPA_SHAPE_D32 1, 4, 64
 #endif
 #ifndef SDPA_SHAPE_D64
-#define SDPA_SHAPE_D64 1, 4, 64, 0
+#define SDPA_SHAPE_D64 1, 4, 64
 #endif
 #ifndef SDPA_SHAPE_D128
-#define SDPA_SHAPE_D128 1, 4, 32, 0
+#define SDPA_SHAPE_D128 1, 4, 32
 #endif
-template <int NB_, int NW_, int BN_, int KL_> struct ShapeOf {
-  static constexpr int NB = NB_, NW = NW_, BN = BN_, KL = KL_;
+template <int NB_, int NW_, int BN_> struct ShapeOf {
+  static constexpr int NB = NB_, NW = NW_, BN = BN_;
 };
 template <int D> struct MfmaShape;
 template <> struct MfmaShape<32> : ShapeOf<SDPA_SHAPE_D32> {};
@@ -29,8 +28,7 @@ template <> struct MfmaShape<128> : ShapeOf<SDPA_SHAPE_D128> {};
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
   constexpr int NB = MfmaShape<D>::NB, NW = MfmaShape<D>::NW, BN = MfmaShape<D>::BN;
-  constexpr int KL = MfmaShape<D>::KL;
-  using K = MfmaFwd<BF16, D, NB, NW, BN, KL, CAUSAL, VARLEN, OUTF32>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>;
   MfmaParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -46,7 +44,8 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   // scale 0 is carried as a tiny positive multiplier: every visible score
   // becomes 0 to within 1e-30 relative, masked scores stay -inf
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, KL, CAUSAL, VARLEN, OUTF32>), dim3(p.total),
+  p.inv_c = 1.0f / p.c;
+  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
 }

@@ -70,6 +70,8 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   const int path = path_for(dtype, d);
   if (path < 0) return SDPA_ERR_UNSUPPORTED;
   if (scale < 0.f) return SDPA_ERR_UNSUPPORTED;
+  // the kernels work in base 2 with scale * log2(e), which must be finite
+  if (!std::isfinite(scale * 1.4426950408889634f)) return SDPA_ERR_UNSUPPORTED;
 
   // matrix-core path: one head's rows (plus a query tile of slack) must fit
   // the 32-bit byte offsets of its buffer loads

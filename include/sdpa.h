@@ -83,7 +83,8 @@ typedef enum {
  *           equal max_s(len_s); used only to size the launch grid.
  * d         head dimension, >= 1.
  * scale     multiplier of <q_i, k_j>; finite and >= 0 (1/sqrt(d) is the
- *           usual choice).
+ *           usual choice), with scale * log2(e) finite in fp32; every
+ *           scale * <q_i, k_j> must be finite in fp32.
  * is_causal 0 or 1.
  * cu_seqlens device pointer to B+1 int32 offsets, or NULL for dense.  The
  *           caller guarantees cu_seqlens[0] = 0, non-decreasing entries and
@@ -105,7 +106,8 @@ typedef enum {
  *                        dtype, packed with Nq != Nk, misaligned pointers,
  *                        or element counts overflowing int64;
  *   SDPA_ERR_UNSUPPORTED d or dtype outside the supported set, negative
- *                        scale, out_dtype other than SDPA_SAME/SDPA_F32;
+ *                        scale or scale * log2(e) above the fp32 range,
+ *                        out_dtype other than SDPA_SAME/SDPA_F32;
  *   SDPA_ERR_DEVICE      the current device is not gfx950;
  *   SDPA_ERR_LAUNCH      the kernel launch failed.
  * Nothing is launched unless SDPA_OK is returned.

@@ -83,7 +83,7 @@ def call(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=4, Nq=128, Nk=128, d=64, scale=0
     (dict(o=Q + 64), INVALID),  # output overlaps q
     (dict(d=48), UNSUPPORTED), (dict(d=16), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(dt=BF16, d=80), UNSUPPORTED), (dict(dt=F32, d=129), UNSUPPORTED),
-    (dict(scale=-0.5), UNSUPPORTED), (dict(dt=F16, odt=BF16), UNSUPPORTED),
+    (dict(scale=-0.5), UNSUPPORTED), (dict(scale=3.0e38), UNSUPPORTED), (dict(dt=F16, odt=BF16), UNSUPPORTED),
     (dict(dt=F32, odt=F16), UNSUPPORTED),
 ])
 def test_invalid_calls_rejected_on_host(lib, kw, status):
