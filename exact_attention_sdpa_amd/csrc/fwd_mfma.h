@@ -31,16 +31,15 @@
 //                      Lane l owns query l%32 and keys 8(r/4)+4(l/32)+r%4,
 //                      r = 0..15, so a row max is 15 in-lane ops plus one
 //                      v_permlane32_swap exchange with lane l^32.
-//   softmax (exp2)     each row keeps a reference mu in raw-score units; the
-//                      S accumulator is seeded with -mu, so the matrix core
-//                      returns s - mu and t = c*(s - mu) is one multiply
-//                      (c = scale*log2(e)); P = exp2(t).  The first tile sets
-//                      mu to the row maximum.  Later tiles do not compute a
-//                      maximum at all: every lane's fp32 sum of its P values
-//                      bounds each of them, and only if a sum exceeds 2^15
-//                      (an f16 P could overflow) is the tile redone with mu
-//                      raised to the new maximum.  Row sums accumulate the
-//                      fp32 P, so the logsumexp is exact to fp32 rounding.
+//   softmax (exp2)     t = s*c - m with c = scale*log2(e) and m a per-row
+//                      reference (one fma per score); P = exp2(t).  The
+//                      first 32 keys set m to their row maximum.  After that
+//                      no maximum is computed at all: every lane's fp32 sum
+//                      of its P values bounds each of them, and only if a sum
+//                      exceeds 2^15 (an f16 P could overflow) is the block
+//                      redone with m raised to the block maximum.  Row sums
+//                      accumulate the fp32 P, so the logsumexp is exact to
+//                      fp32 rounding.
 //   P                  converted to f16 straight from the accumulator
 //                      registers (no LDS round trip).
 //   O^T += V^T . P^T   A = V^T read from LDS in the key order of P's
@@ -80,7 +79,6 @@ struct MfmaParams {
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
   float c;             // scale * log2(e), at least 1e-30
-  float inv_c;         // 1 / c
 };
 
 // Build option: raise the wave priority while it issues matrix-core work
@@ -269,12 +267,10 @@ struct MfmaFwd {
       }
   }
 
-  // S^T - mu = K Q^T - mu for key block kk (32 keys) of the tile in LDS K
-  // buffer `buf`; the accumulator starts at -mu, broadcast over the lane's
-  // 16 registers.
+  // Raw scores S^T = K Q^T for key block kk (32 keys) of the tile in LDS K
+  // buffer `buf`.
   static __device__ __forceinline__ void scores(f32x16 (&s)[NB], const Smem& sm, int buf, int kk,
-                                                const Lanes& ln, const u32x4 (&qf)[NB][DS],
-                                                const f32x16 (&negmu)[NB]) {
+                                                const Lanes& ln, const u32x4 (&qf)[NB][DS]) {
     u32x4 kf[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
@@ -282,7 +278,7 @@ struct MfmaFwd {
     if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      f32x16 acc = negmu[qb];
+      f32x16 acc = {};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
         acc = BF16 ? mfma_bf16(kf[ds], qf[qb][ds], acc) : mfma_f16(kf[ds], qf[qb][ds], acc);
@@ -293,8 +289,8 @@ struct MfmaFwd {
 
   struct State {
     f32x16 o[NB][DB];
-    f32x16 negmu[NB];   // -mu broadcast (seed of the S accumulator)
-    float mu[NB], l[NB];
+    float m[NB];   // row reference, log2 units: t = s*c - m
+    float l[NB];
   };
 
   struct Ctx {
@@ -303,12 +299,16 @@ struct MfmaFwd {
     Head hd;
     int ntiles, nk, wq0, l32, hl, tid;
     bool wave_live;
-    float c, inv_c;
+    float c;
   };
+
+  static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
+    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
+  }
 
   // ---- softmax update of one tile, one block of 32 keys at a time
 
-  // Causal / key-tail mask on s - mu of the block at key kb0.
+  // Causal / key-tail mask on the raw scores of the block at key kb0.
   static __device__ __forceinline__ void mask_block(f32x16 (&s)[NB], int kb0, int nk, int wq0,
                                                     int l32, int hl) {
 #pragma unroll
@@ -323,39 +323,12 @@ struct MfmaFwd {
     }
   }
 
-  // Row maximum of t over the block (4 chains, then the lane pair l, l^32).
+  // Row maximum over the block (4 chains, then the lane pair l, l^32).
   static __device__ __forceinline__ float row_max(const f32x16& t) {
     float x[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r & 3] = fmaxf(x[r & 3], t[r]);
     return pair_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  }
-
-  // Move row qb's reference up by x (log2 units; per lane, exec-masked so
-  // the accumulators are rescaled in place): mu += x/c; the scaled block t
-  // drops by x and the pending unscaled block sn (s - mu) by x/c (both up
-  // to one rounding of x/c, far below the fp32 error of s itself); with
-  // RESCALE, l and O are scaled by 2^-x (without it they are still zero).
-  template <bool RESCALE, bool PENDING>
-  static __device__ __forceinline__ void raise_by(f32x16& t, f32x16& sn, int qb, float x,
-                                                  float inv_c, State& S) {
-    const float dmu = x * inv_c;
-    S.mu[qb] += dmu;
-    if (RESCALE) {
-      const float alpha = __builtin_amdgcn_exp2f(-x);
-      S.l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) t[r] -= x;
-    if (PENDING)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sn[r] -= dmu;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S.negmu[qb][r] = -S.mu[qb];
   }
 
   // P = exp2(t) of a block: the lane's fp32 sums (two partial sums per row)
@@ -384,36 +357,34 @@ struct MfmaFwd {
       }
   }
 
-  // One tile: for each key block kk, the products S(kk+1) are issued before
-  // the softmax of block kk (they do not depend on it) and P V of block kk
-  // after it, so the matrix cores and the vector ALUs of one wave overlap.
-  // Each P is at most its lane's block sum; a lane over the limit (rare)
-  // raises its row to the block maximum (blocks already in O are rescaled
-  // with O and l) and the block's exponentials are redone.  The first block
-  // of the first tile sets the reference to its row maximum (finite: key 0
-  // is visible to every row).
+  // One tile, one block of 32 keys at a time: the products S(kk+1) are
+  // issued before the softmax of block kk (they do not depend on it) and
+  // P V of block kk after it.
+  //   t = s*c - m (one fma per score), P = exp2(t).
+  // The first block of the first tile sets m to its row maximum (finite:
+  // key 0 is visible to every row).  After that no row maximum is taken:
+  // each P is at most its lane's block sum, so one compare per block proves
+  // that no f16 P can overflow.  A lane over the limit (rare) raises its
+  // row to the block maximum, O and l are rescaled in place, and the
+  // block's exponentials are redone.
   static __device__ __forceinline__ void tile(const Smem& sm, int buf, int kb, bool first,
                                               bool masked, const Ctx& x, const u32x4 (&qf)[NB][DS],
                                               State& S) {
     f32x16 sc[NB], sn[NB];
-    scores(sc, sm, buf, 0, x.ln, qf, S.negmu);
+    scores(sc, sm, buf, 0, x.ln, qf);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
       const bool pending = kk + 1 < KB;
-      if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf, S.negmu);
       if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+      if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf);
+      if (kk == 0 && first) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
+      }
 #pragma unroll
       for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] *= x.c;
-      if (kk == 0 && first) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          const float m = row_max(sc[qb]);
-          if (KB > 1) raise_by<false, true>(sc[qb], sn[qb], qb, m, x.inv_c, S);
-          else raise_by<false, false>(sc[qb], sn[qb], qb, m, x.inv_c, S);
-        }
-      }
+        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -S.m[qb]);
       float bs[NB][2];
       u32x4 pf[NB][2];
       exp_block(sc, bs, pf);
@@ -423,11 +394,18 @@ struct MfmaFwd {
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
-          const float m = row_max(sc[qb]);
-          if (m > 0.f) {
-            if (pending) raise_by<true, true>(sc[qb], sn[qb], qb, m, x.inv_c, S);
-            else raise_by<true, false>(sc[qb], sn[qb], qb, m, x.inv_c, S);
-          }
+          // rows with nothing to raise take y = 0 (a no-op), so no per-lane
+          // branch splits the accumulators' live ranges
+          const float y = fmaxf(row_max(sc[qb]), 0.f);
+          const float alpha = __builtin_amdgcn_exp2f(-y);
+          S.m[qb] += y;
+          S.l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[qb][r] -= y;
         }
         exp_block(sc, bs, pf);
       }
@@ -448,10 +426,6 @@ struct MfmaFwd {
         if (pending) sc[qb] = sn[qb];
       }
     }
-  }
-
-  static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
-    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
   }
 
   // Step j (K and V of tile j in buffers B): loads tile j+1 into registers;
@@ -487,7 +461,6 @@ struct MfmaFwd {
     x.hl = lane / 32;
     x.l32 = lane % 32;
     x.c = p.c;
-    x.inv_c = p.inv_c;
 
     // ---- which tile: XCD-contiguous ranges, heads' tiles back to back
     int tile = blockIdx.x;
@@ -545,10 +518,8 @@ struct MfmaFwd {
     State S;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      S.mu[qb] = 0.f;
+      S.m[qb] = 0.f;
       S.l[qb] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S.negmu[qb][r] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -600,7 +571,7 @@ struct MfmaFwd {
             }
           }
         if (p.lse != nullptr && x.hl == 0) {
-          const float lse = (S.mu[qb] * x.c + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+          const float lse = (S.m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
           if (VARLEN)
             p.lse[(int64_t)(p.cu[b] + qi) * p.H + h] = lse;
           else
@@ -611,8 +582,21 @@ struct MfmaFwd {
   }
 };
 
+// Waves per SIMD the register allocation is fitted to, per head dimension.
+#ifndef SDPA_WAVES_D32
+#define SDPA_WAVES_D32 4
+#endif
+#ifndef SDPA_WAVES_D64
+#define SDPA_WAVES_D64 4
+#endif
+#ifndef SDPA_WAVES_D128
+#define SDPA_WAVES_D128 2
+#endif
+template <int D>
+constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D64 : SDPA_WAVES_D128;
+
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(NW * 64, kWavesPerSimd<D>) void fwd_mfma_kernel(MfmaParams p) {
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);

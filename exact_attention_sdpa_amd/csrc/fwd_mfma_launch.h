@@ -44,7 +44,6 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   // scale 0 is carried as a tiny positive multiplier: every visible score
   // becomes 0 to within 1e-30 relative, masked scores stay -inf
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  p.inv_c = 1.0f / p.c;
   hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
