@@ -590,7 +590,7 @@ struct MfmaFwd {
 #define SDPA_WAVES_D64 4
 #endif
 #ifndef SDPA_WAVES_D128
-#define SDPA_WAVES_D128 2
+#define SDPA_WAVES_D128 3
 #endif
 template <int D>
 constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D64 : SDPA_WAVES_D128;

@@ -12,10 +12,10 @@ namespace sdpa {
 #define SDPA_SHAPE_D32 1, 4, 64
 #endif
 #ifndef SDPA_SHAPE_D64
-#define SDPA_SHAPE_D64 1, 4, 64
+#define SDPA_SHAPE_D64 1, 8, 64
 #endif
 #ifndef SDPA_SHAPE_D128
-#define SDPA_SHAPE_D128 1, 4, 32
+#define SDPA_SHAPE_D128 1, 8, 32
 #endif
 template <int NB_, int NW_, int BN_> struct ShapeOf {
   static constexpr int NB = NB_, NW = NW_, BN = BN_;
