@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module holds no attention arithmetic: it only draws random numbers,
 rounds them to the storage dtype, and decodes stored values back to float64
@@ -6,7 +6,8 @@ exactly.  The oracle and the GPU path both consume what it produces.
 
 Every tensor comes from ``numpy.random.default_rng(SeedSequence([seed, cfg,
 tensor_id]))`` with tensor ids q=0, k=1, v=2, lengths=3, forced index=4,
-sampled rows=5, so a workload is reproducible on any machine with no torch
+sampled rows=5, upstream gradient dO=6, so a workload is reproducible on any
+machine with no torch
 RNG involved.  Values are drawn in float32 and rounded to the storage dtype
 with round-to-nearest-even (bf16 rounding is done on the bit pattern).
 
@@ -35,7 +36,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for SeedSequence
-_TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS = 0, 1, 2, 3, 4, 5
+_TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS, _TID_DO = 0, 1, 2, 3, 4, 5, 6
 
 # largest float16 strictly below 1.0; uniform draws are clamped here so that
 # rounding to f16 never produces 1.0 (the pages' torch.rand is [0, 1)).
@@ -159,6 +160,13 @@ def make_dense(B, H, Nq, Nk, d, dtype="f16", dist="normal", is_causal=False,
                     is_causal=is_causal, scale=sc,
                     q=to_storage(q32, dtype), k=to_storage(k32, dtype),
                     v=to_storage(v32, dtype))
+
+
+def make_grad_out(w: Workload, seed=0, cfg=0, dist="normal") -> np.ndarray:
+    """Upstream gradient dO for workload ``w`` (the shape of its output), in
+    its storage dtype."""
+    shape = (w.q.shape[0], w.q.shape[1], w.q.shape[2], w.d) if not w.varlen else w.q.shape
+    return to_storage(_draw(_rng(seed, cfg, _TID_DO), shape, dist), w.dtype)
 
 
 def nested_lengths(batch: int, max_len: int, pad_fraction: float, seed=0, cfg=4) -> np.ndarray:

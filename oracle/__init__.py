@@ -1,6 +1,7 @@
-"""CPU oracle for the attention forward: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the attention forward and its gradients: TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path never does.
 """
 from .sdpa import sdpa_fwd, sdpa_fwd_rows, sdpa_fwd_varlen, attention_weights  # noqa: F401
+from .grad import sdpa_bwd, attention_grads  # noqa: F401

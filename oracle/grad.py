@@ -1,0 +1,73 @@
+"""fp64 CPU oracle for the gradients of exact attention (the backward pass).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares
+no code with the GPU path and imports nothing from it.
+
+What it computes:
+
+* The FlashAttention article (method paragraph) names two techniques: tiling
+  the forward pass, and recomputing attention in the backward pass instead
+  of keeping the N x N matrix.  The pages print no backward formulas.  What a
+  backward pass computes is fixed by calculus: for an upstream gradient dO
+  of the forward output O (oracle/sdpa.py), the gradients of
+  L = sum(dO * O) with respect to q, k and v.  The logsumexp output is an
+  auxiliary statistic and is not differentiated.
+* Written out by the chain rule, per (batch, head) unit, with
+  S = scale * q k^T (masked entries excluded) and P = softmax_rows(S):
+      dV    = P^T dO
+      dP    = dO V^T
+      dS_ij = P_ij * (dP_ij - sum_j' P_ij' dP_ij')     (Jacobian of softmax)
+      dQ    = scale * dS K
+      dK    = scale * dS^T Q
+  Masked entries have P = 0 and so contribute nothing.
+
+Inputs are upcast to float64 exactly; numpy matmul is the only library
+primitive used.  The row-maximum shift inside the softmax only guards
+against overflow.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _probs(q, k, scale, is_causal):
+    """P = softmax_rows(scale * q k^T), keys j > i excluded when causal."""
+    s = float(scale) * (q @ k.T)
+    if is_causal:
+        allowed = np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None]
+        s = np.where(allowed, s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)  # overflow guard only
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=1, keepdims=True)
+
+
+def attention_grads(q, k, v, do, scale, is_causal=False):
+    """One unit: q [nq,d], k/v [nk,d], do [nq,dv] -> (dq, dk, dv) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    p = _probs(q, k, scale, is_causal)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    dq = float(scale) * (ds @ k)
+    dk = float(scale) * (ds.T @ q)
+    return dq, dk, dv
+
+
+def sdpa_bwd(q, k, v, do, scale, is_causal=False):
+    """Dense: q/do [B,H,Nq,d], k/v [B,H,Nk,d] -> dq, dk, dv (float64)."""
+    q = np.asarray(q)
+    B, H, Nq, _ = q.shape
+    if Nq == 0 or k.shape[2] == 0:
+        raise ValueError("empty query or key set")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(v.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = attention_grads(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                           scale, is_causal)
+    return dq, dk, dv
