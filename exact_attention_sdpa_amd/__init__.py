@@ -1,13 +1,15 @@
-"""MI355X-native fused exact attention forward.
+"""MI355X-native fused exact attention, forward and backward.
 
 Thin Python binding of the C ABI in include/sdpa.h: argument marshalling
 only.  Every step of the computation runs in the HIP kernels of
 libsdpa.so; PyTorch supplies device memory and the current stream.
 
-``sdpa_fwd`` mirrors the C entry point one to one.  ``scaled_dot_product_
-attention`` is the functional form of the PyTorch SDPA tutorial ("Fused
-implementations"): it allocates the output (and optionally the logsumexp)
-and calls ``sdpa_fwd`` on the current stream.
+``sdpa_fwd`` and ``sdpa_bwd`` mirror the C entry points one to one.
+``scaled_dot_product_attention`` is the functional form of the PyTorch SDPA
+tutorial ("Fused implementations"): it allocates the output (and optionally
+the logsumexp) and calls ``sdpa_fwd`` on the current stream.
+``scaled_dot_product_attention_backward`` allocates the gradients and calls
+``sdpa_bwd``; ``attention`` wraps both in a torch.autograd.Function.
 """
 from __future__ import annotations
 
@@ -18,8 +20,9 @@ from . import _lib
 from ._lib import (SDPA_BF16, SDPA_ERR_DEVICE, SDPA_ERR_INVALID, SDPA_ERR_LAUNCH,  # noqa: F401
                    SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version",
-           "scaled_dot_product_attention", "SdpaError"]
+__all__ = ["sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+           "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
+           "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
 
 class SdpaError(RuntimeError):
@@ -27,7 +30,7 @@ class SdpaError(RuntimeError):
 
     def __init__(self, status: int):
         self.status = status
-        super().__init__(f"sdpa_fwd: {sdpa_status_str(status)} (status {status})")
+        super().__init__(f"sdpa: {sdpa_status_str(status)} (status {status})")
 
 
 def _ptr(x):
@@ -50,6 +53,23 @@ def sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, cu_seqlens, d
                              _ptr(cu_seqlens), int(dtype), int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
+
+
+def sdpa_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
+             is_causal, dtype, out_dtype, grad_dtype, stream):
+    """Call the C backward entry point (same conventions as sdpa_fwd)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(B), int(H),
+                             int(Nq), int(Nk), int(d), float(scale), int(is_causal), int(dtype),
+                             int(out_dtype), int(grad_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_bwd_workspace_bytes(B: int, H: int, Nq: int) -> int:
+    return int(_lib.lib().sdpa_bwd_workspace_bytes(int(B), int(H), int(Nq)))
 
 
 def sdpa_supports(dtype: int, d: int, is_causal: bool = False, varlen: bool = False) -> int:
@@ -148,3 +168,77 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
         if lse is not None:
             lse = lse[:, 0]
     return (out, lse) if return_lse else out
+
+
+def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
+                                          is_causal=False, scale=None, grad_dtype=None,
+                                          stream=None):
+    """Gradients (dq, dk, dv) of sum(grad_out * out) for dense inputs
+    [B,H,N,d], given the forward's out and lse.  ``grad_out`` is cast to the
+    input dtype (the matrix cores consume it); ``grad_dtype`` None keeps the
+    input dtype, torch.float32 requests f32 gradients."""
+    import torch
+    if not (query.dtype == key.dtype == value.dtype):
+        raise SdpaError(SDPA_ERR_INVALID)
+    q, k, v, o = _contig(query), _contig(key), _contig(value), _contig(out)
+    if q.dim() != 4 or k.dim() != 4 or o.shape != q.shape or grad_out.shape != q.shape:
+        raise SdpaError(SDPA_ERR_INVALID)
+    dt = _code(q.dtype)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if lse is None or lse.shape != (B, H, Nq) or lse.dtype != torch.float32:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    if gdt not in (q.dtype, torch.float32) or o.dtype not in (q.dtype, torch.float32):
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    do = _contig(grad_out.to(q.dtype))
+    lse = _contig(lse)
+    dq = torch.empty(q.shape, dtype=gdt, device=q.device)
+    dk = torch.empty(k.shape, dtype=gdt, device=q.device)
+    dv = torch.empty(v.shape, dtype=gdt, device=q.device)
+    work = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale, bool(is_causal),
+                 dt, SDPA_F32 if o.dtype != q.dtype else SDPA_SAME,
+                 SDPA_F32 if gdt != q.dtype else SDPA_SAME, stream)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, is_causal, scale):
+            out, lse = scaled_dot_product_attention(q, k, v, is_causal=is_causal, scale=scale,
+                                                    return_lse=True)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.is_causal, ctx.scale = is_causal, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = scaled_dot_product_attention_backward(
+                q, k, v, out, lse, grad_out, is_causal=ctx.is_causal, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_ATTN = None
+
+
+def attention(query, key, value, is_causal=False, scale=None):
+    """Differentiable dense attention [B,H,N,d]: the forward and backward
+    both run in the HIP kernels."""
+    global _ATTN
+    if _ATTN is None:
+        _ATTN = _autograd_function()
+    return _ATTN.apply(query, key, value, bool(is_causal), scale)

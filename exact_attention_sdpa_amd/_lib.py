@@ -12,7 +12,8 @@ SDPA_F16, SDPA_BF16, SDPA_F32, SDPA_SAME = 0, 1, 2, 255
 SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVICE = range(5)
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+           "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
 
@@ -30,6 +31,12 @@ def lib() -> ctypes.CDLL:
     L.sdpa_fwd.restype = ctypes.c_int
     L.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_bwd.restype = ctypes.c_int
+    L.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                           ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                           ctypes.c_int, vp]
+    L.sdpa_bwd_workspace_bytes.restype = i64
+    L.sdpa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     L.sdpa_supports.restype = ctypes.c_int
     L.sdpa_supports.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
     L.sdpa_status_str.restype = ctypes.c_char_p

@@ -1,0 +1,552 @@
+// Attention backward on gfx950 matrix cores (f16 / bf16 inputs).
+//
+// Method: the FlashAttention article (method paragraph) names recomputation
+// in the backward pass as its second technique: the N x N probabilities are
+// not kept from the forward pass but rebuilt tile by tile from Q, K and the
+// stored logsumexp.  The gradients are the chain rule of the exact forward
+// definition:
+//   P = exp(scale*Q K^T - lse)          (rows already normalised)
+//   dV = P^T dO,   dP = dO V^T,   D_i = <dO_i, O_i> = sum_j P_ij dP_ij
+//   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q
+//
+// Three kernels, no atomics (deterministic):
+//   rowdot   D_i = <dO_i, O_i> in fp32, one thread per row.
+//   dq       one wave per 32 query rows (lanes own queries, as in the
+//            forward): S^T = K Q^T and dP^T = V dO^T on the matrix cores,
+//            P and dS in registers, dQ^T += K^T dS^T with K^T staged in LDS
+//            in the key order of dS's registers.
+//   dkdv     one wave per 32 key rows (lanes own keys): S = Q K^T and
+//            dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS, with Q^T
+//            and dO^T staged in LDS in the query order of P's registers.
+// Matrix-core layout of v_mfma_f32_32x32x16 (measured, see the forward):
+// A lane l holds row l%32, k-slots 8(l/32)..+7; B lane l holds column l%32,
+// the same k-slots; C lane l, register r holds row 8(r/4)+4(l/32)+r%4,
+// column l%32.  Products whose k index comes from an accumulator use the
+// accumulator's register order as the k order, and the other operand is
+// staged permuted to match (vt_key_pos).
+// bf16 inputs: the transposed copies are converted to f16 and P and dS are
+// f16, so the last products run on the f16 matrix cores.
+#pragma once
+
+#include "fwd_mfma.h"
+
+namespace sdpa {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* out;        // forward output O (input dtype or f32)
+  const uint16_t* dout;   // upstream gradient dO (input dtype)
+  const float* lse;       // [B,H,Nq], natural log
+  float* dsum;            // [B,H,Nq] workspace: <dO_i, O_i>
+  void* dq;
+  void* dk;
+  void* dv;
+  int H, Nq, Nk;
+  int n_tiles;            // tiles per head of the launched kernel
+  int total;              // grid size
+  float c;                // scale * log2(e)
+  float scale;
+};
+
+// unpack 8 16-bit values (f16 or bf16) to fp32
+template <bool BF16>
+__device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      const uint32_t e = w[i];
+      x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(e & 0xffffu));
+      x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+    }
+  }
+}
+
+// ---- D_i = <dO_i, O_i>, one thread per row
+template <bool BF16, int D, bool OF32>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D; c += 8) {
+    float g[8], o[8];
+    unpack8<BF16>(*reinterpret_cast<const u32x4*>(p.dout + r * D + c), g);
+    if (OF32) {
+      const float* op = reinterpret_cast<const float*>(p.out) + r * D + c;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(op);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(op + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] = a[i];
+        o[4 + i] = b[i];
+      }
+    } else {
+      unpack8<BF16>(*reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.out) + r * D + c), o);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(g[i], o[i], acc);
+  }
+  p.dsum[r] = acc;
+}
+
+// ---- shared pieces of the two tile kernels
+
+// XCD-contiguous tile order (blocks are dispatched round-robin over the 8
+// XCDs): each XCD gets a contiguous range, so a head's tiles share an L2.
+__device__ __forceinline__ int bwd_tile_of_block(int total) {
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  return t;
+}
+
+// Buffer view of `rows` rows of a head starting at row r0; rows past `nrows`
+// read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* head, int r0, int nrows,
+                                                            int rs_bytes, int D) {
+  const int off = r0 * rs_bytes;
+  const int valid = max(((nrows - 1) * rs_bytes + D * 2) - off, 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(head) + off),
+                                           (short)0, valid, kBufferWord3);
+}
+
+// 16-byte chunk of row `row` (relative to the view), columns c..c+7
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, int row, int col, int rs_bytes) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, row * rs_bytes + col * 2, 0, 0));
+}
+
+// Two rows (2pr, 2pr+1) x 8 columns -> 8 words of the transposed copy: word
+// e holds (row 2pr, row 2pr+1) of column e, f16.
+template <bool BF16>
+__device__ __forceinline__ void store_pair_t(uint32_t* dst, int tw, u32x4 a, u32x4 b) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t x = a[w], y = b[w];
+    if (BF16) {
+      x = bf16x2_to_f16x2(x);
+      y = bf16x2_to_f16x2(y);
+    }
+    dst[(2 * w) * tw] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+    dst[(2 * w + 1) * tw] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+  }
+}
+
+// Store a d-major accumulator (lane = row of the output, registers = d) of
+// one 32-row block: rows row0 + l%32 < nrows, scaled by `mul`.
+template <bool BF16, bool GF32, int DB>
+__device__ __forceinline__ void store_rows(void* base, int64_t off0, int64_t rs, int row, int nrows,
+                                           int hl, const f32x16 (&acc)[DB], float mul) {
+  if (row >= nrows) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = db * 32 + 8 * g + 4 * hl;
+      const float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
+      const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+      const int64_t off = off0 + (int64_t)row * rs + dcol;
+      if (GF32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off) = f32x4{x0, x1, x2, x3};
+      } else {
+        const u32x2 w = BF16 ? u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)}
+                             : u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + off) = w;
+      }
+    }
+}
+
+// ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32>
+struct BwdDq {
+  static constexpr int BM = NW * 32;
+  static constexpr int KB = BN / 32;
+  static constexpr int DS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int NC = D / 8;
+  static constexpr int KROW = D + 8;            // row-major LDS row, elements
+  static constexpr int TW = BN / 2 + 4;         // transposed LDS row, words
+  static constexpr int PAIRS = (BN / 2) * NC;   // K: (2 rows x 16 bytes) tasks
+  static constexpr int VCH = BN * NC;           // V: 16-byte tasks
+  static constexpr int PPT = (PAIRS + NT - 1) / NT;
+  static constexpr int VPT = (VCH + NT - 1) / NT;
+  static_assert(BN % 32 == 0 && D % 32 == 0, "shape");
+
+  struct __attribute__((aligned(16))) Buf {
+    uint16_t k[BN * KROW];
+    uint16_t v[BN * KROW];
+    uint32_t kt[D * TW];   // K^T, f16, keys in vt_key_pos order
+  };
+  struct __attribute__((aligned(16))) Smem {
+    Buf b[2];
+  };
+  struct Regs {
+    u32x4 k0[PPT], k1[PPT], v[VPT];
+  };
+  struct Stage {
+    int kg[PPT], kl[PPT], kt[PPT], vg[VPT], vl[VPT];
+  };
+
+  static __device__ void run(const BwdParams& p, Smem& sm) {
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int l32 = lane % 32, hl = lane / 32;
+    const int tile = bwd_tile_of_block(p.total);
+    const int qt = tile % p.n_tiles, bh = tile / p.n_tiles;
+    const int nq = p.Nq, nk = p.Nk;
+    const int rs_bytes = D * 2;
+    const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
+    const int q0 = qt * BM, q0w = q0 + wave * 32;
+    const int kend = CAUSAL ? min(nk, q0 + BM) : nk;
+    const int ntiles = (kend + BN - 1) / BN;
+
+    // this wave's Q and dO rows as B operands; lse and D of its row
+    const __amdgpu_buffer_rsrc_t qr = rows_rsrc(p.q + qoff, 0, nq, rs_bytes, D);
+    const __amdgpu_buffer_rsrc_t gr = rows_rsrc(p.dout + qoff, 0, nq, rs_bytes, D);
+    u32x4 qf[DS], gf[DS];
+    const int qi = q0w + l32;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      qf[ds] = ld16(qr, qi, ds * 16 + hl * 8, rs_bytes);
+      gf[ds] = ld16(gr, qi, ds * 16 + hl * 8, rs_bytes);
+    }
+    const bool qok = qi < nq;
+    const float lse2 = qok ? p.lse[(int64_t)bh * nq + qi] * 1.4426950408889634f : 0.f;
+    const float dd = qok ? p.dsum[(int64_t)bh * nq + qi] : 0.f;
+
+    Stage st;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int t = tid + i * NT;
+      const int pr = t % (BN / 2), c = t / (BN / 2);
+      st.kg[i] = 2 * pr;
+      st.kl[i] = 2 * pr * KROW + c * 8;
+      st.kt[i] = c * 8 * TW + vt_key_pos(2 * pr) / 2;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int t = tid + i * NT;
+      st.vg[i] = t / NC;
+      st.vl[i] = (t / NC) * KROW + (t % NC) * 8;
+    }
+    auto col_of_pair = [&](int i) { return ((tid + i * NT) / (BN / 2)) * 8; };
+    auto col_of_v = [&](int i) { return ((tid + i * NT) % NC) * 8; };
+
+    auto load = [&](Regs& r, int j) {
+      const __amdgpu_buffer_rsrc_t kr = rows_rsrc(p.k + kvoff, j * BN, nk, rs_bytes, D);
+      const __amdgpu_buffer_rsrc_t vr = rows_rsrc(p.v + kvoff, j * BN, nk, rs_bytes, D);
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        if (PAIRS % NT == 0 || tid + i * NT < PAIRS) {
+          r.k0[i] = ld16(kr, st.kg[i], col_of_pair(i), rs_bytes);
+          r.k1[i] = ld16(kr, st.kg[i] + 1, col_of_pair(i), rs_bytes);
+        }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (VCH % NT == 0 || tid + i * NT < VCH) r.v[i] = ld16(vr, st.vg[i], col_of_v(i), rs_bytes);
+    };
+    auto store = [&](int buf, const Regs& r) {
+      Buf& b = sm.b[buf];
+#pragma unroll
+      for (int i = 0; i < PPT; ++i)
+        if (PAIRS % NT == 0 || tid + i * NT < PAIRS) {
+          *reinterpret_cast<u32x4*>(&b.k[st.kl[i]]) = r.k0[i];
+          *reinterpret_cast<u32x4*>(&b.k[st.kl[i] + KROW]) = r.k1[i];
+          store_pair_t<BF16>(&b.kt[st.kt[i]], TW, r.k0[i], r.k1[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (VCH % NT == 0 || tid + i * NT < VCH) *reinterpret_cast<u32x4*>(&b.v[st.vl[i]]) = r.v[i];
+    };
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    {
+      Regs r0;
+      load(r0, 0);
+      store(0, r0);
+    }
+    __syncthreads();
+
+    const int kl = l32 * KROW + hl * 8;
+    for (int j = 0; j < ntiles; ++j) {
+      const int buf = j & 1;
+      Regs rn;
+      const bool nxt = j + 1 < ntiles;
+      if (nxt) load(rn, j + 1);
+      const int kb = j * BN;
+      const bool live = !(CAUSAL && kb > q0w + 31);
+      if (live) {
+        const Buf& b = sm.b[buf];
+        const bool masked = (kb + BN > nk) || (CAUSAL && kb + BN - 1 > q0w);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          f32x16 s = {}, dp = {};
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(&b.k[kl + kk * 32 * KROW + ds * 16]);
+            const u32x4 va = *reinterpret_cast<const u32x4*>(&b.v[kl + kk * 32 * KROW + ds * 16]);
+            s = BF16 ? mfma_bf16(ka, qf[ds], s) : mfma_f16(ka, qf[ds], s);
+            dp = BF16 ? mfma_bf16(va, gf[ds], dp) : mfma_f16(va, gf[ds], dp);
+          }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+              if (key >= nk || (CAUSAL && key > qi)) s[r] = -INFINITY;
+            }
+          }
+          u32x4 dsf[2];
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * hs + 2 * i;
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], p.c, -lse2));
+              w[i] = pack_f16(p0 * (dp[r] - dd), p1 * (dp[r + 1] - dd));
+            }
+            dsf[hs] = u32x4{w[0], w[1], w[2], w[3]};
+          }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const u32x4 kta = *reinterpret_cast<const u32x4*>(
+                  &b.kt[l32 * TW + hl * 4 + 8 * hs + db * 32 * TW + 16 * kk]);
+              acc[db] = mfma_f16(kta, dsf[hs], acc[db]);
+            }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        }
+      }
+      if (nxt) store(buf ^ 1, rn);
+      __syncthreads();
+    }
+    store_rows<BF16, GF32, DB>(p.dq, qoff, D, qi, nq, hl, acc, p.scale);
+  }
+};
+
+// ---- dK, dV: one wave per 32 key rows, query tiles of BQ rows streamed
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32>
+struct BwdDkdv {
+  static constexpr int BK = NW * 32;
+  static constexpr int KB = BQ / 32;
+  static constexpr int DS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int NC = D / 8;
+  static constexpr int KROW = D + 8;
+  static constexpr int TW = BQ / 2 + 4;
+  static constexpr int PAIRS = (BQ / 2) * NC;   // Q and dO: (2 rows x 16 bytes) tasks
+  static constexpr int PPT = (PAIRS + NT - 1) / NT;
+  static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NT, "shape");
+
+  struct __attribute__((aligned(16))) Buf {
+    uint16_t q[BQ * KROW];
+    uint16_t g[BQ * KROW];     // dO rows
+    uint32_t qt[D * TW];       // Q^T, f16, queries in vt_key_pos order
+    uint32_t gt[D * TW];       // dO^T, likewise
+    float lse2[BQ];            // lse * log2(e); +inf past the last row
+    float dd[BQ];              // <dO_i, O_i>; 0 past the last row
+  };
+  struct __attribute__((aligned(16))) Smem {
+    Buf b[2];
+  };
+  struct Regs {
+    u32x4 q0[PPT], q1[PPT], g0[PPT], g1[PPT];
+    float l2, dd;
+  };
+
+  static __device__ void run(const BwdParams& p, Smem& sm) {
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int l32 = lane % 32, hl = lane / 32;
+    const int tile = bwd_tile_of_block(p.total);
+    const int kt = tile % p.n_tiles, bh = tile / p.n_tiles;
+    const int nq = p.Nq, nk = p.Nk;
+    const int rs_bytes = D * 2;
+    const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
+    const int k0 = kt * BK, k0w = k0 + wave * 32;
+    const int ki = k0w + l32;
+    const int nqt = (nq + BQ - 1) / BQ;
+    // causal: query tiles before the one holding query k0 see none of the
+    // workgroup's keys
+    const int i0 = CAUSAL ? min(k0 / BQ, nqt) : 0;
+
+    // this wave's K and V rows as B operands
+    const __amdgpu_buffer_rsrc_t kr = rows_rsrc(p.k + kvoff, 0, nk, rs_bytes, D);
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(p.v + kvoff, 0, nk, rs_bytes, D);
+    u32x4 kf[DS], vf[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      kf[ds] = ld16(kr, ki, ds * 16 + hl * 8, rs_bytes);
+      vf[ds] = ld16(vr, ki, ds * 16 + hl * 8, rs_bytes);
+    }
+
+    int pg[PPT], pl[PPT], ptl[PPT], pc[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int t = tid + i * NT;
+      const int pr = t % (BQ / 2), c = t / (BQ / 2);
+      pg[i] = 2 * pr;
+      pc[i] = c * 8;
+      pl[i] = 2 * pr * KROW + c * 8;
+      ptl[i] = c * 8 * TW + vt_key_pos(2 * pr) / 2;
+    }
+
+    auto load = [&](Regs& r, int i) {
+      const int r0 = i * BQ;
+      const __amdgpu_buffer_rsrc_t qv = rows_rsrc(p.q + qoff, r0, nq, rs_bytes, D);
+      const __amdgpu_buffer_rsrc_t gv = rows_rsrc(p.dout + qoff, r0, nq, rs_bytes, D);
+#pragma unroll
+      for (int t = 0; t < PPT; ++t)
+        if (PAIRS % NT == 0 || tid + t * NT < PAIRS) {
+          r.q0[t] = ld16(qv, pg[t], pc[t], rs_bytes);
+          r.q1[t] = ld16(qv, pg[t] + 1, pc[t], rs_bytes);
+          r.g0[t] = ld16(gv, pg[t], pc[t], rs_bytes);
+          r.g1[t] = ld16(gv, pg[t] + 1, pc[t], rs_bytes);
+        }
+      if (tid < BQ) {
+        const int row = r0 + tid;
+        const bool ok = row < nq;
+        r.l2 = ok ? p.lse[(int64_t)bh * nq + row] * 1.4426950408889634f : INFINITY;
+        r.dd = ok ? p.dsum[(int64_t)bh * nq + row] : 0.f;
+      }
+    };
+    auto store = [&](int buf, const Regs& r) {
+      Buf& b = sm.b[buf];
+#pragma unroll
+      for (int t = 0; t < PPT; ++t)
+        if (PAIRS % NT == 0 || tid + t * NT < PAIRS) {
+          *reinterpret_cast<u32x4*>(&b.q[pl[t]]) = r.q0[t];
+          *reinterpret_cast<u32x4*>(&b.q[pl[t] + KROW]) = r.q1[t];
+          *reinterpret_cast<u32x4*>(&b.g[pl[t]]) = r.g0[t];
+          *reinterpret_cast<u32x4*>(&b.g[pl[t] + KROW]) = r.g1[t];
+          store_pair_t<BF16>(&b.qt[ptl[t]], TW, r.q0[t], r.q1[t]);
+          store_pair_t<BF16>(&b.gt[ptl[t]], TW, r.g0[t], r.g1[t]);
+        }
+      if (tid < BQ) {
+        b.lse2[tid] = r.l2;
+        b.dd[tid] = r.dd;
+      }
+    };
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
+
+    if (i0 < nqt) {
+      Regs r0;
+      load(r0, i0);
+      store(0, r0);
+    }
+    __syncthreads();
+
+    const int ql = l32 * KROW + hl * 8;
+    for (int i = i0; i < nqt; ++i) {
+      const int buf = (i - i0) & 1;
+      Regs rn;
+      const bool nxt = i + 1 < nqt;
+      if (nxt) load(rn, i + 1);
+      const int qb = i * BQ;
+      const bool live = !(CAUSAL && qb + BQ - 1 < k0w);
+      if (live) {
+        const Buf& b = sm.b[buf];
+        const bool masked = CAUSAL && qb < k0w + 31;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+          f32x16 s = {}, dp = {};
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds) {
+            const u32x4 qa = *reinterpret_cast<const u32x4*>(&b.q[ql + kk * 32 * KROW + ds * 16]);
+            const u32x4 ga = *reinterpret_cast<const u32x4*>(&b.g[ql + kk * 32 * KROW + ds * 16]);
+            s = BF16 ? mfma_bf16(qa, kf[ds], s) : mfma_f16(qa, kf[ds], s);
+            dp = BF16 ? mfma_bf16(ga, vf[ds], dp) : mfma_f16(ga, vf[ds], dp);
+          }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          // lse and D of the lane's 16 query rows: register r holds query
+          // 8(r/4) + 4*hl + r%4 of the block
+          float l2[16], dq[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int idx = kk * 32 + 8 * g + 4 * hl;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&b.lse2[idx]);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(&b.dd[idx]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              l2[4 * g + e] = a[e];
+              dq[4 * g + e] = c[e];
+            }
+          }
+          if (masked) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int query = qb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+              if (ki > query) s[r] = -INFINITY;
+            }
+          }
+          u32x4 pf[2], dsf[2];
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            uint32_t wp[4], wd[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 8 * hs + 2 * e;
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2[r]));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], p.c, -l2[r + 1]));
+              wp[e] = pack_f16(p0, p1);
+              wd[e] = pack_f16(p0 * (dp[r] - dq[r]), p1 * (dp[r + 1] - dq[r + 1]));
+            }
+            pf[hs] = u32x4{wp[0], wp[1], wp[2], wp[3]};
+            dsf[hs] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+          }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const int wofs = l32 * TW + hl * 4 + 8 * hs + db * 32 * TW + 16 * kk;
+              const u32x4 ga = *reinterpret_cast<const u32x4*>(&b.gt[wofs]);
+              const u32x4 qa = *reinterpret_cast<const u32x4*>(&b.qt[wofs]);
+              dv[db] = mfma_f16(ga, pf[hs], dv[db]);
+              dk[db] = mfma_f16(qa, dsf[hs], dk[db]);
+            }
+          if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        }
+      }
+      if (nxt) store(buf ^ 1, rn);
+      __syncthreads();
+    }
+    store_rows<BF16, GF32, DB>(p.dk, kvoff, D, ki, nk, hl, dk, p.scale);
+    store_rows<BF16, GF32, DB>(p.dv, kvoff, D, ki, nk, hl, dv, 1.f);
+  }
+};
+
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
+  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32>;
+  __shared__ typename K::Smem sm;
+  K::run(p, sm);
+}
+
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams p) {
+  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32>;
+  __shared__ typename K::Smem sm;
+  K::run(p, sm);
+}
+
+}  // namespace sdpa

@@ -1,0 +1,15 @@
+// Matrix-core backward, f16 inputs: head-dim dispatch.
+#include "bwd_mfma_launch.h"
+
+namespace sdpa {
+
+hipError_t launch_bwd_mfma_f16(const BwdArgs& a) {
+  switch (a.d) {
+    case 32: return launch_bwd_d<false, 32>(a);
+    case 64: return launch_bwd_d<false, 64>(a);
+    case 128: return launch_bwd_d<false, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdpa

@@ -25,11 +25,40 @@ struct FwdArgs {
   hipStream_t stream;       // null = the null stream
 };
 
+// Validated arguments of one backward call (dense layouts only).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;          // forward output O
+  const void* dout;         // upstream gradient dO (input dtype)
+  const float* lse;         // forward logsumexp, natural log
+  void* dq;
+  void* dk;
+  void* dv;
+  float* work;              // B*H*Nq floats
+  int64_t B, H, Nq, Nk, d;
+  float scale;
+  bool causal;
+  bool out_f32;             // O is f32 (else the input type)
+  bool grad_f32;            // dq/dk/dv are f32 (else the input type)
+  sdpa_dtype dtype;         // SDPA_F16 or SDPA_BF16
+  hipStream_t stream;
+};
+
 // Host-only argument checks (no HIP calls).  Fills `a` on success.
 sdpa_status validate(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                      int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
                      sdpa_dtype out_dtype, void* stream, FwdArgs* a);
+
+// Host-only checks of a backward call.  Fills `a` on success.
+sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                         int64_t d, float scale, int is_causal, sdpa_dtype dtype,
+                         sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream,
+                         BwdArgs* a);
 
 // 1 = matrix-core path, 0 = plain f32 path, -1 = unsupported.
 int path_for(sdpa_dtype dtype, int64_t d);
@@ -38,5 +67,7 @@ int path_for(sdpa_dtype dtype, int64_t d);
 hipError_t launch_fwd_mfma_f16(const FwdArgs& a);
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_mfma_f16(const BwdArgs& a);
+hipError_t launch_bwd_mfma_bf16(const BwdArgs& a);
 
 }  // namespace sdpa

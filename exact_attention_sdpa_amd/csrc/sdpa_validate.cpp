@@ -1,4 +1,4 @@
-// Host-side argument checks of sdpa_fwd.  Makes no HIP calls, so every
+// Host-side argument checks of sdpa_fwd and sdpa_bwd.  Makes no HIP calls, so every
 // error path can be exercised without a GPU.
 #include <algorithm>
 #include <cmath>
@@ -109,6 +109,89 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->scale = scale;
   a->causal = is_causal != 0;
   a->out_f32 = out_f32;
+  a->dtype = dtype;
+  a->stream = static_cast<hipStream_t>(stream);
+  return SDPA_OK;
+}
+
+sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                         int64_t d, float scale, int is_causal, sdpa_dtype dtype,
+                         sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream,
+                         BwdArgs* a) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return SDPA_ERR_INVALID;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return SDPA_ERR_INVALID;
+  if (is_causal != 0 && is_causal != 1) return SDPA_ERR_INVALID;
+  if (dtype != SDPA_F16 && dtype != SDPA_BF16 && dtype != SDPA_F32) return SDPA_ERR_INVALID;
+  if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+  const int64_t lim = (int64_t)1 << 30;
+  if (H > lim || Nq > lim || Nk > lim || B > lim) return SDPA_ERR_INVALID;
+  int64_t rows_q, rows_k, eq, ek, tmp;
+  if (!mul_ok(B, H, &tmp) || !mul_ok(tmp, Nq, &rows_q) || !mul_ok(tmp, Nk, &rows_k) ||
+      !mul_ok(rows_q, d, &eq) || !mul_ok(rows_k, d, &ek) || eq > INT64_MAX / 4 ||
+      ek > INT64_MAX / 4)
+    return SDPA_ERR_INVALID;
+  if (tmp * ((std::max(Nq, Nk) + 31) / 32) > INT32_MAX) return SDPA_ERR_INVALID;
+  auto kind = [&](sdpa_dtype t, bool* f32) -> sdpa_status {
+    if (t == SDPA_SAME || t == dtype) {
+      *f32 = dtype == SDPA_F32;
+      return SDPA_OK;
+    }
+    if (t == SDPA_F32) {
+      *f32 = true;
+      return SDPA_OK;
+    }
+    return (t == SDPA_F16 || t == SDPA_BF16) ? SDPA_ERR_UNSUPPORTED : SDPA_ERR_INVALID;
+  };
+  bool out_f32, grad_f32;
+  sdpa_status st = kind(out_dtype, &out_f32);
+  if (st != SDPA_OK) return st;
+  st = kind(grad_dtype, &grad_f32);
+  if (st != SDPA_OK) return st;
+  // the backward runs on the matrix cores only
+  if (dtype == SDPA_F32 || path_for(dtype, d) != 1) return SDPA_ERR_UNSUPPORTED;
+  if (scale < 0.f || !std::isfinite(scale * 1.4426950408889634f)) return SDPA_ERR_UNSUPPORTED;
+  if ((std::max(Nq, Nk) + 256) * d * 2 > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 4))
+    return SDPA_ERR_INVALID;
+  // outputs must not overlap the inputs or each other
+  const int64_t ib = 2, gb = grad_f32 ? 4 : 2, obb = out_f32 ? 4 : 2;
+  const void* ins[] = {q, k, v, out, dout, lse, workspace};
+  const int64_t inb[] = {eq * ib, ek * ib, ek * ib, eq * obb, eq * ib, rows_q * 4, rows_q * 4};
+  const void* outs[] = {dq, dk, dv};
+  const int64_t outb[] = {eq * gb, ek * gb, ek * gb};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 7; ++i)
+      if (overlap(outs[o], outb[o], ins[i], inb[i])) return SDPA_ERR_INVALID;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return SDPA_ERR_INVALID;
+  }
+  for (int i = 0; i < 6; ++i)
+    if (overlap(workspace, rows_q * 4, ins[i], inb[i])) return SDPA_ERR_INVALID;
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->out = out;
+  a->dout = dout;
+  a->lse = lse;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->work = workspace;
+  a->B = B;
+  a->H = H;
+  a->Nq = Nq;
+  a->Nk = Nk;
+  a->d = d;
+  a->scale = scale;
+  a->causal = is_causal != 0;
+  a->out_f32 = out_f32;
+  a->grad_f32 = grad_f32;
   a->dtype = dtype;
   a->stream = static_cast<hipStream_t>(stream);
   return SDPA_OK;

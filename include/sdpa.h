@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 1
+#define SDPA_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -116,6 +116,47 @@ SDPA_API sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void*
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                               float scale, int is_causal, const int32_t* cu_seqlens,
                               sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
+/* Backward pass of sdpa_fwd: the gradients dq, dk, dv of sum(dout * out)
+ * with respect to q, k and v.  The FlashAttention article (method
+ * paragraph) names recomputation in the backward pass as its second
+ * technique: the attention probabilities are rebuilt tile by tile from q, k
+ * and the forward's lse instead of being stored.  What is computed is the
+ * chain rule of the forward definition above:
+ *     P = exp(s - lse),   dV = P^T dO,   dP = dO V^T,
+ *     dS = P * (dP - rowsum(dO * O)),   dQ = scale dS K,   dK = scale dS^T Q
+ * (masked pairs have P = 0).
+ *
+ * q, k, v   the forward's inputs, dense [B,H,Nq,d] / [B,H,Nk,d], dtype.
+ * out       the forward's output O [B,H,Nq,d] in out_dtype.
+ * dout      upstream gradient dO [B,H,Nq,d] in dtype.
+ * lse       the forward's logsumexp [B,H,Nq] (fp32, natural log).
+ * dq, dk, dv  outputs [B,H,Nq,d] / [B,H,Nk,d] in grad_dtype; every element
+ *           is written (keys no query attends get zero gradients).
+ * workspace B*H*Nq floats owned by the caller (sdpa_bwd_workspace_bytes);
+ *           overwritten.
+ * B, H, Nq, Nk, d, scale, is_causal  as in sdpa_fwd (dense layouts only).
+ * dtype     SDPA_F16 or SDPA_BF16; d in {32, 64, 128}.
+ * out_dtype / grad_dtype  SDPA_SAME or SDPA_F32.
+ * stream    hipStream_t, or NULL.  All pointers are device pointers, 16-byte
+ *           aligned (lse and workspace: 4-byte); outputs must not overlap
+ *           any input or each other.
+ *
+ * Returns SDPA_OK, or SDPA_ERR_INVALID / SDPA_ERR_UNSUPPORTED /
+ * SDPA_ERR_DEVICE / SDPA_ERR_LAUNCH with the meanings of sdpa_fwd (f32
+ * inputs and packed batches are unsupported).  Queues three kernels on
+ * `stream`; allocates nothing.  Nothing is launched unless SDPA_OK is
+ * returned.
+ */
+SDPA_API sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t d, float scale, int is_causal, sdpa_dtype dtype,
+                              sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
+
+/* Bytes of the workspace sdpa_bwd needs (B*H*Nq floats), or -1 if the sizes
+ * overflow.  Pure host function. */
+SDPA_API int64_t sdpa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
 
 /* 1 if (dtype, d, is_causal, varlen) is served by the matrix-core path,
  * 0 if it is served by the plain f32 path, -1 if unsupported.  Pure host

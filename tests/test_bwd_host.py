@@ -1,0 +1,63 @@
+"""sdpa_bwd on the host: malformed calls are rejected before any device work,
+and the workspace size is B*H*Nq floats."""
+import pytest
+
+from exact_attention_sdpa_amd import _lib
+
+OK, INVALID, UNSUPPORTED, LAUNCH, DEVICE = range(5)
+F16, BF16, F32, SAME = 0, 1, 2, 255
+
+# fake, well separated, 256-byte aligned addresses (never dereferenced: every
+# call here returns before any HIP call)
+BASE = {"q": 0x1000000, "k": 0x2000000, "v": 0x3000000, "o": 0x4000000, "g": 0x5000000,
+        "lse": 0x6000000, "dq": 0x7000000, "dk": 0x8000000, "dv": 0x9000000,
+        "w": 0xA000000}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def call(lib, B=2, H=4, Nq=128, Nk=128, d=64, scale=0.125, causal=0, dt=F16, odt=SAME,
+         gdt=SAME, **ptrs):
+    p = dict(BASE)
+    p.update(ptrs)
+    return lib.sdpa_bwd(p["q"], p["k"], p["v"], p["o"], p["g"], p["lse"], p["dq"], p["dk"],
+                        p["dv"], p["w"], B, H, Nq, Nk, d, scale, causal, dt, odt, gdt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(g=None), INVALID),
+    (dict(lse=None), INVALID), (dict(dq=None), INVALID), (dict(w=None), INVALID),
+    (dict(B=0), INVALID), (dict(Nk=0), INVALID), (dict(d=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(causal=3), INVALID), (dict(dt=9), INVALID),
+    (dict(odt=7), INVALID), (dict(gdt=7), INVALID),
+    (dict(q=BASE["q"] + 8), INVALID), (dict(dk=BASE["dk"] + 4), INVALID),
+    (dict(lse=BASE["lse"] + 2), INVALID),
+    (dict(dq=BASE["q"] + 256), INVALID),     # dq overlaps q
+    (dict(dv=BASE["dk"] + 512), INVALID),    # dv overlaps dk
+    (dict(w=BASE["lse"]), INVALID),          # workspace overlaps lse
+    (dict(dt=F32), UNSUPPORTED), (dict(d=48), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(scale=-1.0), UNSUPPORTED), (dict(dt=BF16, gdt=F16), UNSUPPORTED),
+    (dict(dt=F16, odt=BF16), UNSUPPORTED),
+])
+def test_invalid_bwd_calls_rejected_on_host(lib, kw, status):
+    assert call(lib, **kw) == status
+
+
+def test_workspace_bytes(lib):
+    assert lib.sdpa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert lib.sdpa_bwd_workspace_bytes(0, 3, 5) == 0
+    assert lib.sdpa_bwd_workspace_bytes(-1, 3, 5) == -1
+    assert lib.sdpa_bwd_workspace_bytes(1 << 40, 1 << 40, 1) == -1
+
+
+def test_no_device_is_reported(lib):
+    try:
+        import torch
+        if torch.cuda.device_count() > 0:
+            pytest.skip("a GPU is present")
+    except Exception:
+        pass
+    assert call(lib) == DEVICE
