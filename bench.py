@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused SDPA fwd TFLOP/s + % of MFMA fp16 peak (B32 H32 N1024 d32)"
+METRIC_BWD = "fused SDPA bwd TFLOP/s (2.5x forward FLOPs) + % of MFMA fp16 peak"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
 # the tutorial's flash-backend time for B32 H32 N1024 d32 fp16 (hardware
 # unstated): 2262.901 us -> 4*32*32*1024*1024*32 / 2262.901e-6 = 60.74 TFLOP/s
@@ -119,6 +120,38 @@ def cpu_baseline(w, budget_s: float):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": sample, "seconds": round(dt, 2),
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_bwd(w, budget_s, cfg):
+    """The fp64 gradient oracle on whole (batch, head) units of the workload,
+    until about ``budget_s`` seconds have passed (same FLOP convention as
+    the GPU line).  None for sequences too long to hold a unit's N x N
+    matrices in host memory."""
+    import numpy as np
+    import oracle
+    from exact_attention_sdpa_amd import inputs
+    if w.Nq * w.Nk > (1 << 26):
+        return None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    do = inputs.make_grad_out(w, cfg=cfg)
+    flops, n = 0.0, 0
+    t0 = time.perf_counter()
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for (b, h) in units:
+        dec = lambda x: inputs.storage_to_f64(x[b:b + 1, h:h + 1], w.dtype)
+        oracle.sdpa_bwd(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal)
+        flops += 2.5 * 4.0 * w.Nq * w.Nk * w.d / (2 if w.is_causal else 1)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def copy_calibration(torch) -> int:
@@ -243,6 +276,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="noncausal", choices=sorted(WORKLOADS))
+    ap.add_argument("--pass", dest="which", default="fwd", choices=("fwd", "bwd"),
+                    help="time the forward (default, the headline metric) or the backward "
+                         "pass (sdpa_bwd: dQ, dK, dV; dense workloads)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU work for the oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -303,6 +339,25 @@ def main(argv=None) -> int:
         if st != 0:
             raise sdpa.SdpaError(st)
 
+    if a.which == "bwd":
+        if w.varlen:
+            print("bench.py: the backward pass takes dense inputs only", file=sys.stderr)
+            return 2
+        step()   # the forward's out and lse feed the backward
+        g = up(inputs.make_grad_out(w, cfg=WORKLOADS[a.workload]))
+        gdt = torch.float32 if out_f32 else q.dtype
+        dq, dk, dv = (torch.empty(x.shape, dtype=gdt, device="cuda") for x in (q, k, v))
+        work = torch.empty((w.B, H, w.Nq), dtype=torch.float32, device="cuda")
+        bargs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), g.data_ptr(),
+                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), work.data_ptr(),
+                 w.B, H, w.Nq, w.Nk, w.d, float(w.scale), int(w.is_causal), dt, odt,
+                 sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME, handle]
+
+        def step():  # noqa: F811 -- the timed step is the backward call
+            st = L.sdpa_bwd(*bargs)
+            if st != 0:
+                raise sdpa.SdpaError(st)
+
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -333,15 +388,19 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
 
-    flops = w.flops()
+    # backward: the usual convention of 2.5x the forward's FLOPs (five
+    # products of the forward's size: S, dP, dV, dK, dQ)
+    flops = w.flops() * (2.5 if a.which == "bwd" else 1.0)
     ms_per_step = wall * 1e3 / a.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kmean * 1e-3) / 1e12
     rec = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC if a.which == "fwd" else METRIC_BWD,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(value / PAGES_FLASH_TFLOPS, 2) if a.workload == "noncausal" else None,
+        "vs_baseline": (round(value / PAGES_FLASH_TFLOPS, 2)
+                        if a.workload == "noncausal" and a.which == "fwd" else None),
         "dtype": w.dtype, "data": "synthetic", "config": describe(w, a.workload),
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "kernel_ms": {"mean": round(kmean, 4), "median_single": round(float(np.median(kern_ms)), 4),
@@ -349,10 +408,13 @@ def main(argv=None) -> int:
                       "stdev_single": round(float(np.std(kern_ms)), 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic(a.workload)},
+                     "traffic": stored_traffic(a.workload) if a.which == "fwd" else None},
     }
+    if a.which == "bwd":
+        rec["kernels"] = "rowdot + dq + dkdv (kernel_ms spans all three)"
     if a.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+        rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget) if a.which == "fwd"
+                               else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload]))
     print(json.dumps(rec), flush=True)
     return 0
 

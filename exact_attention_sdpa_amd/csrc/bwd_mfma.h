@@ -357,8 +357,8 @@ struct BwdDkdv {
     uint16_t g[BQ * KROW];     // dO rows
     uint32_t qt[D * TW];       // Q^T, f16, queries in vt_key_pos order
     uint32_t gt[D * TW];       // dO^T, likewise
-    float lse2[BQ];            // lse * log2(e); +inf past the last row
-    float dd[BQ];              // <dO_i, O_i>; 0 past the last row
+    float nl[BQ];              // -lse * log2(e) / c; -inf past the last row
+    float nd[BQ];              // -<dO_i, O_i>; 0 past the last row
   };
   struct __attribute__((aligned(16))) Smem {
     Buf b[2];
@@ -419,8 +419,8 @@ struct BwdDkdv {
       if (tid < BQ) {
         const int row = r0 + tid;
         const bool ok = row < nq;
-        r.l2 = ok ? p.lse[(int64_t)bh * nq + row] * 1.4426950408889634f : INFINITY;
-        r.dd = ok ? p.dsum[(int64_t)bh * nq + row] : 0.f;
+        r.l2 = ok ? -p.lse[(int64_t)bh * nq + row] * 1.4426950408889634f / p.c : -INFINITY;
+        r.dd = ok ? -p.dsum[(int64_t)bh * nq + row] : 0.f;
       }
     };
     auto store = [&](int buf, const Regs& r) {
@@ -436,8 +436,8 @@ struct BwdDkdv {
           store_pair_t<BF16>(&b.gt[ptl[t]], TW, r.g0[t], r.g1[t]);
         }
       if (tid < BQ) {
-        b.lse2[tid] = r.l2;
-        b.dd[tid] = r.dd;
+        b.nl[tid] = r.l2;
+        b.nd[tid] = r.dd;
       }
     };
 
@@ -467,7 +467,21 @@ struct BwdDkdv {
         const bool masked = CAUSAL && qb < k0w + 31;
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
-          f32x16 s = {}, dp = {};
+          // The accumulators start at -lse*log2(e)/c and -D of the lane's 16
+          // query rows (register r holds query 8(r/4) + 4*hl + r%4 of the
+          // block), so the matrix cores return S - lse/scale and dP - D.
+          f32x16 s, dp;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int idx = kk * 32 + 8 * g + 4 * hl;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&b.nl[idx]);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(&b.nd[idx]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              s[4 * g + e] = a[e];
+              dp[4 * g + e] = c[e];
+            }
+          }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ds = 0; ds < DS; ++ds) {
@@ -477,20 +491,6 @@ struct BwdDkdv {
             dp = BF16 ? mfma_bf16(ga, vf[ds], dp) : mfma_f16(ga, vf[ds], dp);
           }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
-          // lse and D of the lane's 16 query rows: register r holds query
-          // 8(r/4) + 4*hl + r%4 of the block
-          float l2[16], dq[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int idx = kk * 32 + 8 * g + 4 * hl;
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&b.lse2[idx]);
-            const f32x4 c = *reinterpret_cast<const f32x4*>(&b.dd[idx]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              l2[4 * g + e] = a[e];
-              dq[4 * g + e] = c[e];
-            }
-          }
           if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -505,10 +505,10 @@ struct BwdDkdv {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 8 * hs + 2 * e;
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2[r]));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], p.c, -l2[r + 1]));
+              const float p0 = __builtin_amdgcn_exp2f(s[r] * p.c);
+              const float p1 = __builtin_amdgcn_exp2f(s[r + 1] * p.c);
               wp[e] = pack_f16(p0, p1);
-              wd[e] = pack_f16(p0 * (dp[r] - dq[r]), p1 * (dp[r + 1] - dq[r + 1]));
+              wd[e] = pack_f16(p0 * dp[r], p1 * dp[r + 1]);
             }
             pf[hs] = u32x4{wp[0], wp[1], wp[2], wp[3]};
             dsf[hs] = u32x4{wd[0], wd[1], wd[2], wd[3]};
@@ -535,15 +535,26 @@ struct BwdDkdv {
   }
 };
 
+// waves per SIMD the dQ kernel's registers are fitted to
+#ifndef SDPA_BWD_DQ_WAVES_D64
+#define SDPA_BWD_DQ_WAVES_D64 4
+#endif
+template <int D>
+constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64 : 2;
+
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, kBwdDqWavesPerSimd<D>) void bwd_dq_kernel(BwdParams p) {
   using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
 
+// waves per SIMD the dK/dV kernel's registers are fitted to
+template <int D>
+constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
+
 template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, kBwdKvWavesPerSimd<D>) void bwd_dkdv_kernel(BwdParams p) {
   using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);

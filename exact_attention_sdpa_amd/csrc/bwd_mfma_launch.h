@@ -44,7 +44,8 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   p.H = (int)a.H;
   p.Nq = (int)a.Nq;
   p.Nk = (int)a.Nk;
-  p.c = a.scale * 1.4426950408889634f;
+  // scale 0 is carried as a tiny positive multiplier, as in the forward
+  p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   p.scale = a.scale;
   // D_i = <dO_i, O_i>
   const int64_t rows = a.B * a.H * a.Nq;
