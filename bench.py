@@ -38,13 +38,14 @@ PAGES_FLASH_TFLOPS = 137.438953472e9 / 2262.901e-6 / 1e12
 WORKLOADS = {"noncausal": 2, "causal": 3, "varlen": 4, "long": 5}
 
 
-def kernel_sources_digest() -> str:
-    """Hash of the HIP sources, used to tell whether stored counter results
-    still describe the current kernels."""
+def kernel_sources_digest(prefix: str = "fwd_") -> str:
+    """Hash of the HIP sources of one kernel family (file names starting with
+    ``prefix``; the forward's by default), used to tell whether stored
+    counter results still describe the current kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_sdpa_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip", ".cpp")):
+        if name.startswith(prefix) and name.endswith((".h", ".hip", ".cpp")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
