@@ -13,13 +13,20 @@ from __future__ import annotations
 import math
 
 
-def attend(q, k, v, scale, is_causal=False):
+def attend(q, k, v, scale, is_causal=False, allowed=None):
     """q: list of nq rows, k/v: lists of nk rows (sequences of floats).
+    ``allowed(i, j)``, if given, further restricts which keys row i sees; a
+    row that sees no key gets a zero output row and lse = -inf.
 
     Returns (O as list of rows, lse as list)."""
     out, lse = [], []
     for i, qi in enumerate(q):
-        keys = [j for j in range(len(k)) if (not is_causal) or j <= i]
+        keys = [j for j in range(len(k)) if ((not is_causal) or j <= i)
+                and (allowed is None or allowed(i, j))]
+        if not keys:
+            out.append([0.0] * len(v[0]))
+            lse.append(-math.inf)
+            continue
         weights = []
         for j in keys:
             dot = math.fsum(float(a) * float(b) for a, b in zip(qi, k[j]))
