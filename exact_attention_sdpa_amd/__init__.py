@@ -17,10 +17,11 @@ import math
 import warnings
 
 from . import _lib
-from ._lib import (SDPA_BF16, SDPA_ERR_DEVICE, SDPA_ERR_INVALID, SDPA_ERR_LAUNCH,  # noqa: F401
-                   SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32, SDPA_OK, SDPA_SAME)
+from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa: F401
+                   SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
+                   SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -51,6 +52,19 @@ def sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, cu_seqlens, d
     st = _lib.lib().sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H),
                              int(Nq), int(Nk), int(d), float(scale), int(is_causal),
                              _ptr(cu_seqlens), int(dtype), int(out_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_fwd_block_sparse(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, block_mask,
+                          mask_heads, dtype, out_dtype, stream):
+    """Call the block-sparse C entry point (same conventions as sdpa_fwd)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_fwd_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+        int(d), float(scale), int(is_causal), _ptr(block_mask), int(mask_heads), int(dtype),
+        int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -108,15 +122,19 @@ def _contig(t):
 def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.0,
                                  is_causal=False, scale=None, cu_seqlens=None,
                                  max_seqlen=None, out_dtype=None, return_lse=False,
-                                 stream=None):
+                                 stream=None, block_mask=None):
     """Attention forward on device tensors.
 
     Dense: query [B,H,Nq,d] (or [B,Nq,d], read as H=1), key/value
     [B,H,Nk,d].  Packed (cu_seqlens, an int32 device tensor of B+1 offsets,
     with max_seqlen): query/key/value [T,H,d].  ``out_dtype`` None keeps the
     input dtype; torch.float32 requests an f32 output.  Returns out, or
-    (out, lse) with ``return_lse``.  A mask or dropout is not supported and
-    raises, as the tutorial's backends do for inputs they cannot serve."""
+    (out, lse) with ``return_lse``.  ``block_mask`` (dense layouts only) is
+    a uint8 device tensor [Hm, ceil(Nq/128), ceil(Nk/128)] with Hm 1 or H (or
+    2-D, shared by every head): query i sees key j only where the entry of
+    (i // 128, j // 128) is nonzero; rows that see no key give zeros and
+    lse = -inf.  An elementwise mask or dropout is not supported and raises,
+    as the tutorial's backends do for inputs they cannot serve."""
     import torch
     if attn_mask is not None:
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
@@ -160,9 +178,23 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    odc = _code(odt) if odt != q.dtype else SDPA_SAME
     with torch.cuda.device(q.device):
-        sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal), cu_seqlens, dt,
-                 _code(odt) if odt != q.dtype else SDPA_SAME, stream)
+        if block_mask is not None:
+            if cu_seqlens is not None:
+                raise SdpaError(SDPA_ERR_UNSUPPORTED)
+            bm = block_mask[None] if block_mask.dim() == 2 else block_mask
+            blk = SDPA_BLOCK_SPARSE_BLOCK
+            shape = (-(-Nq // blk), -(-Nk // blk))
+            if (bm.dim() != 3 or bm.dtype != torch.uint8 or not bm.is_cuda
+                    or bm.shape[0] not in (1, H) or tuple(bm.shape[1:]) != shape):
+                raise SdpaError(SDPA_ERR_INVALID)
+            bm = bm.contiguous()
+            sdpa_fwd_block_sparse(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal),
+                                  bm, bm.shape[0], dt, odc, stream)
+        else:
+            sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal), cu_seqlens,
+                     dt, odc, stream)
     if squeeze:
         out = out[:, 0]
         if lse is not None:

@@ -10,9 +10,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 
 SDPA_F16, SDPA_BF16, SDPA_F32, SDPA_SAME = 0, 1, 2, 255
 SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVICE = range(5)
+SDPA_BLOCK_SPARSE_BLOCK = 128
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+EXPORTS = ("sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
@@ -31,6 +32,10 @@ def lib() -> ctypes.CDLL:
     L.sdpa_fwd.restype = ctypes.c_int
     L.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_fwd_block_sparse.restype = ctypes.c_int
+    L.sdpa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                        ctypes.c_float, ctypes.c_int, vp, i64, ctypes.c_int,
+                                        ctypes.c_int, vp]
     L.sdpa_bwd.restype = ctypes.c_int
     L.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,

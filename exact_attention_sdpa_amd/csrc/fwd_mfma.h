@@ -79,7 +79,15 @@ struct MfmaParams {
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
   float c;             // scale * log2(e), at least 1e-30
+  // block-sparse launches: mask [Hm][ceil(Nq/128)][ceil(Nk/128)], nonzero =
+  // the 128x128 block of (query, key) pairs is visible
+  const uint8_t* bmask;
+  int bm_hstride;      // bytes between the heads' masks (0: one mask for all)
+  int bm_nqb, bm_nkb;  // mask rows and columns
 };
+
+// Block size of block-sparse masks (query rows x keys).
+constexpr int kSparseBlock = 128;
 
 // Build option: raise the wave priority while it issues matrix-core work
 // (measured a few percent faster on MI355X).
@@ -134,7 +142,8 @@ __host__ __device__ constexpr int vt_key_pos(int k) {
   return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
+          bool BSP = false>
 struct MfmaFwd {
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
   static constexpr int KB = BN / 32;       // 32-key blocks per step
@@ -150,6 +159,8 @@ struct MfmaFwd {
   static constexpr int VPT = (VPAIRS + NT - 1) / NT;
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(BN % 32 == 0 && BN <= 128, "key block");
+  static_assert(!BSP || (kSparseBlock % BN == 0 && kSparseBlock % (NB * 32) == 0 && !VARLEN),
+                "block-sparse tiling");
 
   struct __attribute__((aligned(16))) Smem {
     uint16_t k[2][BN * KROW];
@@ -300,10 +311,23 @@ struct MfmaFwd {
     int ntiles, nk, wq0, l32, hl, tid;
     bool wave_live;
     float c;
+    const uint8_t* mrow;       // block-sparse: this wave's mask row
+    const uint8_t* mwg[2];     // block-sparse: the workgroup's mask rows
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
-    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
+    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1) ||
+           (BSP && x.mrow[(t * BN) / kSparseBlock] == 0);
+  }
+
+  // Block-sparse: first tile >= t that some wave of the workgroup needs.
+  static __device__ __forceinline__ int next_tile(const Ctx& x, int t) {
+    if (!BSP) return t;
+    for (; t < x.ntiles; ++t) {
+      const int kc = (t * BN) / kSparseBlock;
+      if ((x.mwg[0][kc] | x.mwg[1][kc]) != 0) break;
+    }
+    return t;
   }
 
   // ---- softmax update of one tile, one block of 32 keys at a time
@@ -377,14 +401,30 @@ struct MfmaFwd {
       const bool pending = kk + 1 < KB;
       if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
       if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf);
-      if (kk == 0 && first) {
+      if (BSP) {
+        // block-sparse: a row's reference is set by the first block in
+        // which it sees a key (its first visible block can be anywhere)
+        bool unset = false;
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) {
+            const float mm = row_max(sc[qb]) * x.c;
+            if (S.m[qb] == -INFINITY) S.m[qb] = mm;
+          }
+        }
+      } else if (kk == 0 && first) {
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
       }
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb)
+      for (int qb = 0; qb < NB; ++qb) {
+        // rows that have not seen a key yet have only -inf scores here
+        const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -S.m[qb]);
+        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
+      }
       float bs[NB][2];
       u32x4 pf[NB][2];
       exp_block(sc, bs, pf);
@@ -428,23 +468,23 @@ struct MfmaFwd {
     }
   }
 
-  // Step j (K and V of tile j in buffers B): loads tile j+1 into registers;
-  // S(j), softmax and P.V of tile j; stores tile j+1 into buffers B^1;
-  // barrier.
+  // Step j (K and V of tile j in buffers B): loads tile jn (the next tile
+  // to process, j+1 unless block-sparse) into registers; S(j), softmax and
+  // P.V of tile j; stores tile jn into buffers B^1; barrier.
   template <int B>
   static __device__ __forceinline__ void step(Smem& sm, const Ctx& x, State& S,
-                                              const u32x4 (&qf)[NB][DS], int j) {
+                                              const u32x4 (&qf)[NB][DS], int j, int jn) {
     KRegs kr;
     VRegs vr;
-    const bool nxt = j + 1 < x.ntiles;
+    const bool nxt = jn < x.ntiles;
     if (nxt) {
-      load_k(kr, x.st, x.hd, j + 1, x.tid);
-      load_v(vr, x.st, x.hd, j + 1, x.tid);
+      load_k(kr, x.st, x.hd, jn, x.tid);
+      load_v(vr, x.st, x.hd, jn, x.tid);
     }
     if (!skip_tile(x, j)) {
       const int kb = j * BN;
       const bool masked = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
-      tile(sm, B, kb, j == 0, masked, x, qf, S);
+      tile(sm, B, kb, !BSP && j == 0, masked, x, qf, S);
     }
     if (nxt) {
       store_k(sm, B ^ 1, kr, x.st, x.tid);
@@ -456,7 +496,7 @@ struct MfmaFwd {
   static __device__ void run(const MfmaParams& p, Smem& sm) {
     Ctx x;
     x.tid = threadIdx.x;
-    const int wave = x.tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
     const int lane = x.tid % 64;
     x.hl = lane / 32;
     x.l32 = lane % 32;
@@ -503,6 +543,13 @@ struct MfmaFwd {
     x.ntiles = (kend + BN - 1) / BN;
     x.wq0 = q0 + wave * NB * 32;   // first query row of this wave
     x.wave_live = x.wq0 < nq;
+    if (BSP) {
+      const uint8_t* hm = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride;
+      const int last = min(q0 + BM, nq) - 1;   // the workgroup's last real row
+      x.mwg[0] = hm + (int64_t)(q0 / kSparseBlock) * p.bm_nkb;
+      x.mwg[1] = hm + (int64_t)(last / kSparseBlock) * p.bm_nkb;
+      x.mrow = x.wave_live ? hm + (int64_t)(x.wq0 / kSparseBlock) * p.bm_nkb : x.mwg[0];
+    }
 
     // ---- Q rows as the B operand of S^T = K Q^T
     u32x4 qf[NB][DS];
@@ -518,7 +565,7 @@ struct MfmaFwd {
     State S;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      S.m[qb] = 0.f;
+      S.m[qb] = BSP ? -INFINITY : 0.f;
       S.l[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -529,20 +576,33 @@ struct MfmaFwd {
     setup_staging(x.st, rs, x.tid);
     x.ln = setup_lanes(x.l32, x.hl);
 
-    // ---- prologue: tile 0 staged
-    {
+    // ---- prologue: the first tile staged
+    int j = next_tile(x, 0);
+    if (j < x.ntiles) {
       KRegs k0;
       VRegs v0;
-      load_k(k0, x.st, x.hd, 0, x.tid);
-      load_v(v0, x.st, x.hd, 0, x.tid);
+      load_k(k0, x.st, x.hd, j, x.tid);
+      load_v(v0, x.st, x.hd, j, x.tid);
       store_k(sm, 0, k0, x.st, x.tid);
       store_v(sm, 0, v0, x.st, x.tid);
     }
     __syncthreads();
 
-    for (int j = 0; j < x.ntiles; j += 2) {
-      step<0>(sm, x, S, qf, j);
-      if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1);
+    if (!BSP) {
+      for (; j < x.ntiles; j += 2) {
+        step<0>(sm, x, S, qf, j, j + 1);
+        if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1, j + 2);
+      }
+    } else {
+      while (j < x.ntiles) {
+        int jn = next_tile(x, j + 1);
+        step<0>(sm, x, S, qf, j, jn);
+        if (jn >= x.ntiles) break;
+        j = jn;
+        jn = next_tile(x, j + 1);
+        step<1>(sm, x, S, qf, j, jn);
+        j = jn;
+      }
     }
 
     // ---- epilogue: normalise, store O and lse once
@@ -551,7 +611,8 @@ struct MfmaFwd {
     for (int qb = 0; qb < NB; ++qb) {
       const int qi = x.wq0 + qb * 32 + x.l32;
       const float lt = pair_sum(S.l[qb]);
-      const float inv = 1.f / lt;
+      // block-sparse rows that saw no key: O = 0, lse = -inf
+      const float inv = (BSP && !(lt > 0.f)) ? 0.f : 1.f / lt;
       if (qi < nq) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -595,9 +656,10 @@ struct MfmaFwd {
 template <int D>
 constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D64 : SDPA_WAVES_D128;
 
-template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
+          bool BSP = false>
 __global__ __launch_bounds__(NW * 64, kWavesPerSimd<D>) void fwd_mfma_kernel(MfmaParams p) {
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -4,6 +4,8 @@
 #include "fwd_mfma.h"
 #include "sdpa_internal.h"
 
+static_assert(sdpa::kSparseBlock == SDPA_BLOCK_SPARSE_BLOCK, "mask block size");
+
 namespace sdpa {
 
 // Tile shape per head dimension: NB blocks of 32 query rows per wave, NW
@@ -25,10 +27,10 @@ template <> struct MfmaShape<32> : ShapeOf<SDPA_SHAPE_D32> {};
 template <> struct MfmaShape<64> : ShapeOf<SDPA_SHAPE_D64> {};
 template <> struct MfmaShape<128> : ShapeOf<SDPA_SHAPE_D128> {};
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32>
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, bool BSP = false>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
   constexpr int NB = MfmaShape<D>::NB, NW = MfmaShape<D>::NW, BN = MfmaShape<D>::BN;
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
   MfmaParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -44,7 +46,11 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   // scale 0 is carried as a tiny positive multiplier: every visible score
   // becomes 0 to within 1e-30 relative, masked scores stay -inf
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
-  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32>), dim3(p.total),
+  p.bmask = a.bmask;
+  p.bm_nqb = (int)((a.Nq + kSparseBlock - 1) / kSparseBlock);
+  p.bm_nkb = (int)((a.Nk + kSparseBlock - 1) / kSparseBlock);
+  p.bm_hstride = a.mask_heads > 1 ? p.bm_nqb * p.bm_nkb : 0;
+  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -52,6 +58,14 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
 template <bool BF16, int D>
 hipError_t launch_mfma_d(const FwdArgs& a) {
   const bool varlen = a.cu != nullptr;
+  if (a.bmask != nullptr) {   // block-sparse: dense layouts only
+    if (varlen) return hipErrorInvalidValue;
+    if (a.causal)
+      return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, true>(a)
+                       : launch_mfma_inst<BF16, D, true, false, false, true>(a);
+    return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, true>(a)
+                     : launch_mfma_inst<BF16, D, false, false, false, true>(a);
+  }
 #define SDPA_CASE(C, V, O)                                                   \
   if (a.causal == C && varlen == V && a.out_f32 == O)                        \
     return launch_mfma_inst<BF16, D, C, V, O>(a);

@@ -23,6 +23,8 @@ struct FwdArgs {
   bool out_f32;             // out element type is f32 (else the input type)
   sdpa_dtype dtype;         // SDPA_F16, SDPA_BF16 or SDPA_F32
   hipStream_t stream;       // null = the null stream
+  const uint8_t* bmask;     // block-sparse mask, or null
+  int64_t mask_heads;       // 1 (shared) or H
 };
 
 // Validated arguments of one backward call (dense layouts only).
@@ -53,6 +55,11 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
                      sdpa_dtype out_dtype, void* stream, FwdArgs* a);
 
 // Host-only checks of a backward call.  Fills `a` on success.
+// Adds a block-sparse mask to validated forward arguments: mask non-null,
+// mask_heads 1 or H, f16/bf16 inputs, dense layout, and the mask
+// [mask_heads][ceil(Nq/128)][ceil(Nk/128)] bytes clear of out and lse.
+sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs* a);
+
 sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,

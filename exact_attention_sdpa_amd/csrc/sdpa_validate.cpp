@@ -111,6 +111,25 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->out_f32 = out_f32;
   a->dtype = dtype;
   a->stream = static_cast<hipStream_t>(stream);
+  a->bmask = nullptr;
+  a->mask_heads = 0;
+  return SDPA_OK;
+}
+
+sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs* a) {
+  if (mask == nullptr || (mask_heads != 1 && mask_heads != a->H)) return SDPA_ERR_INVALID;
+  if (a->cu != nullptr) return SDPA_ERR_INVALID;
+  if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
+  constexpr int64_t blk = SDPA_BLOCK_SPARSE_BLOCK;
+  const int64_t nqb = (a->Nq + blk - 1) / blk, nkb = (a->Nk + blk - 1) / blk;
+  int64_t mb = 0, ob = 0;
+  if (!mul_ok(mask_heads * nqb, nkb, &mb) || mb > INT32_MAX) return SDPA_ERR_INVALID;
+  if (!mul_ok(a->B * a->H * a->Nq, a->d * (a->out_f32 ? 4 : elem_bytes(a->dtype)), &ob))
+    return SDPA_ERR_INVALID;
+  if (overlap(mask, mb, a->out, ob)) return SDPA_ERR_INVALID;
+  if (a->lse && overlap(mask, mb, a->lse, a->B * a->H * a->Nq * 4)) return SDPA_ERR_INVALID;
+  a->bmask = mask;
+  a->mask_heads = mask_heads;
   return SDPA_OK;
 }
 

@@ -6,7 +6,7 @@ exactly.  The oracle and the GPU path both consume what it produces.
 
 Every tensor comes from ``numpy.random.default_rng(SeedSequence([seed, cfg,
 tensor_id]))`` with tensor ids q=0, k=1, v=2, lengths=3, forced index=4,
-sampled rows=5, upstream gradient dO=6, so a workload is reproducible on any
+sampled rows=5, upstream gradient dO=6, block mask=7, so a workload is reproducible on any
 machine with no torch
 RNG involved.  Values are drawn in float32 and rounded to the storage dtype
 with round-to-nearest-even (bf16 rounding is done on the bit pattern).
@@ -36,7 +36,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for SeedSequence
-_TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS, _TID_DO = 0, 1, 2, 3, 4, 5, 6
+_TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS, _TID_DO, _TID_MASK = range(8)
 
 # largest float16 strictly below 1.0; uniform draws are clamped here so that
 # rounding to f16 never produces 1.0 (the pages' torch.rand is [0, 1)).
@@ -208,6 +208,20 @@ def sample_rows(n: int, count: int, seed=0, cfg=5) -> np.ndarray:
     """``count`` distinct query rows of [0, n), sorted."""
     rng = _rng(seed, cfg, _TID_ROWS)
     return np.sort(rng.choice(n, size=min(count, n), replace=False)).astype(np.int64)
+
+
+def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False, seed=0,
+                    cfg=0, block=128) -> np.ndarray:
+    """uint8 block mask [heads, ceil(nq/block), ceil(nk/block)]: each entry
+    is 1 with probability ``density``, independently; with ``diagonal`` the
+    entries (i, i) are forced to 1, so every query block sees its own key
+    block."""
+    shape = (heads, -(-nq // block), -(-nk // block))
+    m = (_rng(seed, cfg, _TID_MASK).random(shape) < density).astype(np.uint8)
+    if diagonal:
+        n = min(shape[1], shape[2])
+        m[:, np.arange(n), np.arange(n)] = 1
+    return m
 
 
 CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long"}

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 2
+#define SDPA_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -116,6 +116,30 @@ SDPA_API sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void*
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                               float scale, int is_causal, const int32_t* cu_seqlens,
                               sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
+/* Block size of block-sparse masks: 128 query rows x 128 keys. */
+#define SDPA_BLOCK_SPARSE_BLOCK 128
+
+/* Block-sparse forward.  The FlashAttention article (results paragraph)
+ * benchmarks a block-sparse FlashAttention but gives no mask format; here
+ * query i may attend key j only if block_mask[h][i / 128][j / 128] is
+ * nonzero (and j <= i when is_causal).  Within the visible set the result is
+ * exact attention as in sdpa_fwd.  A row that sees no key gets O = 0 and
+ * lse = -inf.  Blocks no row of a tile needs are neither computed nor read.
+ *
+ * block_mask  device pointer, uint8 [mask_heads][ceil(Nq/128)][ceil(Nk/128)],
+ *             row-major; 0 = masked block.
+ * mask_heads  1 (one mask for every head) or H.
+ * Other arguments as sdpa_fwd, dense layouts only (no cu_seqlens), dtype
+ * SDPA_F16 or SDPA_BF16.  Returns SDPA_ERR_INVALID for a null mask or
+ * mask_heads not in {1, H}, SDPA_ERR_UNSUPPORTED for f32 inputs, otherwise
+ * as sdpa_fwd.
+ */
+SDPA_API sdpa_status sdpa_fwd_block_sparse(const void* q, const void* k, const void* v, void* out,
+                                           float* lse, int64_t B, int64_t H, int64_t Nq,
+                                           int64_t Nk, int64_t d, float scale, int is_causal,
+                                           const uint8_t* block_mask, int64_t mask_heads,
+                                           sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
 
 /* Backward pass of sdpa_fwd: the gradients dq, dk, dv of sum(dout * out)
  * with respect to q, k and v.  The FlashAttention article (method
