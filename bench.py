@@ -10,7 +10,8 @@ uniform [0,1) inputs, non-causal (the PyTorch SDPA tutorial's dispatcher
 benchmark).  Prints one JSON line.
 
 Throughput counts 4*B*H*Nq*Nk*d FLOPs per step (halved when causal; summed
-per sequence for packed batches).  `roofline.achieved` divides the same
+per sequence for packed batches; 4*d per visible (query, key) pair for the
+block-sparse workload, which calls sdpa_fwd_block_sparse).  `roofline.achieved` divides the same
 FLOPs by the kernel's own average duration from HIP events recorded around
 each launch on the launch stream; the peak is MI355X's published dense
 fp16/bf16 matrix rate, 2.5 PFLOP/s.  `cpu_baseline` times the fp64 CPU
@@ -22,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,19 +37,28 @@ PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
 # unstated): 2262.901 us -> 4*32*32*1024*1024*32 / 2262.901e-6 = 60.74 TFLOP/s
 PAGES_FLASH_TFLOPS = 137.438953472e9 / 2262.901e-6 / 1e12
 
-WORKLOADS = {"noncausal": 2, "causal": 3, "varlen": 4, "long": 5}
+WORKLOADS = {"noncausal": 2, "causal": 3, "varlen": 4, "long": 5, "block_sparse": 6}
+
+
+def _code_only(src: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (the kernel
+    sources hold no string literals that contain comment markers)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
 
 
 def kernel_sources_digest(prefix: str = "fwd_") -> str:
-    """Hash of the HIP sources of one kernel family (file names starting with
-    ``prefix``; the forward's by default), used to tell whether stored
-    counter results still describe the current kernels."""
+    """Hash of the code (comments and layout ignored) of one kernel family's
+    HIP sources (file names starting with ``prefix``; the forward's by
+    default), used to tell whether stored counter results still describe the
+    current kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_sdpa_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith(prefix) and name.endswith((".h", ".hip", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -72,6 +83,11 @@ def describe(w, name):
            "inputs": "uniform [0,1)" if name == "noncausal" else "normal(0,1)"}
     if w.varlen:
         cfg["total_rows"] = int(w.cu_seqlens[-1])
+    if w.block_mask is not None:
+        cfg["workload"] += " block-sparse"
+        cfg["block_mask"] = (f"{w.block_mask.shape[0]} x {w.block_mask.shape[1]} x "
+                             f"{w.block_mask.shape[2]} blocks of 128x128, p=1/4 + diagonal, "
+                             f"{100 * float(w.block_mask.mean()):.2f}% kept")
     return cfg
 
 
@@ -87,6 +103,8 @@ def cpu_baseline(w, budget_s: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    if w.block_mask is not None:
+        return _cpu_baseline_block_sparse(w, budget_s, threads)
     flops = 0.0
     n = 0
     t0 = time.perf_counter()
@@ -121,6 +139,35 @@ def cpu_baseline(w, budget_s: float):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": sample, "seconds": round(dt, 2),
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _cpu_baseline_block_sparse(w, budget_s, threads):
+    """The fp64 block-sparse oracle on the last 256 query rows of each
+    (batch, head) unit in turn, FLOPs counted over the visible pairs."""
+    import numpy as np
+
+    from exact_attention_sdpa_amd import inputs
+    from oracle import block_sparse as obsp
+    rows = np.arange(w.Nq - 256, w.Nq)
+    flops, n = 0.0, 0
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    t0 = time.perf_counter()
+    for (b, h) in units:
+        m = w.block_mask[h if w.block_mask.shape[0] == w.H else 0]
+        vis = obsp.visibility(w.Nq, w.Nk, m, 128, w.is_causal, rows)
+        q = inputs.storage_to_f64(w.q[b, h, rows], w.dtype)
+        k = inputs.storage_to_f64(w.k[b, h], w.dtype)
+        v = inputs.storage_to_f64(w.v[b, h], w.dtype)
+        obsp.attend_masked(q, k, v, w.scale, vis)
+        flops += 4.0 * w.d * float(vis.sum())
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units, last 256 "
+                                        f"query rows each",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline_bwd(w, budget_s, cfg):
@@ -226,7 +273,8 @@ def summarize(a) -> int:
         "",
         "Kernel trace (average over the profiled launches):",
         f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- "
-        f"python3 bench.py --workload {a.workload} --steps 20 --warmup 3 --cpu-budget 0",
+        f"python3 bench.py --workload {a.workload} --steps {a.steps} --warmup {a.warmup} "
+        f"--cpu-budget 0",
         f"  kernel:  {k['Name']}",
         f"  calls {k['Calls']}  average {avg_ns / 1e3:.2f} us  min {float(k['MinNs']) / 1e3:.2f} us"
         f"  max {float(k['MaxNs']) / 1e3:.2f} us",
@@ -340,9 +388,19 @@ def main(argv=None) -> int:
         if st != 0:
             raise sdpa.SdpaError(st)
 
+    if w.block_mask is not None:
+        bm = torch.from_numpy(np.ascontiguousarray(w.block_mask)).cuda()
+        sargs = args[:12] + [bm.data_ptr(), int(bm.shape[0]), dt, odt, handle]
+
+        def step():  # noqa: F811 -- the block-sparse entry point
+            st = L.sdpa_fwd_block_sparse(*sargs)
+            if st != 0:
+                raise sdpa.SdpaError(st)
+
     if a.which == "bwd":
-        if w.varlen:
-            print("bench.py: the backward pass takes dense inputs only", file=sys.stderr)
+        if w.varlen or w.block_mask is not None:
+            print("bench.py: the backward pass takes dense, unmasked inputs only",
+                  file=sys.stderr)
             return 2
         step()   # the forward's out and lse feed the backward
         g = up(inputs.make_grad_out(w, cfg=WORKLOADS[a.workload]))

@@ -51,6 +51,15 @@
 // of the first 32 keys are issued under the exponentials of the next 32).
 // LDS holds two K and two V buffers, filled from registers loaded one step
 // earlier, with one barrier per step.
+//
+// Block-sparse instantiation (BSP; the FlashAttention article's results
+// section benchmarks a block-sparse variant without fixing a mask format):
+// a uint8 mask over 128x128 blocks says which key blocks each block of 128
+// query rows attends.  A workgroup is then exactly one mask row (128 rows),
+// steps only through the key tiles its row keeps (found from a 64-column
+// bit set built by one ballot), and never loads the others.  A row's
+// reference m is set by the first block in which it sees a key; a row that
+// sees none writes O = 0 and lse = -inf.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -159,8 +168,10 @@ struct MfmaFwd {
   static constexpr int VPT = (VPAIRS + NT - 1) / NT;
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(BN % 32 == 0 && BN <= 128, "key block");
-  static_assert(!BSP || (kSparseBlock % BN == 0 && kSparseBlock % (NB * 32) == 0 && !VARLEN),
-                "block-sparse tiling");
+  // block-sparse: a workgroup's rows are exactly one mask row, and a key
+  // tile never straddles two mask columns
+  static_assert(!BSP || (NW * NB * 32 == kSparseBlock && kSparseBlock % BN == 0 && !VARLEN),
+                "block-sparse tile shape");
 
   struct __attribute__((aligned(16))) Smem {
     uint16_t k[2][BN * KROW];
@@ -311,21 +322,34 @@ struct MfmaFwd {
     int ntiles, nk, wq0, l32, hl, tid;
     bool wave_live;
     float c;
-    const uint8_t* mrow;       // block-sparse: this wave's mask row
-    const uint8_t* mwg[2];     // block-sparse: the workgroup's mask rows
+    const uint8_t* mrow;       // block-sparse: the workgroup's mask row
+    int nkb;                   // block-sparse: mask columns
+    int mchunk;                // block-sparse: which 64 columns mbits holds
+    uint64_t mbits;            // block-sparse: those columns, bit set = kept
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
-    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1) ||
-           (BSP && x.mrow[(t * BN) / kSparseBlock] == 0);
+    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
   }
 
-  // Block-sparse: first tile >= t that some wave of the workgroup needs.
-  static __device__ __forceinline__ int next_tile(const Ctx& x, int t) {
+  // Block-sparse: the first tile >= t whose key block the mask row keeps
+  // (>= ntiles if none).  The row is read 64 columns at a time, one byte
+  // per lane, into a wave-uniform bit set, so the scan waits on memory once
+  // per 64 columns rather than once per tile.
+  static __device__ __forceinline__ int next_tile(Ctx& x, int t) {
     if (!BSP) return t;
-    for (; t < x.ntiles; ++t) {
-      const int kc = (t * BN) / kSparseBlock;
-      if ((x.mwg[0][kc] | x.mwg[1][kc]) != 0) break;
+    constexpr int TPB = kSparseBlock / BN;   // key tiles per mask column
+    while (t < x.ntiles) {
+      const int kc = t / TPB;
+      const int chunk = kc >> 6;
+      if (chunk != x.mchunk) {
+        const int c = chunk * 64 + (int)(x.tid & 63);
+        x.mbits = __builtin_amdgcn_ballot_w64(c < x.nkb && x.mrow[c] != 0);
+        x.mchunk = chunk;
+      }
+      const uint64_t rest = x.mbits >> (kc & 63);
+      if (rest != 0) return max(t, (kc + (int)__builtin_ctzll(rest)) * TPB);
+      t = (chunk + 1) * 64 * TPB;
     }
     return t;
   }
@@ -544,11 +568,10 @@ struct MfmaFwd {
     x.wq0 = q0 + wave * NB * 32;   // first query row of this wave
     x.wave_live = x.wq0 < nq;
     if (BSP) {
-      const uint8_t* hm = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride;
-      const int last = min(q0 + BM, nq) - 1;   // the workgroup's last real row
-      x.mwg[0] = hm + (int64_t)(q0 / kSparseBlock) * p.bm_nkb;
-      x.mwg[1] = hm + (int64_t)(last / kSparseBlock) * p.bm_nkb;
-      x.mrow = x.wave_live ? hm + (int64_t)(x.wq0 / kSparseBlock) * p.bm_nkb : x.mwg[0];
+      x.mrow = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + (int64_t)qt * p.bm_nkb;
+      x.nkb = p.bm_nkb;
+      x.mchunk = -1;
+      x.mbits = 0;
     }
 
     // ---- Q rows as the B operand of S^T = K Q^T
@@ -655,10 +678,25 @@ struct MfmaFwd {
 #endif
 template <int D>
 constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D64 : SDPA_WAVES_D128;
+// the block-sparse kernels (4 waves of 128 rows: twice the staging
+// registers per lane of the 8-wave dense shapes)
+#ifndef SDPA_BSP_WAVES_D32
+#define SDPA_BSP_WAVES_D32 4
+#endif
+#ifndef SDPA_BSP_WAVES_D64
+#define SDPA_BSP_WAVES_D64 4
+#endif
+#ifndef SDPA_BSP_WAVES_D128
+#define SDPA_BSP_WAVES_D128 2
+#endif
+template <int D>
+constexpr int kBspWavesPerSimd =
+    D == 32 ? SDPA_BSP_WAVES_D32 : D == 64 ? SDPA_BSP_WAVES_D64 : SDPA_BSP_WAVES_D128;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
           bool BSP = false>
-__global__ __launch_bounds__(NW * 64, kWavesPerSimd<D>) void fwd_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(NW * 64, BSP ? kBspWavesPerSimd<D> : kWavesPerSimd<D>) void
+fwd_mfma_kernel(MfmaParams p) {
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);

@@ -1,6 +1,8 @@
 // Grid set-up and instantiation of the matrix-core forward for one head dim.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_mfma.h"
 #include "sdpa_internal.h"
 
@@ -27,9 +29,26 @@ template <> struct MfmaShape<32> : ShapeOf<SDPA_SHAPE_D32> {};
 template <> struct MfmaShape<64> : ShapeOf<SDPA_SHAPE_D64> {};
 template <> struct MfmaShape<128> : ShapeOf<SDPA_SHAPE_D128> {};
 
+// Block-sparse shapes: 128 query rows per workgroup, one mask row, so every
+// wave of a workgroup needs the same key tiles.
+#ifndef SDPA_BSP_SHAPE_D32
+#define SDPA_BSP_SHAPE_D32 1, 4, 64
+#endif
+#ifndef SDPA_BSP_SHAPE_D64
+#define SDPA_BSP_SHAPE_D64 1, 4, 32
+#endif
+#ifndef SDPA_BSP_SHAPE_D128
+#define SDPA_BSP_SHAPE_D128 1, 4, 64
+#endif
+template <int D> struct BspShape;
+template <> struct BspShape<32> : ShapeOf<SDPA_BSP_SHAPE_D32> {};
+template <> struct BspShape<64> : ShapeOf<SDPA_BSP_SHAPE_D64> {};
+template <> struct BspShape<128> : ShapeOf<SDPA_BSP_SHAPE_D128> {};
+
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, bool BSP = false>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
-  constexpr int NB = MfmaShape<D>::NB, NW = MfmaShape<D>::NW, BN = MfmaShape<D>::BN;
+  using S = std::conditional_t<BSP, BspShape<D>, MfmaShape<D>>;
+  constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
   MfmaParams p;
   p.q = static_cast<const uint16_t*>(a.q);

@@ -26,6 +26,11 @@ Workloads (each stands in for a workload printed on the pages):
 5. long      -- the 64k-token regime of the FlashAttention article's
                 benchmark paragraph on one GPU: B=1, H=16, N=65536, d=64,
                 bf16, causal; checked on 256 sampled query rows per head.
+6. block_sparse -- the block-sparse FlashAttention of the same benchmark
+                paragraph, at the same 64k-token size: B=1, H=16, N=65536,
+                d=64, bf16, non-causal, one mask per head over 128x128
+                blocks, each block kept with probability 1/4 and the
+                diagonal blocks always kept (the pages give no mask).
 """
 from __future__ import annotations
 
@@ -118,6 +123,7 @@ class Workload:
     v: np.ndarray
     cu_seqlens: Optional[np.ndarray] = None
     rows: Optional[np.ndarray] = None  # sampled query rows (dense only)
+    block_mask: Optional[np.ndarray] = None  # uint8 [Hm, nqb, nkb] (dense only)
 
     @property
     def varlen(self) -> bool:
@@ -137,7 +143,11 @@ class Workload:
 
     def flops(self) -> float:
         """Metric FLOPs: 4*B*H*Nq*Nk*d, halved when causal; varlen sums
-        4*H*len^2*d over sequences (halved when causal)."""
+        4*H*len^2*d over sequences (halved when causal); with a block mask,
+        4*d per (query, key) pair the mask leaves visible."""
+        if self.block_mask is not None:
+            return 4.0 * self.d * self.B * visible_pairs(self.block_mask, self.Nq, self.Nk,
+                                                         self.is_causal, self.H)
         if self.varlen:
             lens = np.diff(self.cu_seqlens.astype(np.int64))
             f = float(np.sum(4.0 * self.H * lens.astype(np.float64) ** 2 * self.d))
@@ -210,6 +220,26 @@ def sample_rows(n: int, count: int, seed=0, cfg=5) -> np.ndarray:
     return np.sort(rng.choice(n, size=min(count, n), replace=False)).astype(np.int64)
 
 
+def visible_pairs(mask: np.ndarray, nq: int, nk: int, is_causal: bool, heads: int,
+                  block: int = 128) -> float:
+    """Number of (query, key) pairs a block mask leaves visible, summed over
+    ``heads`` heads (a one-head mask counts once per head); causal pairs
+    need key <= query.  Bookkeeping for the FLOP count only."""
+    m = np.asarray(mask) != 0
+    rq = np.minimum(block, nq - block * np.arange(m.shape[1]))      # rows per block row
+    rk = np.minimum(block, nk - block * np.arange(m.shape[2]))      # keys per block column
+    if is_causal:
+        per = np.zeros((m.shape[1], m.shape[2]))
+        for i in range(m.shape[1]):
+            r = block * i + np.arange(rq[i])                        # query indices
+            for j in range(m.shape[2]):
+                per[i, j] = np.sum(np.clip(r - block * j + 1, 0, rk[j]))
+    else:
+        per = np.outer(rq, rk).astype(np.float64)
+    tot = float(np.sum(m * per[None]))
+    return tot * heads if m.shape[0] == 1 else tot
+
+
 def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False, seed=0,
                     cfg=0, block=128) -> np.ndarray:
     """uint8 block mask [heads, ceil(nq/block), ceil(nk/block)]: each entry
@@ -224,7 +254,8 @@ def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False
     return m
 
 
-CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long"}
+CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long",
+                6: "block_sparse"}
 
 
 def make_config(i: int, seed: int = 0) -> Workload:
@@ -244,5 +275,11 @@ def make_config(i: int, seed: int = 0) -> Workload:
         w = make_dense(1, 16, 65536, 65536, 64, "bf16", "normal", True, seed, 5,
                        name="long")
         w.rows = sample_rows(65536, 256, seed, 5)
+        return w
+    if i == 6:
+        w = make_dense(1, 16, 65536, 65536, 64, "bf16", "normal", False, seed, 6,
+                       name="block_sparse")
+        w.block_mask = make_block_mask(16, 65536, 65536, 0.25, diagonal=True, seed=seed, cfg=6)
+        w.rows = sample_rows(65536, 256, seed, 6)
         return w
     raise ValueError(f"no config {i}")

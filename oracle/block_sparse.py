@@ -39,10 +39,10 @@ def attend_masked(q, k, v, scale, allowed):
     return out, lse
 
 
-def visibility(nq, nk, mask2d, block, is_causal):
+def visibility(nq, nk, mask2d, block, is_causal, rows=None):
     """[nq, nk] boolean: mask entry of (i // block, j // block), and j <= i
-    when causal."""
-    i = np.arange(nq)[:, None]
+    when causal.  With ``rows``, only those query rows ([len(rows), nk])."""
+    i = (np.arange(nq) if rows is None else np.asarray(rows))[:, None]
     j = np.arange(nk)[None, :]
     vis = np.asarray(mask2d)[i // block, j // block] != 0
     if is_causal:

@@ -99,3 +99,17 @@ def test_large_configs_shapes():
     assert w5.q.shape == (1, 16, 65536, 64) and w5.q.dtype == np.uint16
     assert len(w5.rows) == 256 and len(np.unique(w5.rows)) == 256
     assert w5.rows.min() >= 0 and w5.rows.max() < 65536
+
+
+def test_visible_pairs_counts_the_oracle_visibility():
+    """The block-sparse FLOP count equals the number of visible pairs of the
+    oracle's visibility matrix (small shapes, ragged blocks, causal)."""
+    from oracle import block_sparse as obsp
+    for nq, nk, causal, heads in [(300, 200, False, 3), (300, 300, True, 1), (129, 257, True, 2),
+                                  (1, 130, False, 1)]:
+        m = inputs.make_block_mask(heads, nq, nk, 0.5, seed=nq, cfg=nk)
+        want = sum(int(obsp.visibility(nq, nk, m[h], 128, causal).sum()) for h in range(heads))
+        assert inputs.visible_pairs(m, nq, nk, causal, heads) == want
+        # a one-head mask counts once per head
+        assert inputs.visible_pairs(m[:1], nq, nk, causal, 4) == \
+            4 * int(obsp.visibility(nq, nk, m[0], 128, causal).sum())

@@ -102,3 +102,10 @@ def test_planted_mistakes_are_caught(mistake):
     assert not np.allclose(o, np.array(want[0]), rtol=1e-9, atol=1e-9)
     ok, _ = bs.attend_masked(q, k, v, 0.7, bs.visibility(nq, nk, m, blk, False))
     np.testing.assert_allclose(ok, np.array(want[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_visibility_rows_selects_rows():
+    m = np.random.default_rng(3).integers(0, 2, (3, 2))
+    full = bs.visibility(20, 13, m, 7, True)
+    rows = np.array([0, 6, 7, 19])
+    np.testing.assert_array_equal(bs.visibility(20, 13, m, 7, True, rows), full[rows])

@@ -129,3 +129,25 @@ def test_binding_rejects_bad_masks():
         sdpa.scaled_dot_product_attention(q32, q32, q32,
                                           block_mask=torch.ones(1, 2, 2, device="cuda",
                                                                 dtype=torch.uint8))
+
+
+def test_block_sparse_workload_full_size():
+    """The benchmarked block-sparse workload (B1 H16 N65536 d64 bf16, one
+    mask per head) in the benchmark's launch configuration, checked on its
+    256 sampled query rows in four heads."""
+    w = inputs.make_config(6)
+    q, k, v = (G.to_device(x, w.dtype) for x in (w.q, w.k, w.v))
+    bm = torch.from_numpy(w.block_mask).to("cuda")
+    out, lse = sdpa.scaled_dot_product_attention(
+        q, k, v, scale=float(w.scale), block_mask=bm, out_dtype=torch.float32,
+        return_lse=True)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(w.rows).to("cuda")
+    for h in (0, 5, 10, 15):
+        vis = obsp.visibility(w.Nq, w.Nk, w.block_mask[h], 128, False, w.rows)
+        ref, lref = obsp.attend_masked(inputs.storage_to_f64(w.q[0, h, w.rows], w.dtype),
+                                       inputs.storage_to_f64(w.k[0, h], w.dtype),
+                                       inputs.storage_to_f64(w.v[0, h], w.dtype), w.scale, vis)
+        o = out[0, h].index_select(0, rows).double().cpu().numpy()
+        ls = lse[0, h].index_select(0, rows).double().cpu().numpy()
+        _check(o, ls, ref, lref, "bf16", f"block_sparse head {h}")
