@@ -11,8 +11,9 @@ benchmark).  Prints one JSON line.
 
 Throughput counts 4*B*H*Nq*Nk*d FLOPs per step (halved when causal; summed
 per sequence for packed batches; 4*d per visible (query, key) pair for the
-block-sparse workload, which calls sdpa_fwd_block_sparse).  `roofline.achieved` divides the same
-FLOPs by the kernel's own average duration from HIP events recorded around
+block-sparse workload, which calls sdpa_fwd_block_sparse).  `--dropout P`
+times sdpa_fwd_dropout instead (same FLOPs).  `roofline.achieved` divides the
+same FLOPs by the kernel's own average duration from HIP events recorded around
 each launch on the launch stream; the peak is MI355X's published dense
 fp16/bf16 matrix rate, 2.5 PFLOP/s.  `cpu_baseline` times the fp64 CPU
 oracle on a bounded sample of the same workload.
@@ -76,13 +77,16 @@ def stored_traffic(workload: str):
     return ent.get("bytes_per_launch")
 
 
-def describe(w, name):
+def describe(w, name, dropout=0.0):
     cfg = {"workload": f"{name}: B{w.B} H{w.H} Nq{w.Nq} Nk{w.Nk} d{w.d} {w.dtype}"
                        f"{' causal' if w.is_causal else ''}{' packed' if w.varlen else ''}",
            "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.is_causal,
            "inputs": "uniform [0,1)" if name == "noncausal" else "normal(0,1)"}
     if w.varlen:
         cfg["total_rows"] = int(w.cu_seqlens[-1])
+    if dropout > 0:
+        cfg["workload"] += f" dropout p={dropout:g}"
+        cfg["dropout_p"] = dropout
     if w.block_mask is not None:
         cfg["workload"] += " block-sparse"
         cfg["block_mask"] = (f"{w.block_mask.shape[0]} x {w.block_mask.shape[1]} x "
@@ -91,9 +95,10 @@ def describe(w, name):
     return cfg
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, dropout: float = 0.0):
     """Time the fp64 oracle on whole (batch, head) units of the workload
-    until about `budget_s` seconds of CPU work, and scale to TFLOP/s."""
+    until about `budget_s` seconds of CPU work, and scale to TFLOP/s (the
+    dropout oracle when ``dropout`` > 0)."""
     import numpy as np
 
     import oracle
@@ -105,6 +110,8 @@ def cpu_baseline(w, budget_s: float):
         threads = 1
     if w.block_mask is not None:
         return _cpu_baseline_block_sparse(w, budget_s, threads)
+    if dropout > 0:
+        return _cpu_baseline_dropout(w, budget_s, threads, dropout)
     flops = 0.0
     n = 0
     t0 = time.perf_counter()
@@ -167,6 +174,30 @@ def _cpu_baseline_block_sparse(w, budget_s, threads):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units, last 256 "
                                         f"query rows each",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _cpu_baseline_dropout(w, budget_s, threads, p):
+    """The fp64 dropout oracle on whole (batch, head) units (dense
+    workloads of at most 8192 rows)."""
+    from exact_attention_sdpa_amd import inputs
+    from oracle import dropout as odrop
+    if w.varlen or w.Nq * w.Nk > (1 << 26):
+        return None
+    flops, n = 0.0, 0
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    t0 = time.perf_counter()
+    for (b, h) in units:
+        dec = lambda x: inputs.storage_to_f64(x[b, h], w.dtype)
+        odrop.attend_dropout(dec(w.q), dec(w.k), dec(w.v), w.scale, w.is_causal, p, 1, 0,
+                             b * w.H + h)
+        flops += 4.0 * w.Nq * w.Nk * w.d / (2 if w.is_causal else 1)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units",
             "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -267,13 +298,14 @@ def summarize(a) -> int:
     alg_read = (rows_q + 2 * rows_k) * w.H * w.d * el
     alg_write = rows_q * w.H * (w.d * out_el + 4)
     name = k["Name"].split("(")[0].replace("void ", "").replace("sdpa::", "")
-    tag = f"fwd_mfma_{a.workload}"
+    tag = f"fwd_mfma_{a.workload}" + ("_dropout" if a.dropout > 0 else "")
+    dflag = f" --dropout {a.dropout:g}" if a.dropout > 0 else ""
     txt = [
-        f"# {tag}: rocprofv3 summary, workload {describe(w, a.workload)['workload']}",
+        f"# {tag}: rocprofv3 summary, workload {describe(w, a.workload, a.dropout)['workload']}",
         "",
         "Kernel trace (average over the profiled launches):",
         f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- "
-        f"python3 bench.py --workload {a.workload} --steps {a.steps} --warmup {a.warmup} "
+        f"python3 bench.py --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
         f"--cpu-budget 0",
         f"  kernel:  {k['Name']}",
         f"  calls {k['Calls']}  average {avg_ns / 1e3:.2f} us  min {float(k['MinNs']) / 1e3:.2f} us"
@@ -283,7 +315,7 @@ def summarize(a) -> int:
         "",
         "HBM traffic (separate counter passes, one counter block each):",
         f"  commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
-        f"--workload {a.workload} --steps 5 --warmup 1 --cpu-budget 0",
+        f"--workload {a.workload}{dflag} --steps 5 --warmup 1 --cpu-budget 0",
         "            rocprofv3 --pmc WRITE_SIZE (same program)",
         "            rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 bench.py --calibrate-copy",
         f"  copy of 1 GiB reads FETCH_SIZE {cfetch:.0f} KiB, WRITE_SIZE {cwrite:.0f} KiB"
@@ -308,7 +340,7 @@ def summarize(a) -> int:
             old = json.load(f)
         if old.get("kernel_sources") == rec["kernel_sources"]:
             rec = old
-    rec["workloads"][a.workload] = {
+    rec["workloads"][a.workload + ("_dropout" if a.dropout > 0 else "")] = {
         "bytes_per_launch": round(read_b + write_b), "read_bytes": round(read_b),
         "write_bytes": round(write_b), "algorithmic_bytes": alg_read + alg_write,
         "avg_kernel_us": round(avg_ns / 1e3, 3), "fetch_scale": round(ffac, 5),
@@ -328,6 +360,9 @@ def main(argv=None) -> int:
     ap.add_argument("--pass", dest="which", default="fwd", choices=("fwd", "bwd"),
                     help="time the forward (default, the headline metric) or the backward "
                          "pass (sdpa_bwd: dQ, dK, dV; dense workloads)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout rate on the attention weights (sdpa_fwd_dropout; dense and "
+                         "packed workloads)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU work for the oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -388,6 +423,17 @@ def main(argv=None) -> int:
         if st != 0:
             raise sdpa.SdpaError(st)
 
+    if a.dropout > 0:
+        if w.block_mask is not None:
+            print("bench.py: dropout with a block mask is not supported", file=sys.stderr)
+            return 2
+        dargs = args[:13] + [float(a.dropout), 2023, 0, dt, odt, handle]
+
+        def step():  # noqa: F811 -- the dropout entry point
+            st = L.sdpa_fwd_dropout(*dargs)
+            if st != 0:
+                raise sdpa.SdpaError(st)
+
     if w.block_mask is not None:
         bm = torch.from_numpy(np.ascontiguousarray(w.block_mask)).cuda()
         sargs = args[:12] + [bm.data_ptr(), int(bm.shape[0]), dt, odt, handle]
@@ -398,7 +444,7 @@ def main(argv=None) -> int:
                 raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
-        if w.varlen or w.block_mask is not None:
+        if w.varlen or w.block_mask is not None or a.dropout > 0:
             print("bench.py: the backward pass takes dense, unmasked inputs only",
                   file=sys.stderr)
             return 2
@@ -460,19 +506,20 @@ def main(argv=None) -> int:
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": (round(value / PAGES_FLASH_TFLOPS, 2)
                         if a.workload == "noncausal" and a.which == "fwd" else None),
-        "dtype": w.dtype, "data": "synthetic", "config": describe(w, a.workload),
+        "dtype": w.dtype, "data": "synthetic", "config": describe(w, a.workload, a.dropout),
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS, 2),
         "kernel_ms": {"mean": round(kmean, 4), "median_single": round(float(np.median(kern_ms)), 4),
                       "min_single": round(float(np.min(kern_ms)), 4),
                       "stdev_single": round(float(np.std(kern_ms)), 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": stored_traffic(a.workload) if a.which == "fwd" else None},
+                     "traffic": (stored_traffic(a.workload + ("_dropout" if a.dropout > 0 else ""))
+                                 if a.which == "fwd" else None)},
     }
     if a.which == "bwd":
         rec["kernels"] = "rowdot + dq + dkdv (kernel_ms spans all three)"
     if a.cpu_budget > 0:
-        rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget) if a.which == "fwd"
+        rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget, a.dropout) if a.which == "fwd"
                                else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload]))
     print(json.dumps(rec), flush=True)
     return 0

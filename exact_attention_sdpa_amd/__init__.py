@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -65,6 +65,19 @@ def sdpa_fwd_block_sparse(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, 
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
         int(d), float(scale), int(is_causal), _ptr(block_mask), int(mask_heads), int(dtype),
         int(out_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_fwd_dropout(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, cu_seqlens,
+                     dropout_p, seed, offset, dtype, out_dtype, stream):
+    """Call the dropout C entry point (same conventions as sdpa_fwd)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_fwd_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+        int(d), float(scale), int(is_causal), _ptr(cu_seqlens), float(dropout_p), int(seed),
+        int(offset), int(dtype), int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -122,7 +135,8 @@ def _contig(t):
 def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.0,
                                  is_causal=False, scale=None, cu_seqlens=None,
                                  max_seqlen=None, out_dtype=None, return_lse=False,
-                                 stream=None, block_mask=None):
+                                 stream=None, block_mask=None, dropout_seed=None,
+                                 dropout_offset=0):
     """Attention forward on device tensors.
 
     Dense: query [B,H,Nq,d] (or [B,Nq,d], read as H=1), key/value
@@ -133,12 +147,17 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     a uint8 device tensor [Hm, ceil(Nq/128), ceil(Nk/128)] with Hm 1 or H (or
     2-D, shared by every head): query i sees key j only where the entry of
     (i // 128, j // 128) is nonzero; rows that see no key give zeros and
-    lse = -inf.  An elementwise mask or dropout is not supported and raises,
-    as the tutorial's backends do for inputs they cannot serve."""
+    lse = -inf.  ``dropout_p`` > 0 drops attention weights with the Philox
+    contract of sdpa_fwd_dropout, keyed by ``dropout_seed`` (drawn from
+    torch's CPU generator when None) and ``dropout_offset``.  An elementwise
+    mask, or dropout together with a block mask, is not supported and
+    raises, as the tutorial's backends do for inputs they cannot serve."""
     import torch
     if attn_mask is not None:
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
-    if dropout_p != 0.0:
+    if not 0.0 <= float(dropout_p) < 1.0:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if dropout_p > 0.0 and block_mask is not None:
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
     if not (query.dtype == key.dtype == value.dtype):
         raise SdpaError(SDPA_ERR_INVALID)
@@ -192,6 +211,11 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
             bm = bm.contiguous()
             sdpa_fwd_block_sparse(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal),
                                   bm, bm.shape[0], dt, odc, stream)
+        elif dropout_p > 0.0:
+            if dropout_seed is None:
+                dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+            sdpa_fwd_dropout(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal),
+                             cu_seqlens, dropout_p, dropout_seed, dropout_offset, dt, odc, stream)
         else:
             sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, bool(is_causal), cu_seqlens,
                      dt, odc, stream)

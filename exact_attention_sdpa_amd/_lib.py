@@ -13,8 +13,8 @@ SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVIC
 SDPA_BLOCK_SPARSE_BLOCK = 128
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
-           "sdpa_status_str", "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
+           "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
 
@@ -36,6 +36,10 @@ def lib() -> ctypes.CDLL:
     L.sdpa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                         ctypes.c_float, ctypes.c_int, vp, i64, ctypes.c_int,
                                         ctypes.c_int, vp]
+    L.sdpa_fwd_dropout.restype = ctypes.c_int
+    L.sdpa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                   ctypes.c_int, vp, ctypes.c_float, ctypes.c_uint64,
+                                   ctypes.c_uint32, ctypes.c_int, ctypes.c_int, vp]
     L.sdpa_bwd.restype = ctypes.c_int
     L.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,

@@ -65,6 +65,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "philox.h"
+
 namespace sdpa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -93,10 +95,18 @@ struct MfmaParams {
   const uint8_t* bmask;
   int bm_hstride;      // bytes between the heads' masks (0: one mask for all)
   int bm_nqb, bm_nkb;  // mask rows and columns
+  // dropout launches: keep (query i, key j) of unit u iff a 16-bit number
+  // of Philox4x32-10(key = seed, counter = (n(j), i, u, offset)) is below
+  // drop_t; kept weights are scaled by drop_scale = 1 / (1 - p)
+  uint32_t seed_lo, seed_hi, drop_offset, drop_t;
+  float drop_scale;
 };
 
 // Block size of block-sparse masks (query rows x keys).
 constexpr int kSparseBlock = 128;
+
+// Kernel variants: plain, block-sparse, dropout on the attention weights.
+enum FwdVariant : int { kPlain = 0, kBlockSparse = 1, kDropout = 2 };
 
 // Build option: raise the wave priority while it issues matrix-core work
 // (measured a few percent faster on MI355X).
@@ -152,8 +162,10 @@ __host__ __device__ constexpr int vt_key_pos(int k) {
 }
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
-          bool BSP = false>
+          int VAR = kPlain>
 struct MfmaFwd {
+  static constexpr bool BSP = VAR == kBlockSparse;
+  static constexpr bool DROP = VAR == kDropout;
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
   static constexpr int KB = BN / 32;       // 32-key blocks per step
   static constexpr int DS = D / 16;        // k-steps of S = Q K^T
@@ -326,6 +338,8 @@ struct MfmaFwd {
     int nkb;                   // block-sparse: mask columns
     int mchunk;                // block-sparse: which 64 columns mbits holds
     uint64_t mbits;            // block-sparse: those columns, bit set = kept
+    uint32_t unit;             // dropout: b*H + h (packed: sequence*H + h)
+    uint32_t seed_lo, seed_hi, doff, dt;   // dropout: key, offset, threshold
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
@@ -405,6 +419,35 @@ struct MfmaFwd {
       }
   }
 
+  // Dropout on the block of 32 keys at kb0: zero the f16 P of the dropped
+  // (query, key) pairs.  Lane (row i, half hl) holds, in pf[qb][hs] word w,
+  // keys kb0 + 16 hs + 4 hl + {0, 1, 2, 3} + 8 (w >> 1) as pairs (2(w&1),
+  // 2(w&1)+1): exactly the 8 keys of Philox call n = kb0/8 + 2 hs + hl of
+  // row i, whose output word w carries their two 16-bit numbers (low half
+  // = first key of the pair).  The row sums keep the undropped P; the
+  // 1/(1-p) scale is applied to O at the end.
+  static __device__ __forceinline__ void drop_block(u32x4 (&pf)[NB][2], int kb0, const Ctx& x) {
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) {
+      const uint32_t row = (uint32_t)(x.wq0 + qb * 32 + x.l32);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        uint32_t r[4];
+        philox4x32_10((uint32_t)(kb0 >> 3) + 2 * hs + x.hl, row, x.unit, x.doff, x.seed_lo,
+                      x.seed_hi, r);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // r16 - T has its upper 16 bits all set iff r16 < T (T <= 65536);
+          // one byte permute gathers both halves' upper bytes into the
+          // pair's mask
+          const uint32_t dlo = (r[w] & 0xffffu) - x.dt;
+          const uint32_t dhi = (r[w] >> 16) - x.dt;
+          pf[qb][hs][w] &= __builtin_amdgcn_perm(dhi, dlo, 0x07060302u);
+        }
+      }
+    }
+  }
+
   // One tile, one block of 32 keys at a time: the products S(kk+1) are
   // issued before the softmax of block kk (they do not depend on it) and
   // P V of block kk after it.
@@ -473,6 +516,7 @@ struct MfmaFwd {
         }
         exp_block(sc, bs, pf);
       }
+      if (DROP) drop_block(pf, kb + kk * 32, x);
       if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs)
@@ -567,6 +611,13 @@ struct MfmaFwd {
     x.ntiles = (kend + BN - 1) / BN;
     x.wq0 = q0 + wave * NB * 32;   // first query row of this wave
     x.wave_live = x.wq0 < nq;
+    if (DROP) {
+      x.unit = (uint32_t)bh;
+      x.seed_lo = p.seed_lo;
+      x.seed_hi = p.seed_hi;
+      x.doff = p.drop_offset;
+      x.dt = p.drop_t;
+    }
     if (BSP) {
       x.mrow = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + (int64_t)qt * p.bm_nkb;
       x.nkb = p.bm_nkb;
@@ -635,7 +686,7 @@ struct MfmaFwd {
       const int qi = x.wq0 + qb * 32 + x.l32;
       const float lt = pair_sum(S.l[qb]);
       // block-sparse rows that saw no key: O = 0, lse = -inf
-      const float inv = (BSP && !(lt > 0.f)) ? 0.f : 1.f / lt;
+      const float inv = (BSP && !(lt > 0.f)) ? 0.f : (DROP ? p.drop_scale : 1.f) / lt;
       if (qi < nq) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -692,12 +743,29 @@ constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D6
 template <int D>
 constexpr int kBspWavesPerSimd =
     D == 32 ? SDPA_BSP_WAVES_D32 : D == 64 ? SDPA_BSP_WAVES_D64 : SDPA_BSP_WAVES_D128;
+// the dropout kernels (the Philox rounds need about ten more live registers)
+#ifndef SDPA_DROP_WAVES_D32
+#define SDPA_DROP_WAVES_D32 4
+#endif
+#ifndef SDPA_DROP_WAVES_D64
+#define SDPA_DROP_WAVES_D64 3
+#endif
+#ifndef SDPA_DROP_WAVES_D128
+#define SDPA_DROP_WAVES_D128 2
+#endif
+template <int D>
+constexpr int kDropWavesPerSimd =
+    D == 32 ? SDPA_DROP_WAVES_D32 : D == 64 ? SDPA_DROP_WAVES_D64 : SDPA_DROP_WAVES_D128;
+template <int D, int VAR>
+constexpr int kVariantWavesPerSimd = VAR == kBlockSparse ? kBspWavesPerSimd<D>
+                                     : VAR == kDropout   ? kDropWavesPerSimd<D>
+                                                         : kWavesPerSimd<D>;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
-          bool BSP = false>
-__global__ __launch_bounds__(NW * 64, BSP ? kBspWavesPerSimd<D> : kWavesPerSimd<D>) void
+          int VAR = kPlain>
+__global__ __launch_bounds__(NW * 64, (kVariantWavesPerSimd<D, VAR>)) void
 fwd_mfma_kernel(MfmaParams p) {
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -45,11 +45,27 @@ template <> struct BspShape<32> : ShapeOf<SDPA_BSP_SHAPE_D32> {};
 template <> struct BspShape<64> : ShapeOf<SDPA_BSP_SHAPE_D64> {};
 template <> struct BspShape<128> : ShapeOf<SDPA_BSP_SHAPE_D128> {};
 
-template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, bool BSP = false>
+// Dropout shapes.
+#ifndef SDPA_DROP_SHAPE_D32
+#define SDPA_DROP_SHAPE_D32 SDPA_SHAPE_D32
+#endif
+#ifndef SDPA_DROP_SHAPE_D64
+#define SDPA_DROP_SHAPE_D64 SDPA_SHAPE_D64
+#endif
+#ifndef SDPA_DROP_SHAPE_D128
+#define SDPA_DROP_SHAPE_D128 SDPA_SHAPE_D128
+#endif
+template <int D> struct DropShape;
+template <> struct DropShape<32> : ShapeOf<SDPA_DROP_SHAPE_D32> {};
+template <> struct DropShape<64> : ShapeOf<SDPA_DROP_SHAPE_D64> {};
+template <> struct DropShape<128> : ShapeOf<SDPA_DROP_SHAPE_D128> {};
+
+template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, int VAR = kPlain>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
-  using S = std::conditional_t<BSP, BspShape<D>, MfmaShape<D>>;
+  using S = std::conditional_t<VAR == kBlockSparse, BspShape<D>,
+                               std::conditional_t<VAR == kDropout, DropShape<D>, MfmaShape<D>>>;
   constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   MfmaParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -69,7 +85,12 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.bm_nqb = (int)((a.Nq + kSparseBlock - 1) / kSparseBlock);
   p.bm_nkb = (int)((a.Nk + kSparseBlock - 1) / kSparseBlock);
   p.bm_hstride = a.mask_heads > 1 ? p.bm_nqb * p.bm_nkb : 0;
-  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, BSP>), dim3(p.total),
+  p.seed_lo = (uint32_t)(a.drop_seed & 0xffffffffu);
+  p.seed_hi = (uint32_t)(a.drop_seed >> 32);
+  p.drop_offset = a.drop_offset;
+  p.drop_t = a.drop_t;
+  p.drop_scale = a.drop_scale;
+  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -80,10 +101,24 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
   if (a.bmask != nullptr) {   // block-sparse: dense layouts only
     if (varlen) return hipErrorInvalidValue;
     if (a.causal)
-      return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, true>(a)
-                       : launch_mfma_inst<BF16, D, true, false, false, true>(a);
-    return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, true>(a)
-                     : launch_mfma_inst<BF16, D, false, false, false, true>(a);
+      return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, kBlockSparse>(a)
+                       : launch_mfma_inst<BF16, D, true, false, false, kBlockSparse>(a);
+    return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, kBlockSparse>(a)
+                     : launch_mfma_inst<BF16, D, false, false, false, kBlockSparse>(a);
+  }
+  if (a.dropout) {
+#define SDPA_DCASE(C, V, O)                                                  \
+    if (a.causal == C && varlen == V && a.out_f32 == O)                      \
+      return launch_mfma_inst<BF16, D, C, V, O, kDropout>(a);
+    SDPA_DCASE(false, false, false)
+    SDPA_DCASE(false, false, true)
+    SDPA_DCASE(false, true, false)
+    SDPA_DCASE(false, true, true)
+    SDPA_DCASE(true, false, false)
+    SDPA_DCASE(true, false, true)
+    SDPA_DCASE(true, true, false)
+    SDPA_DCASE(true, true, true)
+#undef SDPA_DCASE
   }
 #define SDPA_CASE(C, V, O)                                                   \
   if (a.causal == C && varlen == V && a.out_f32 == O)                        \

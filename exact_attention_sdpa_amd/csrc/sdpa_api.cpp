@@ -62,6 +62,23 @@ sdpa_status sdpa_fwd_block_sparse(const void* q, const void* k, const void* v, v
   return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+sdpa_status sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                             int is_causal, const int32_t* cu_seqlens, float dropout_p,
+                             uint64_t seed, uint32_t offset, sdpa_dtype dtype,
+                             sdpa_dtype out_dtype, void* stream) {
+  sdpa::FwdArgs a;
+  const sdpa_status st = sdpa::validate(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal,
+                                        cu_seqlens, dtype, out_dtype, stream, &a);
+  if (st != SDPA_OK) return st;
+  const sdpa_status sd = sdpa::validate_dropout(dropout_p, seed, offset, &a);
+  if (sd != SDPA_OK) return sd;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  const hipError_t e =
+      dtype == SDPA_BF16 ? sdpa::launch_fwd_mfma_bf16(a) : sdpa::launch_fwd_mfma_f16(a);
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* out,
                      const void* dout, const float* lse, void* dq, void* dk, void* dv,
                      float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,

@@ -25,6 +25,11 @@ struct FwdArgs {
   hipStream_t stream;       // null = the null stream
   const uint8_t* bmask;     // block-sparse mask, or null
   int64_t mask_heads;       // 1 (shared) or H
+  bool dropout;             // dropout on the attention weights
+  uint64_t drop_seed;       // Philox key
+  uint32_t drop_offset;     // last Philox counter word
+  uint32_t drop_t;          // keep iff the 16-bit number < drop_t
+  float drop_scale;         // 1 / (1 - p)
 };
 
 // Validated arguments of one backward call (dense layouts only).
@@ -59,6 +64,11 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
 // mask_heads 1 or H, f16/bf16 inputs, dense layout, and the mask
 // [mask_heads][ceil(Nq/128)][ceil(Nk/128)] bytes clear of out and lse.
 sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs* a);
+
+// Adds dropout to validated forward arguments: 0 <= p < 1 (p = 0 leaves the
+// plain kernel), f16/bf16 inputs; the keep threshold floor((1-p) 65536 + 1/2)
+// and the scale 1/(1-p) are computed here, in double.
+sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a);
 
 sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,

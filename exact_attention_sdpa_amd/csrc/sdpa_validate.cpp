@@ -113,6 +113,11 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->stream = static_cast<hipStream_t>(stream);
   a->bmask = nullptr;
   a->mask_heads = 0;
+  a->dropout = false;
+  a->drop_seed = 0;
+  a->drop_offset = 0;
+  a->drop_t = 65536;
+  a->drop_scale = 1.f;
   return SDPA_OK;
 }
 
@@ -130,6 +135,19 @@ sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs
   if (a->lse && overlap(mask, mb, a->lse, a->B * a->H * a->Nq * 4)) return SDPA_ERR_INVALID;
   a->bmask = mask;
   a->mask_heads = mask_heads;
+  return SDPA_OK;
+}
+
+sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a) {
+  if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;   // NaN fails too
+  if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
+  if (p == 0.f) return SDPA_OK;   // no dropout: the plain kernel
+  const double keep = 1.0 - (double)p;
+  a->dropout = true;
+  a->drop_seed = seed;
+  a->drop_offset = offset;
+  a->drop_t = (uint32_t)std::floor(keep * 65536.0 + 0.5);
+  a->drop_scale = (float)(1.0 / keep);
   return SDPA_OK;
 }
 

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 3
+#define SDPA_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -140,6 +140,31 @@ SDPA_API sdpa_status sdpa_fwd_block_sparse(const void* q, const void* k, const v
                                            int64_t Nk, int64_t d, float scale, int is_causal,
                                            const uint8_t* block_mask, int64_t mask_heads,
                                            sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
+/* Forward with dropout on the attention weights (the SDPA tutorial's
+ * CausalSelfAttention passes its dropout rate to the functional call in
+ * training).  Each softmax weight P_ij is kept with probability 1 - p and
+ * kept weights are divided by 1 - p:
+ *     O_i = sum_j P_ij z_ij / (1 - p) v_j;   lse as sdpa_fwd (undropped).
+ * z comes from Philox4x32-10 (Salmon et al., SC 2011), key = (seed low 32
+ * bits, seed high 32 bits), counter = (n(j), i, u, offset) with
+ * u = b*H + h (packed: sequence*H + h, i counted from the sequence start),
+ * n(j) = 2*(j >> 4) + ((j >> 2) & 1); the 16-bit half e(j) =
+ * 4*((j >> 3) & 1) + (j & 3) of the output (word e >> 1, bits 16*(e & 1)..)
+ * is compared with T = floor((1 - p) * 65536 + 1/2): kept iff below.  The
+ * same (seed, offset) gives the same mask on every call.
+ *
+ * dropout_p  0 <= p < 1 (else SDPA_ERR_INVALID); p = 0 is exactly sdpa_fwd.
+ * seed, offset  as above.
+ * Other arguments as sdpa_fwd; dtype SDPA_F16 or SDPA_BF16 (SDPA_F32:
+ * SDPA_ERR_UNSUPPORTED).
+ */
+SDPA_API sdpa_status sdpa_fwd_dropout(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                      int64_t d, float scale, int is_causal,
+                                      const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                                      uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                      void* stream);
 
 /* Backward pass of sdpa_fwd: the gradients dq, dk, dv of sum(dout * out)
  * with respect to q, k and v.  The FlashAttention article (method

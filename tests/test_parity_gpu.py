@@ -284,8 +284,11 @@ def test_unsupported_raises():
     q = torch.zeros(1, 1, 8, 48, dtype=torch.float16, device="cuda")
     with pytest.raises(S.SdpaError):
         S.scaled_dot_product_attention(q, q, q)
-    with pytest.raises(S.SdpaError):
-        S.scaled_dot_product_attention(q[..., :32], q[..., :32], q[..., :32], dropout_p=0.1)
+    with pytest.raises(S.SdpaError):     # p must be below 1
+        S.scaled_dot_product_attention(q[..., :32], q[..., :32], q[..., :32], dropout_p=1.0)
+    with pytest.raises(S.SdpaError):     # dropout needs f16/bf16 inputs
+        q32 = q[..., :32].float()
+        S.scaled_dot_product_attention(q32, q32, q32, dropout_p=0.1)
     with pytest.raises(S.SdpaError):
         S.scaled_dot_product_attention(q[..., :32], q[..., :32], q[..., :32],
                                        attn_mask=torch.ones(8, 8, device="cuda"))
