@@ -71,3 +71,40 @@ def sdpa_bwd(q, k, v, do, scale, is_causal=False):
             dq[b, h], dk[b, h], dv[b, h] = attention_grads(q[b, h], k[b, h], v[b, h], do[b, h],
                                                            scale, is_causal)
     return dq, dk, dv
+
+
+def attention_grads_dropout(q, k, v, do, scale, is_causal, p, seed, offset, unit):
+    """Gradients of L = sum(dO * O) for the dropout forward of
+    oracle/dropout.py, whose mask z (fixed by seed, offset and the unit
+    index) is a constant: O = (P * z / (1 - p)) V.  By the chain rule, with
+    W = P * z / (1 - p):
+        dV    = W^T dO
+        dW    = dO V^T,  dP = dW * z / (1 - p)
+        dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+        dQ    = scale dS K,  dK = scale dS^T Q
+    (sum_j' P_ij' dP_ij' = <dO_i, O_i>, as without dropout.)"""
+    from .dropout import keep_mask
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    P = _probs(q, k, scale, is_causal)
+    zr = keep_mask(q.shape[0], k.shape[0], unit, p, seed, offset) / (1.0 - float(np.float32(p)))
+    dv = (P * zr).T @ do
+    dp = (do @ v.T) * zr
+    ds = P * (dp - np.sum(P * dp, axis=1, keepdims=True))
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
+
+
+def sdpa_bwd_dropout(q, k, v, do, scale, is_causal, p, seed, offset=0):
+    """Dense layouts, unit u = b*H + h (as the dropout forward)."""
+    q = np.asarray(q)
+    B, H = q.shape[:2]
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(np.shape(k), dtype=np.float64)
+    dv = np.empty(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = attention_grads_dropout(
+                q[b, h], k[b, h], v[b, h], do[b, h], scale, is_causal, p, seed, offset, b * H + h)
+    return dq, dk, dv

@@ -131,3 +131,55 @@ def test_planted_mistakes_are_caught(mistake):
     # control: the unmutated formulas pass the same comparison
     ok = grad.attention_grads(q, k, v, do, 0.8, causal)
     assert all(np.allclose(g, w, rtol=1e-5, atol=1e-6) for g, w in zip(ok, want))
+
+
+# ---- gradients through dropout (the mask is a constant of the seed) -----------
+
+def _loss_dropout(q, k, v, do, scale, causal, p, seed):
+    from oracle import dropout as odrop
+    o, _ = odrop.attend_dropout(q, k, v, scale, causal, p, seed, 3, 0)
+    return float(np.sum(do * o))
+
+
+@pytest.mark.parametrize("nq,nk,d,causal", [(5, 7, 4, False), (6, 6, 3, True), (4, 20, 2, True)])
+def test_dropout_grads_match_finite_differences(nq, nk, d, causal):
+    q, k, v = _rand((nq, d), 41), _rand((nk, d), 42), _rand((nk, d), 43)
+    do = _rand((nq, d), 44)
+    p, seed, h = 0.3, 17, 1e-6
+    want = []
+    for x in (q, k, v):
+        g = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss_dropout(q, k, v, do, 0.7, causal, p, seed)
+            x[idx] = old - h
+            lm = _loss_dropout(q, k, v, do, 0.7, causal, p, seed)
+            x[idx] = old
+            g[idx] = (lp - lm) / (2 * h)
+        want.append(g)
+    got = grad.attention_grads_dropout(q, k, v, do, 0.7, causal, p, seed, 3, 0)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-6, atol=1e-7)
+    # the mask matters: some weight of this case is dropped
+    from oracle import dropout as odrop
+    assert not odrop.keep_mask(nq, nk, 0, p, seed, 3).all()
+
+
+def test_dropout_grads_at_p_zero_are_the_plain_grads():
+    q, k, v, do = (_rand((2, 3, 9, 4), s) for s in (51, 52, 53, 54))
+    a = grad.sdpa_bwd_dropout(q, k, v, do, 0.5, True, 0.0, 5)
+    b = grad.sdpa_bwd(q, k, v, do, 0.5, True)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-14)
+
+
+def test_dropout_rowsum_identity():
+    """sum_j P_ij dP_ij = <dO_i, O_i> also with dropout (the GPU path's D)."""
+    from oracle import dropout as odrop
+    q, k, v, do = _rand((7, 4), 61), _rand((9, 4), 62), _rand((9, 4), 63), _rand((7, 4), 64)
+    P = grad._probs(q, k, 0.5, False)
+    zr = odrop.keep_mask(7, 9, 2, 0.4, 8, 1) / (1.0 - float(np.float32(0.4)))
+    o, _ = odrop.attend_dropout(q, k, v, 0.5, False, 0.4, 8, 1, 2)
+    np.testing.assert_allclose(np.sum(P * (do @ v.T) * zr, axis=1), np.sum(do * o, axis=1),
+                               rtol=1e-12, atol=1e-12)
