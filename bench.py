@@ -201,7 +201,7 @@ def _cpu_baseline_dropout(w, budget_s, threads, p):
             "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline_bwd(w, budget_s, cfg):
+def cpu_baseline_bwd(w, budget_s, cfg, dropout=0.0):
     """The fp64 gradient oracle on whole (batch, head) units of the workload,
     until about ``budget_s`` seconds have passed (same FLOP convention as
     the GPU line).  None for sequences too long to hold a unit's N x N
@@ -222,7 +222,11 @@ def cpu_baseline_bwd(w, budget_s, cfg):
     units = [(b, h) for b in range(w.B) for h in range(w.H)]
     for (b, h) in units:
         dec = lambda x: inputs.storage_to_f64(x[b:b + 1, h:h + 1], w.dtype)
-        oracle.sdpa_bwd(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal)
+        if dropout > 0:
+            oracle.sdpa_bwd_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal,
+                                    dropout, 2023, 0)
+        else:
+            oracle.sdpa_bwd(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal)
         flops += 2.5 * 4.0 * w.Nq * w.Nk * w.d / (2 if w.is_causal else 1)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -444,7 +448,7 @@ def main(argv=None) -> int:
                 raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
-        if w.varlen or w.block_mask is not None or a.dropout > 0:
+        if w.varlen or w.block_mask is not None:
             print("bench.py: the backward pass takes dense, unmasked inputs only",
                   file=sys.stderr)
             return 2
@@ -458,8 +462,11 @@ def main(argv=None) -> int:
                  w.B, H, w.Nq, w.Nk, w.d, float(w.scale), int(w.is_causal), dt, odt,
                  sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME, handle]
 
+        if a.dropout > 0:   # the forward above ran with the same dropout contract
+            bargs = bargs[:17] + [float(a.dropout), 2023, 0] + bargs[17:]
+
         def step():  # noqa: F811 -- the timed step is the backward call
-            st = L.sdpa_bwd(*bargs)
+            st = (L.sdpa_bwd_dropout if a.dropout > 0 else L.sdpa_bwd)(*bargs)
             if st != 0:
                 raise sdpa.SdpaError(st)
 
@@ -520,7 +527,8 @@ def main(argv=None) -> int:
         rec["kernels"] = "rowdot + dq + dkdv (kernel_ms spans all three)"
     if a.cpu_budget > 0:
         rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget, a.dropout) if a.which == "fwd"
-                               else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload]))
+                               else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload],
+                                                     a.dropout))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -91,6 +91,20 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, sc
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(B), int(H),
                              int(Nq), int(Nk), int(d), float(scale), int(is_causal), int(dtype),
                              int(out_dtype), int(grad_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_bwd_dropout(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
+                     is_causal, dropout_p, seed, offset, dtype, out_dtype, grad_dtype, stream):
+    """Call the dropout backward C entry point (same conventions as sdpa_fwd)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_bwd_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
+        int(is_causal), float(dropout_p), int(seed), int(offset), int(dtype), int(out_dtype),
+        int(grad_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -228,11 +242,13 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
 
 def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
                                           is_causal=False, scale=None, grad_dtype=None,
-                                          stream=None):
+                                          stream=None, dropout_p=0.0, dropout_seed=None,
+                                          dropout_offset=0):
     """Gradients (dq, dk, dv) of sum(grad_out * out) for dense inputs
     [B,H,N,d], given the forward's out and lse.  ``grad_out`` is cast to the
     input dtype (the matrix cores consume it); ``grad_dtype`` None keeps the
-    input dtype, torch.float32 requests f32 gradients."""
+    input dtype, torch.float32 requests f32 gradients.  After a dropout
+    forward, pass its ``dropout_p``, ``dropout_seed`` and ``dropout_offset``."""
     import torch
     if not (query.dtype == key.dtype == value.dtype):
         raise SdpaError(SDPA_ERR_INVALID)
@@ -259,10 +275,18 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
     work = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    odc = SDPA_F32 if o.dtype != q.dtype else SDPA_SAME
+    gdc = SDPA_F32 if gdt != q.dtype else SDPA_SAME
     with torch.cuda.device(q.device):
-        sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale, bool(is_causal),
-                 dt, SDPA_F32 if o.dtype != q.dtype else SDPA_SAME,
-                 SDPA_F32 if gdt != q.dtype else SDPA_SAME, stream)
+        if dropout_p > 0.0:
+            if dropout_seed is None:
+                raise SdpaError(SDPA_ERR_INVALID)   # the forward's seed is needed
+            sdpa_bwd_dropout(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
+                             bool(is_causal), dropout_p, dropout_seed, dropout_offset, dt, odc,
+                             gdc, stream)
+        else:
+            sdpa_bwd(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
+                     bool(is_causal), dt, odc, gdc, stream)
     return dq, dk, dv
 
 
@@ -271,19 +295,23 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, is_causal, scale):
+        def forward(ctx, q, k, v, is_causal, scale, dropout_p, seed, offset):
             out, lse = scaled_dot_product_attention(q, k, v, is_causal=is_causal, scale=scale,
-                                                    return_lse=True)
+                                                    dropout_p=dropout_p, dropout_seed=seed,
+                                                    dropout_offset=offset, return_lse=True)
             ctx.save_for_backward(q, k, v, out, lse)
             ctx.is_causal, ctx.scale = is_causal, scale
+            ctx.drop = (dropout_p, seed, offset)
             return out
 
         @staticmethod
         def backward(ctx, grad_out):
             q, k, v, out, lse = ctx.saved_tensors
+            p, seed, offset = ctx.drop
             dq, dk, dv = scaled_dot_product_attention_backward(
-                q, k, v, out, lse, grad_out, is_causal=ctx.is_causal, scale=ctx.scale)
-            return dq, dk, dv, None, None
+                q, k, v, out, lse, grad_out, is_causal=ctx.is_causal, scale=ctx.scale,
+                dropout_p=p, dropout_seed=seed, dropout_offset=offset)
+            return dq, dk, dv, None, None, None, None, None
 
     return _Attention
 
@@ -291,10 +319,17 @@ def _autograd_function():
 _ATTN = None
 
 
-def attention(query, key, value, is_causal=False, scale=None):
+def attention(query, key, value, is_causal=False, scale=None, dropout_p=0.0, dropout_seed=None,
+              dropout_offset=0):
     """Differentiable dense attention [B,H,N,d]: the forward and backward
-    both run in the HIP kernels."""
+    both run in the HIP kernels.  With ``dropout_p`` > 0 the backward
+    regenerates the forward's mask from the same seed (drawn from torch's
+    CPU generator when None) and offset."""
     global _ATTN
     if _ATTN is None:
         _ATTN = _autograd_function()
-    return _ATTN.apply(query, key, value, bool(is_causal), scale)
+    if dropout_p > 0.0 and dropout_seed is None:
+        import torch
+        dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+    return _ATTN.apply(query, key, value, bool(is_causal), scale, float(dropout_p), dropout_seed,
+                       int(dropout_offset))

@@ -28,6 +28,8 @@
 // f16, so the last products run on the f16 matrix cores.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_mfma.h"
 
 namespace sdpa {
@@ -48,7 +50,18 @@ struct BwdParams {
   int total;              // grid size
   float c;                // scale * log2(e)
   float scale;
+  // dropout (the forward's Philox contract): key, last counter word, keep
+  // threshold on the 16-bit numbers, 1 / (1 - p)
+  uint32_t seed_lo, seed_hi, drop_offset, drop_t;
+  float drop_scale;
 };
+
+// 1/(1-p) if the 16-bit number u is below the keep threshold, else 0: the
+// sign of u - T (T <= 65536) selects the bits of the scale.
+__device__ __forceinline__ float keep_scale(uint32_t u, uint32_t t, float rp) {
+  const uint32_t m = (uint32_t)((int32_t)(u - t) >> 31);
+  return __uint_as_float(__float_as_uint(rp) & m);
+}
 
 // unpack 8 16-bit values (f16 or bf16) to fp32
 template <bool BF16>
@@ -160,7 +173,7 @@ __device__ __forceinline__ void store_rows(void* base, int64_t off0, int64_t rs,
 }
 
 // ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
-template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32>
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false>
 struct BwdDq {
   static constexpr int BM = NW * 32;
   static constexpr int KB = BN / 32;
@@ -308,13 +321,24 @@ struct BwdDq {
           u32x4 dsf[2];
 #pragma unroll
           for (int hs = 0; hs < 2; ++hs) {
+            // dropout: the forward's keep decisions of these 8 keys of row
+            // qi (same lane layout as the forward), dP scaled by z/(1-p)
+            uint32_t rr[4];
+            if (DROP)
+              philox4x32_10((uint32_t)((kb + kk * 32) >> 3) + 2 * hs + hl, (uint32_t)qi,
+                            (uint32_t)bh, p.drop_offset, p.seed_lo, p.seed_hi, rr);
             uint32_t w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 8 * hs + 2 * i;
               const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2));
               const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], p.c, -lse2));
-              w[i] = pack_f16(p0 * (dp[r] - dd), p1 * (dp[r + 1] - dd));
+              float d0 = dp[r] - dd, d1 = dp[r + 1] - dd;
+              if (DROP) {
+                d0 = __builtin_fmaf(keep_scale(rr[i] & 0xffffu, p.drop_t, p.drop_scale), dp[r], -dd);
+                d1 = __builtin_fmaf(keep_scale(rr[i] >> 16, p.drop_t, p.drop_scale), dp[r + 1], -dd);
+              }
+              w[i] = pack_f16(p0 * d0, p1 * d1);
             }
             dsf[hs] = u32x4{w[0], w[1], w[2], w[3]};
           }
@@ -338,7 +362,54 @@ struct BwdDq {
 };
 
 // ---- dK, dV: one wave per 32 key rows, query tiles of BQ rows streamed
-template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32>
+// Dropout keep bits in the transposed layout of the dK/dV kernel.  Lane
+// (l32, hl) owns key key0 + l32 and needs the decisions of the 32 queries
+// q0 .. q0+31 of a block.  Each lane first draws, as the forward does, the
+// two Philox calls of query q0 + l32 for keys key0 .. key0+31; then each of
+// the 16 (call, word, half) positions is turned into a 64-lane ballot whose
+// bit L is the decision of query q0 + L%32 for one key (lanes L < 32) or
+// for the key 4 above it (L >= 32).  The 32 ballot halves are spread over
+// lanes 0..31 and every lane fetches the one of its key.  Returns bit q =
+// keep (query q0 + q, key key0 + l32).
+// v with lane `lane` replaced by the wave-uniform value s.  s is typically
+// a ballot just written by a vector compare, and a vector instruction that
+// reads an SGPR written by a vector instruction needs two wait states on
+// gfx950; the compiler cannot see inside the asm, so the nop is written here.
+template <int lane>
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t s) {
+  asm("s_nop 1\n\tv_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "i"(lane));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t keep_bits_of_key(int q0, int key0, int l32, int hl,
+                                                     uint32_t unit, const BwdParams& p) {
+  uint32_t r[2][4];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+    philox4x32_10((uint32_t)(key0 >> 3) + 2 * hs + hl, (uint32_t)(q0 + l32), unit, p.drop_offset,
+                  p.seed_lo, p.seed_hi, r[hs]);
+  uint32_t v = 0;
+  auto put = [&](auto idx_c, uint32_t u) {
+    constexpr int idx = decltype(idx_c)::value;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(u < p.drop_t);
+    v = write_lane<2 * idx>(v, (uint32_t)bal);
+    v = write_lane<2 * idx + 1>(v, (uint32_t)(bal >> 32));
+  };
+  // ballot index hs * 8 + w * 2 + b for half b of word w of call hs
+#define SDPA_PUT(HS, W)                                                         \
+  put(std::integral_constant<int, HS * 8 + W * 2>{}, r[HS][W] & 0xffffu);       \
+  put(std::integral_constant<int, HS * 8 + W * 2 + 1>{}, r[HS][W] >> 16);
+  SDPA_PUT(0, 0) SDPA_PUT(0, 1) SDPA_PUT(0, 2) SDPA_PUT(0, 3)
+  SDPA_PUT(1, 0) SDPA_PUT(1, 1) SDPA_PUT(1, 2) SDPA_PUT(1, 3)
+#undef SDPA_PUT
+  // key offset l32 = 16 hs + 8 (w >> 1) + 4 h + 2 (w & 1) + b
+  const int w = 2 * ((l32 >> 3) & 1) + ((l32 >> 1) & 1);
+  const int idx = ((l32 >> 4) & 1) * 8 + w * 2 + (l32 & 1);
+  const int src = 2 * idx + ((l32 >> 2) & 1);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)v);
+}
+
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP = false>
 struct BwdDkdv {
   static constexpr int BK = NW * 32;
   static constexpr int KB = BQ / 32;
@@ -470,16 +541,20 @@ struct BwdDkdv {
           // The accumulators start at -lse*log2(e)/c and -D of the lane's 16
           // query rows (register r holds query 8(r/4) + 4*hl + r%4 of the
           // block), so the matrix cores return S - lse/scale and dP - D.
+          // With dropout dP starts at 0 and -D stays in registers, since
+          // dS = P (z dP / (1-p) - D) needs D on its own.
           f32x16 s, dp;
+          f32x4 ndv[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int idx = kk * 32 + 8 * g + 4 * hl;
             const f32x4 a = *reinterpret_cast<const f32x4*>(&b.nl[idx]);
             const f32x4 c = *reinterpret_cast<const f32x4*>(&b.nd[idx]);
+            if (DROP) ndv[g] = c;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               s[4 * g + e] = a[e];
-              dp[4 * g + e] = c[e];
+              dp[4 * g + e] = DROP ? 0.f : c[e];
             }
           }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -498,6 +573,8 @@ struct BwdDkdv {
               if (ki > query) s[r] = -INFINITY;
             }
           }
+          uint32_t zb = 0;
+          if (DROP) zb = keep_bits_of_key(qb + kk * 32, k0w, l32, hl, (uint32_t)bh, p) >> (4 * hl);
           u32x4 pf[2], dsf[2];
 #pragma unroll
           for (int hs = 0; hs < 2; ++hs) {
@@ -507,8 +584,17 @@ struct BwdDkdv {
               const int r = 8 * hs + 2 * e;
               const float p0 = __builtin_amdgcn_exp2f(s[r] * p.c);
               const float p1 = __builtin_amdgcn_exp2f(s[r + 1] * p.c);
-              wp[e] = pack_f16(p0, p1);
-              wd[e] = pack_f16(p0 * dp[r], p1 * dp[r + 1]);
+              if (DROP) {
+                // register r holds query 8 (r >> 2) + 4 hl + (r & 3) of the block
+                const float z0 = (zb >> (8 * (r >> 2) + (r & 3))) & 1u ? p.drop_scale : 0.f;
+                const float z1 = (zb >> (8 * (r >> 2) + (r & 3) + 1)) & 1u ? p.drop_scale : 0.f;
+                wp[e] = pack_f16(p0 * z0, p1 * z1);
+                wd[e] = pack_f16(p0 * __builtin_fmaf(z0, dp[r], ndv[r >> 2][r & 3]),
+                                 p1 * __builtin_fmaf(z1, dp[r + 1], ndv[(r + 1) >> 2][(r + 1) & 3]));
+              } else {
+                wp[e] = pack_f16(p0, p1);
+                wd[e] = pack_f16(p0 * dp[r], p1 * dp[r + 1]);
+              }
             }
             pf[hs] = u32x4{wp[0], wp[1], wp[2], wp[3]};
             dsf[hs] = u32x4{wd[0], wd[1], wd[2], wd[3]};
@@ -541,10 +627,14 @@ struct BwdDkdv {
 #endif
 template <int D>
 constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64 : 2;
+// with dropout the Philox state needs more registers
+template <int D>
+constexpr int kBwdDqDropWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 
-template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32>
-__global__ __launch_bounds__(NW * 64, kBwdDqWavesPerSimd<D>) void bwd_dq_kernel(BwdParams p) {
-  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32>;
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP>
+__global__ __launch_bounds__(NW * 64, DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D>)
+void bwd_dq_kernel(BwdParams p) {
+  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
@@ -552,10 +642,14 @@ __global__ __launch_bounds__(NW * 64, kBwdDqWavesPerSimd<D>) void bwd_dq_kernel(
 // waves per SIMD the dK/dV kernel's registers are fitted to
 template <int D>
 constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
+// with dropout: -D of 16 queries and the Philox state stay live
+template <int D>
+constexpr int kBwdKvDropWavesPerSimd = D == 32 ? 3 : D == 64 ? 2 : 1;
 
-template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32>
-__global__ __launch_bounds__(NW * 64, kBwdKvWavesPerSimd<D>) void bwd_dkdv_kernel(BwdParams p) {
-  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32>;
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP>
+__global__ __launch_bounds__(NW * 64, DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvWavesPerSimd<D>)
+void bwd_dkdv_kernel(BwdParams p) {
+  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

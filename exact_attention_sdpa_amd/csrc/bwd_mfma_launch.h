@@ -11,19 +11,19 @@ namespace sdpa {
 constexpr int kBwdDqWaves = 4, kBwdDqKeys = 32;
 constexpr int kBwdKvWaves = 4, kBwdKvRows = 32;
 
-template <bool BF16, int D, bool CAUSAL, bool GF32>
+template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP>
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
-  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32>;
-  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32>;
+  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP>;
+  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP>;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32>),
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP>),
                      dim3(p.total), dim3(kBwdDqWaves * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP>),
                      dim3(p.total), dim3(kBwdKvWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -47,7 +47,13 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   // scale 0 is carried as a tiny positive multiplier, as in the forward
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   p.scale = a.scale;
-  // D_i = <dO_i, O_i>
+  p.seed_lo = (uint32_t)(a.drop_seed & 0xffffffffu);
+  p.seed_hi = (uint32_t)(a.drop_seed >> 32);
+  p.drop_offset = a.drop_offset;
+  p.drop_t = a.drop_t;
+  p.drop_scale = a.drop_scale;
+  // D_i = <dO_i, O_i> (with dropout O is the dropped output, and D is still
+  // sum_j P_ij dP_ij with dP the gradient of the undropped weights)
   const int64_t rows = a.B * a.H * a.Nq;
   const dim3 grid((unsigned)((rows + 255) / 256));
   if (a.out_f32)
@@ -56,11 +62,19 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.causal)
-    return a.grad_f32 ? launch_bwd_tiles<BF16, D, true, true>(a, p)
-                      : launch_bwd_tiles<BF16, D, true, false>(a, p);
-  return a.grad_f32 ? launch_bwd_tiles<BF16, D, false, true>(a, p)
-                    : launch_bwd_tiles<BF16, D, false, false>(a, p);
+#define SDPA_BCASE(C, G, X)                                                   \
+  if (a.causal == C && a.grad_f32 == G && a.dropout == X)                     \
+    return launch_bwd_tiles<BF16, D, C, G, X>(a, p);
+  SDPA_BCASE(false, false, false)
+  SDPA_BCASE(false, true, false)
+  SDPA_BCASE(true, false, false)
+  SDPA_BCASE(true, true, false)
+  SDPA_BCASE(false, false, true)
+  SDPA_BCASE(false, true, true)
+  SDPA_BCASE(true, false, true)
+  SDPA_BCASE(true, true, true)
+#undef SDPA_BCASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sdpa

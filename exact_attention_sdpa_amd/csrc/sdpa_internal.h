@@ -51,6 +51,11 @@ struct BwdArgs {
   bool grad_f32;            // dq/dk/dv are f32 (else the input type)
   sdpa_dtype dtype;         // SDPA_F16 or SDPA_BF16
   hipStream_t stream;
+  bool dropout;             // the forward ran with dropout (same contract)
+  uint64_t drop_seed;
+  uint32_t drop_offset;
+  uint32_t drop_t;
+  float drop_scale;
 };
 
 // Host-only argument checks (no HIP calls).  Fills `a` on success.
@@ -64,6 +69,9 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
 // mask_heads 1 or H, f16/bf16 inputs, dense layout, and the mask
 // [mask_heads][ceil(Nq/128)][ceil(Nk/128)] bytes clear of out and lse.
 sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs* a);
+
+// Adds dropout to validated backward arguments (same rules as the forward).
+sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a);
 
 // Adds dropout to validated forward arguments: 0 <= p < 1 (p = 0 leaves the
 // plain kernel), f16/bf16 inputs; the keep threshold floor((1-p) 65536 + 1/2)

@@ -151,6 +151,18 @@ sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a
   return SDPA_OK;
 }
 
+sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a) {
+  if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;
+  if (p == 0.f) return SDPA_OK;
+  const double keep = 1.0 - (double)p;
+  a->dropout = true;
+  a->drop_seed = seed;
+  a->drop_offset = offset;
+  a->drop_t = (uint32_t)std::floor(keep * 65536.0 + 0.5);
+  a->drop_scale = (float)(1.0 / keep);
+  return SDPA_OK;
+}
+
 sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
@@ -231,6 +243,11 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
   a->grad_f32 = grad_f32;
   a->dtype = dtype;
   a->stream = static_cast<hipStream_t>(stream);
+  a->dropout = false;
+  a->drop_seed = 0;
+  a->drop_offset = 0;
+  a->drop_t = 65536;
+  a->drop_scale = 1.f;
   return SDPA_OK;
 }
 

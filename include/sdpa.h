@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 4
+#define SDPA_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -202,6 +202,22 @@ SDPA_API sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const
                               float* workspace, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                               int64_t d, float scale, int is_causal, sdpa_dtype dtype,
                               sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
+
+/* Backward pass of sdpa_fwd_dropout: the gradients of sum(dO * O) where
+ * O = sum_j P_ij z_ij / (1 - p) v_j and the mask z is the one the forward
+ * drew (it is regenerated from the same dropout_p, seed and offset, never
+ * stored).  With W = P z / (1 - p): dV = W^T dO, dP = (dO V^T) z / (1 - p),
+ * dS = P (dP - <dO, O>), dQ = scale dS K, dK = scale dS^T Q.  `out` and
+ * `lse` are the dropout forward's.  Arguments otherwise as sdpa_bwd;
+ * 0 <= dropout_p < 1 (else SDPA_ERR_INVALID), p = 0 is exactly sdpa_bwd.
+ */
+SDPA_API sdpa_status sdpa_bwd_dropout(const void* q, const void* k, const void* v,
+                                      const void* out, const void* dout, const float* lse,
+                                      void* dq, void* dk, void* dv, float* workspace, int64_t B,
+                                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                      int is_causal, float dropout_p, uint64_t seed,
+                                      uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                      sdpa_dtype grad_dtype, void* stream);
 
 /* Bytes of the workspace sdpa_bwd needs (B*H*Nq floats), or -1 if the sizes
  * overflow.  Pure host function. */

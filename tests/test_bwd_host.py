@@ -61,3 +61,12 @@ def test_no_device_is_reported(lib):
     except Exception:
         pass
     assert call(lib) == DEVICE
+
+
+@pytest.mark.parametrize("pd,status", [(1.0, INVALID), (-0.5, INVALID), (float("nan"), INVALID)])
+def test_invalid_dropout_rate_rejected_on_host(lib, pd, status):
+    a = BASE
+    st = lib.sdpa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], a["dq"], a["dk"],
+                              a["dv"], a["w"], 2, 4, 128, 128, 64, 0.125, 0, pd, 1, 0, F16, SAME,
+                              SAME, None)
+    assert st == status
