@@ -56,8 +56,9 @@ def kernel_sources_digest(prefix: str = "fwd_") -> str:
     current kernels."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_sdpa_amd", "csrc")
+    shared = ("philox.h",)   # included by both kernel families
     for name in sorted(os.listdir(csrc)):
-        if name.startswith(prefix) and name.endswith((".h", ".hip", ".cpp")):
+        if (name.startswith(prefix) or name in shared) and name.endswith((".h", ".hip", ".cpp")):
             with open(os.path.join(csrc, name)) as f:
                 h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
