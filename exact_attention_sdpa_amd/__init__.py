@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -52,6 +52,24 @@ def sdpa_fwd(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal, cu_seqlens, d
     st = _lib.lib().sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H),
                              int(Nq), int(Nk), int(d), float(scale), int(is_causal),
                              _ptr(cu_seqlens), int(dtype), int(out_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_fwd_strided(q, k, v, out, lse, B, H, Nq, Nk, d, q_strides, kv_strides, out_strides,
+                     scale, is_causal, dtype, out_dtype, stream):
+    """Call the strided C entry point; strides are 3-sequences of element
+    strides (batch, head, row)."""
+    import ctypes
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    arr = lambda s: (ctypes.c_int64 * 3)(*[int(x) for x in s])
+    qs, ks, os_ = arr(q_strides), arr(kv_strides), arr(out_strides)
+    st = _lib.lib().sdpa_fwd_strided(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+        int(d), ctypes.cast(qs, ctypes.c_void_p), ctypes.cast(ks, ctypes.c_void_p),
+        ctypes.cast(os_, ctypes.c_void_p), float(scale), int(is_causal), int(dtype),
+        int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -150,7 +168,7 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
                                  is_causal=False, scale=None, cu_seqlens=None,
                                  max_seqlen=None, out_dtype=None, return_lse=False,
                                  stream=None, block_mask=None, dropout_seed=None,
-                                 dropout_offset=0):
+                                 dropout_offset=0, out=None):
     """Attention forward on device tensors.
 
     Dense: query [B,H,Nq,d] (or [B,Nq,d], read as H=1), key/value
@@ -165,7 +183,14 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     contract of sdpa_fwd_dropout, keyed by ``dropout_seed`` (drawn from
     torch's CPU generator when None) and ``dropout_offset``.  An elementwise
     mask, or dropout together with a block mask, is not supported and
-    raises, as the tutorial's backends do for inputs they cannot serve."""
+    raises, as the tutorial's backends do for inputs they cannot serve.
+
+    Dense f16/bf16 inputs that are strided views (for instance the q, k, v
+    of a packed QKV projection, ``c_attn(x).chunk(3, -1)`` viewed as
+    [B,H,N,d]) are read in place through sdpa_fwd_strided when their strides
+    allow it, and ``out`` may be a strided [B,H,Nq,d] view to write into
+    (for instance a [B,N,H*d] buffer viewed as [B,H,N,d]); other inputs are
+    copied to contiguous buffers first."""
     import torch
     if attn_mask is not None:
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
@@ -177,6 +202,13 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
         raise SdpaError(SDPA_ERR_INVALID)
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise SdpaError(SDPA_ERR_INVALID)
+    plain = cu_seqlens is None and block_mask is None and dropout_p == 0.0
+    if (plain and query.dim() == 4 and key.dim() == 4 and value.dim() == 4
+            and query.dtype in (torch.float16, torch.bfloat16)
+            and (out is not None or not (query.is_contiguous() and key.is_contiguous()
+                                         and value.is_contiguous()))):
+        return _strided_forward(query, key, value, is_causal, scale, out_dtype, return_lse,
+                                stream, out)
     q, k, v = _contig(query), _contig(key), _contig(value)
     dt = _code(q.dtype)
     d = q.shape[-1]
@@ -237,6 +269,42 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
         out = out[:, 0]
         if lse is not None:
             lse = lse[:, 0]
+    return (out, lse) if return_lse else out
+
+
+def _strided_ok(t, mult):
+    s = t.stride()
+    return s[3] == 1 and all(x >= 0 and x % mult == 0 for x in s[:3]) and t.data_ptr() % 16 == 0
+
+
+def _strided_forward(query, key, value, is_causal, scale, out_dtype, return_lse, stream, out):
+    import torch
+    q = query if _strided_ok(query, 8) else query.contiguous()
+    if key.stride() == value.stride() and _strided_ok(key, 8) and _strided_ok(value, 8):
+        k, v = key, value
+    else:
+        k, v = key.contiguous(), value.contiguous()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in (q.dtype, torch.float32):
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    elif (tuple(out.shape) != (B, H, Nq, d) or out.dtype != odt or out.device != q.device
+          or not _strided_ok(out, 4)):
+        raise SdpaError(SDPA_ERR_INVALID)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        sdpa_fwd_strided(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3], k.stride()[:3],
+                         out.stride()[:3], scale, bool(is_causal), _code(q.dtype),
+                         _code(odt) if odt != q.dtype else SDPA_SAME, stream)
     return (out, lse) if return_lse else out
 
 

@@ -13,7 +13,7 @@ SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVIC
 SDPA_BLOCK_SPARSE_BLOCK = 128
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
+EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
            "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
@@ -32,6 +32,9 @@ def lib() -> ctypes.CDLL:
     L.sdpa_fwd.restype = ctypes.c_int
     L.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_fwd_strided.restype = ctypes.c_int
+    L.sdpa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.sdpa_fwd_block_sparse.restype = ctypes.c_int
     L.sdpa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                         ctypes.c_float, ctypes.c_int, vp, i64, ctypes.c_int,

@@ -87,6 +87,10 @@ struct MfmaParams {
   const int32_t* cu;   // packed batches: B+1 offsets
   int H;
   int Nq, Nk;          // dense sizes; packed: max sequence length
+  // dense layouts: (batch, head, row) strides in elements; k and v share
+  // theirs (the element stride along d is 1)
+  int64_t q_bs, q_hs, kv_bs, kv_hs, o_bs, o_hs;
+  int q_rs, kv_rs, o_rs;
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
   float c;             // scale * log2(e), at least 1e-30
@@ -582,18 +586,21 @@ struct MfmaFwd {
     const int b = bh / p.H, h = bh % p.H;
 
     int nq, nk;
-    int64_t qoff, kvoff, rs;
+    int64_t qoff, kvoff, ooff, rs, qrs, ors;
     if (VARLEN) {
       const int s0 = p.cu[b], s1 = p.cu[b + 1];
       nq = nk = s1 - s0;
-      rs = (int64_t)p.H * D;
-      qoff = kvoff = (int64_t)s0 * rs + (int64_t)h * D;
+      rs = qrs = ors = (int64_t)p.H * D;
+      qoff = kvoff = ooff = (int64_t)s0 * rs + (int64_t)h * D;
     } else {
       nq = p.Nq;
       nk = p.Nk;
-      rs = D;
-      qoff = (int64_t)bh * p.Nq * D;
-      kvoff = (int64_t)bh * p.Nk * D;
+      rs = p.kv_rs;
+      qrs = p.q_rs;
+      ors = p.o_rs;
+      qoff = (int64_t)b * p.q_bs + (int64_t)h * p.q_hs;
+      kvoff = (int64_t)b * p.kv_bs + (int64_t)h * p.kv_hs;
+      ooff = (int64_t)b * p.o_bs + (int64_t)h * p.o_hs;
     }
     const int q0 = qt * BM;
     if (q0 >= nq) return;  // whole workgroup: tile past the sequence end
@@ -603,7 +610,8 @@ struct MfmaFwd {
     x.hd.kv_bytes = (int)(((int64_t)(nk - 1) * rs + D) * 2);
     x.hd.k = reinterpret_cast<const char*>(p.k + kvoff);
     x.hd.v = reinterpret_cast<const char*>(p.v + kvoff);
-    const int q_bytes = (int)(((int64_t)(nq - 1) * rs + D) * 2);
+    const int q_bytes = (int)(((int64_t)(nq - 1) * qrs + D) * 2);
+    const int q_rs_bytes = (int)(qrs * 2);
     const __amdgpu_buffer_rsrc_t qr =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + qoff), (short)0, q_bytes, kBufferWord3);
 
@@ -633,7 +641,7 @@ struct MfmaFwd {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
         qf[qb][ds] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qi * x.hd.rs_bytes + (ds * 16 + x.hl * 8) * 2, 0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, qi * q_rs_bytes + (ds * 16 + x.hl * 8) * 2, 0, 0));
     }
 
     State S;
@@ -695,7 +703,7 @@ struct MfmaFwd {
             const int dcol = db * 32 + 8 * g + 4 * x.hl;
             const float x0 = S.o[qb][db][4 * g + 0] * inv, x1 = S.o[qb][db][4 * g + 1] * inv;
             const float x2 = S.o[qb][db][4 * g + 2] * inv, x3 = S.o[qb][db][4 * g + 3] * inv;
-            const int64_t off = qoff + (int64_t)qi * rs + dcol;
+            const int64_t off = ooff + (int64_t)qi * ors + dcol;
             if (OUTF32) {
               *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + off) =
                   f32x4{x0, x1, x2, x3};

@@ -76,6 +76,15 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.H = (int)a.H;
   p.Nq = (int)a.Nq;
   p.Nk = (int)a.Nk;
+  p.q_bs = a.q_str[0];
+  p.q_hs = a.q_str[1];
+  p.q_rs = (int)a.q_str[2];
+  p.kv_bs = a.kv_str[0];
+  p.kv_hs = a.kv_str[1];
+  p.kv_rs = (int)a.kv_str[2];
+  p.o_bs = a.o_str[0];
+  p.o_hs = a.o_str[1];
+  p.o_rs = (int)a.o_str[2];
   p.n_qtiles = (int)((a.Nq + K::BM - 1) / K::BM);
   p.total = (int)(a.B * a.H * p.n_qtiles);
   // scale 0 is carried as a tiny positive multiplier: every visible score

@@ -18,6 +18,9 @@ struct FwdArgs {
   float* lse;               // may be null
   const int32_t* cu;        // null for dense
   int64_t B, H, Nq, Nk, d;  // packed: Nq == Nk == max sequence length
+  // dense layouts: (batch, head, row) strides in elements of q, of k and v
+  // (shared), of out; contiguous [B,H,N,d] unless set by the strided entry
+  int64_t q_str[3], kv_str[3], o_str[3];
   float scale;
   bool causal;
   bool out_f32;             // out element type is f32 (else the input type)
@@ -62,9 +65,17 @@ struct BwdArgs {
 sdpa_status validate(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                      int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
-                     sdpa_dtype out_dtype, void* stream, FwdArgs* a);
+                     sdpa_dtype out_dtype, void* stream, FwdArgs* a,
+                     bool check_overlap = true);
 
 // Host-only checks of a backward call.  Fills `a` on success.
+// Replaces the contiguous strides of validated dense forward arguments with
+// caller strides (batch, head, row; elements): non-negative multiples of 8
+// (inputs) or 4 (out), rows of one head within 32-bit buffer offsets, out
+// non-overlapping in itself and clear of q, k, v and lse.
+sdpa_status validate_strides(const int64_t* q_strides, const int64_t* kv_strides,
+                             const int64_t* out_strides, FwdArgs* a);
+
 // Adds a block-sparse mask to validated forward arguments: mask non-null,
 // mask_heads 1 or H, f16/bf16 inputs, dense layout, and the mask
 // [mask_heads][ceil(Nq/128)][ceil(Nk/128)] bytes clear of out and lse.

@@ -26,6 +26,33 @@ bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 int elem_bytes(sdpa_dtype t) { return t == SDPA_F32 ? 4 : 2; }
 
+// bytes from the base of a strided [B,H,N,d] tensor to one past its last
+// element (strides in elements, all non-negative); -1 if that overflows
+int64_t span_bytes(int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* s, int64_t eb) {
+  const __int128 e = ((__int128)(B - 1) * s[0] + (__int128)(H - 1) * s[1] +
+                      (__int128)(N - 1) * s[2] + d) * eb;
+  return e > (__int128)(INT64_MAX / 2) ? -1 : (int64_t)e;
+}
+
+// no two (b, h, n, c) of a strided [B,H,N,d] tensor share an element:
+// along ascending strides, each stride clears the extent of the dims below
+bool no_self_overlap(int64_t B, int64_t H, int64_t N, int64_t d, const int64_t* s) {
+  int64_t st[3] = {s[0], s[1], s[2]}, sz[3] = {B, H, N};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i] || (st[j] == st[i] && sz[j] < sz[i])) {
+        std::swap(st[i], st[j]);
+        std::swap(sz[i], sz[j]);
+      }
+  int64_t extent = d;   // elements covered by the dims below, plus one
+  for (int i = 0; i < 3; ++i) {
+    if (sz[i] == 1) continue;
+    if (st[i] < extent) return false;
+    extent = (sz[i] - 1) * st[i] + extent;
+  }
+  return true;
+}
+
 }  // namespace
 
 int path_for(sdpa_dtype dtype, int64_t d) {
@@ -37,7 +64,7 @@ int path_for(sdpa_dtype dtype, int64_t d) {
 sdpa_status validate(const void* q, const void* k, const void* v, void* out, float* lse,
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                      int is_causal, const int32_t* cu_seqlens, sdpa_dtype dtype,
-                     sdpa_dtype out_dtype, void* stream, FwdArgs* a) {
+                     sdpa_dtype out_dtype, void* stream, FwdArgs* a, bool check_overlap) {
   if (!q || !k || !v || !out) return SDPA_ERR_INVALID;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return SDPA_ERR_INVALID;
   if (is_causal != 0 && is_causal != 1) return SDPA_ERR_INVALID;
@@ -86,7 +113,7 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   if (lse && !aligned(lse, 4)) return SDPA_ERR_INVALID;
   if (cu_seqlens && !aligned(cu_seqlens, 4)) return SDPA_ERR_INVALID;
 
-  if (!varlen) {
+  if (!varlen && check_overlap) {
     const int64_t ib = elem_bytes(dtype), ob = out_f32 ? 4 : elem_bytes(dtype);
     const int64_t obytes = eq * ob;
     if (overlap(out, obytes, q, eq * ib) || overlap(out, obytes, k, ek * ib) ||
@@ -111,6 +138,15 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->out_f32 = out_f32;
   a->dtype = dtype;
   a->stream = static_cast<hipStream_t>(stream);
+  a->q_str[0] = H * Nq * d;
+  a->q_str[1] = Nq * d;
+  a->q_str[2] = d;
+  a->kv_str[0] = H * Nk * d;
+  a->kv_str[1] = Nk * d;
+  a->kv_str[2] = d;
+  a->o_str[0] = H * Nq * d;
+  a->o_str[1] = Nq * d;
+  a->o_str[2] = d;
   a->bmask = nullptr;
   a->mask_heads = 0;
   a->dropout = false;
@@ -118,6 +154,40 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->drop_offset = 0;
   a->drop_t = 65536;
   a->drop_scale = 1.f;
+  return SDPA_OK;
+}
+
+sdpa_status validate_strides(const int64_t* q_strides, const int64_t* kv_strides,
+                             const int64_t* out_strides, FwdArgs* a) {
+  if (!q_strides || !kv_strides || !out_strides) return SDPA_ERR_INVALID;
+  if (a->cu != nullptr) return SDPA_ERR_INVALID;
+  if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 40;
+  for (int i = 0; i < 3; ++i) {
+    // 16-byte input loads; output stores of 4 elements
+    if (q_strides[i] < 0 || kv_strides[i] < 0 || out_strides[i] < 0) return SDPA_ERR_INVALID;
+    if (q_strides[i] > lim || kv_strides[i] > lim || out_strides[i] > lim) return SDPA_ERR_INVALID;
+    if (q_strides[i] % 8 || kv_strides[i] % 8 || out_strides[i] % 4) return SDPA_ERR_INVALID;
+  }
+  // one head's rows (plus a tile of slack) within 32-bit buffer offsets
+  if ((a->Nq + 256) * q_strides[2] * 2 > (int64_t)INT32_MAX ||
+      (a->Nk + 256) * kv_strides[2] * 2 > (int64_t)INT32_MAX)
+    return SDPA_ERR_UNSUPPORTED;
+  if (!no_self_overlap(a->B, a->H, a->Nq, a->d, out_strides)) return SDPA_ERR_INVALID;
+  const int64_t ib = elem_bytes(a->dtype), ob = a->out_f32 ? 4 : ib;
+  const int64_t os = span_bytes(a->B, a->H, a->Nq, a->d, out_strides, ob);
+  const int64_t qs = span_bytes(a->B, a->H, a->Nq, a->d, q_strides, ib);
+  const int64_t ks = span_bytes(a->B, a->H, a->Nk, a->d, kv_strides, ib);
+  if (os < 0 || qs < 0 || ks < 0) return SDPA_ERR_INVALID;
+  if (overlap(a->out, os, a->q, qs) || overlap(a->out, os, a->k, ks) ||
+      overlap(a->out, os, a->v, ks))
+    return SDPA_ERR_INVALID;
+  if (a->lse && overlap(a->out, os, a->lse, a->B * a->H * a->Nq * 4)) return SDPA_ERR_INVALID;
+  for (int i = 0; i < 3; ++i) {
+    a->q_str[i] = q_strides[i];
+    a->kv_str[i] = kv_strides[i];
+    a->o_str[i] = out_strides[i];
+  }
   return SDPA_OK;
 }
 

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 5
+#define SDPA_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -116,6 +116,29 @@ SDPA_API sdpa_status sdpa_fwd(const void* q, const void* k, const void* v, void*
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                               float scale, int is_causal, const int32_t* cu_seqlens,
                               sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
+/* Forward on strided dense layouts, e.g. the q, k, v views that a packed
+ * QKV projection yields (SDPA tutorial, "Causal self-attention": c_attn(x)
+ * [B, N, 3E] chunked into three and viewed as [B, H, N, d]) with the output
+ * written straight into a [B, N, H*d] buffer.  Element (b, h, n, c) of a
+ * tensor with strides s lives at base + b*s[0] + h*s[1] + n*s[2] + c
+ * (elements; the stride along d is 1).
+ *
+ * q_strides, kv_strides, out_strides  host arrays of 3 int64 (batch, head,
+ *             row); k and v share kv_strides.  Input strides: non-negative
+ *             multiples of 8, bases 16-byte aligned; out strides: multiples
+ *             of 4, and no two output elements may share an address.
+ * lse         [B, H, Nq] contiguous (or null).
+ * Other arguments as sdpa_fwd (no packed batches); f16/bf16 only.
+ * SDPA_ERR_INVALID for bad strides or an output that overlaps itself or an
+ * input; SDPA_ERR_UNSUPPORTED if a head's rows exceed 32-bit offsets.
+ */
+SDPA_API sdpa_status sdpa_fwd_strided(const void* q, const void* k, const void* v, void* out,
+                                      float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                      int64_t d, const int64_t* q_strides,
+                                      const int64_t* kv_strides, const int64_t* out_strides,
+                                      float scale, int is_causal, sdpa_dtype dtype,
+                                      sdpa_dtype out_dtype, void* stream);
 
 /* Block size of block-sparse masks: 128 query rows x 128 keys. */
 #define SDPA_BLOCK_SPARSE_BLOCK 128

@@ -111,3 +111,32 @@ def _gpu_present():
         return torch.cuda.device_count() > 0
     except Exception:
         return False
+
+
+def _strided_call(lib, qs=(4 * 128 * 64, 128 * 64, 64), ks=None, os_=None, q=0x1000000,
+                  k=0x2000000, v=0x3000000, o=0x4000000, lse=0x6000000, B=2, H=4, N=128, d=64,
+                  dt=0):
+    import ctypes
+    arr = lambda s: None if s is None else ctypes.cast((ctypes.c_int64 * 3)(*s), ctypes.c_void_p)
+    ks = qs if ks is None else ks
+    os_ = qs if os_ is None else os_
+    return lib.sdpa_fwd_strided(q, k, v, o, lse, B, H, N, N, d, arr(qs), arr(ks), arr(os_),
+                                0.125, 0, dt, 255, None)
+
+
+def test_strided_calls_rejected_on_host(lib):
+    INVALID, UNSUPPORTED, DEVICE = 1, 2, 4
+    # the packed-QKV layout of a [2, 128, 3*256] projection, out [2, 128, 256]
+    qkv = (128 * 768, 64, 768)
+    out = (128 * 256, 64, 256)
+    assert _strided_call(lib, qkv, qkv, out) in (0, DEVICE)
+    assert _strided_call(lib, (1, 64, 768)) == INVALID           # not a multiple of 8
+    assert _strided_call(lib, qkv, qkv, (128 * 256, 2, 256)) == INVALID   # out rows overlap
+    assert _strided_call(lib, qkv, qkv, (0, 64, 256)) == INVALID  # batches share the output
+    assert _strided_call(lib, qkv, qkv, out, o=0x1000000 + 4096) == INVALID  # out inside q
+    assert _strided_call(lib, (-8, 64, 768)) == INVALID
+    assert lib.sdpa_fwd_strided(0x1000000, 0x2000000, 0x3000000, 0x4000000, None, 1, 1, 8, 8,
+                                64, None, None, None, 0.1, 0, 0, 255, None) == INVALID
+    assert _strided_call(lib, qkv, qkv, out, dt=2) == UNSUPPORTED  # f32 inputs
+    # a head's rows past 32-bit offsets
+    assert _strided_call(lib, (0, 0, 1 << 24), (0, 0, 1 << 24), out, N=200) == UNSUPPORTED
