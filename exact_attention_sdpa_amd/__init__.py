@@ -19,9 +19,9 @@ import warnings
 from . import _lib
 from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa: F401
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
-                   SDPA_OK, SDPA_SAME)
+                   SDPA_MASK_ADD, SDPA_MASK_ADD_F32, SDPA_MASK_BOOL, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -69,6 +69,32 @@ def sdpa_fwd_strided(q, k, v, out, lse, B, H, Nq, Nk, d, q_strides, kv_strides, 
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
         int(d), ctypes.cast(qs, ctypes.c_void_p), ctypes.cast(ks, ctypes.c_void_p),
         ctypes.cast(os_, ctypes.c_void_p), float(scale), int(is_causal), int(dtype),
+        int(out_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_fwd_masked(q, k, v, out, lse, B, H, Nq, Nk, d, q_strides, kv_strides, out_strides,
+                    scale, is_causal, mask, mask_kind, mask_strides, dtype, out_dtype, stream):
+    """Call the masked C entry point.  q/kv/out strides: all None
+    (contiguous) or 3-sequences of element strides; mask_strides a
+    3-sequence (batch, head, row)."""
+    import ctypes
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    keep = []
+
+    def arr(s):
+        if s is None:
+            return None
+        a = (ctypes.c_int64 * 3)(*[int(x) for x in s])
+        keep.append(a)
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    st = _lib.lib().sdpa_fwd_masked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+        int(d), arr(q_strides), arr(kv_strides), arr(out_strides), float(scale),
+        int(is_causal), _ptr(mask), int(mask_kind), arr(mask_strides), int(dtype),
         int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
@@ -181,9 +207,14 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     (i // 128, j // 128) is nonzero; rows that see no key give zeros and
     lse = -inf.  ``dropout_p`` > 0 drops attention weights with the Philox
     contract of sdpa_fwd_dropout, keyed by ``dropout_seed`` (drawn from
-    torch's CPU generator when None) and ``dropout_offset``.  An elementwise
-    mask, or dropout together with a block mask, is not supported and
-    raises, as the tutorial's backends do for inputs they cannot serve.
+    torch's CPU generator when None) and ``dropout_offset``.  ``attn_mask``
+    (dense layouts only) is a device tensor broadcastable to [B,H,Nq,Nk]:
+    torch.bool (True = attend), or additive in the input dtype or float32;
+    it runs through sdpa_fwd_masked, and rows with no finite score give
+    zeros and lse = -inf.  A mask together with packed batches, a block
+    mask or dropout, or dropout together with a block mask, is not
+    supported and raises, as the tutorial's backends do for inputs they
+    cannot serve.
 
     Dense f16/bf16 inputs that are strided views (for instance the q, k, v
     of a packed QKV projection, ``c_attn(x).chunk(3, -1)`` viewed as
@@ -192,8 +223,6 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     (for instance a [B,N,H*d] buffer viewed as [B,H,N,d]); other inputs are
     copied to contiguous buffers first."""
     import torch
-    if attn_mask is not None:
-        raise SdpaError(SDPA_ERR_UNSUPPORTED)
     if not 0.0 <= float(dropout_p) < 1.0:
         raise SdpaError(SDPA_ERR_INVALID)
     if dropout_p > 0.0 and block_mask is not None:
@@ -202,6 +231,11 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
         raise SdpaError(SDPA_ERR_INVALID)
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise SdpaError(SDPA_ERR_INVALID)
+    if attn_mask is not None:
+        if cu_seqlens is not None or block_mask is not None or dropout_p > 0.0:
+            raise SdpaError(SDPA_ERR_UNSUPPORTED)
+        return _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype,
+                               return_lse, stream, out)
     plain = cu_seqlens is None and block_mask is None and dropout_p == 0.0
     if (plain and query.dim() == 4 and key.dim() == 4 and value.dim() == 4
             and query.dtype in (torch.float16, torch.bfloat16)
@@ -305,6 +339,90 @@ def _strided_forward(query, key, value, is_causal, scale, out_dtype, return_lse,
         sdpa_fwd_strided(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3], k.stride()[:3],
                          out.stride()[:3], scale, bool(is_causal), _code(q.dtype),
                          _code(odt) if odt != q.dtype else SDPA_SAME, stream)
+    return (out, lse) if return_lse else out
+
+
+def _mask_operand(attn_mask, q, B, H, Nq, Nk, no_heads=False):
+    """(tensor, kind, strides) for sdpa_fwd_masked: the mask viewed as
+    [B,H,Nq,Nk] with broadcast dimensions at stride 0.  A mask whose layout
+    the kernel cannot read in place (key stride not 1, other strides not
+    multiples of 4, misaligned base, or Nk not a multiple of 4) is copied
+    into rows padded to a multiple of 4 elements."""
+    import torch
+    if attn_mask.dtype == torch.bool:
+        kind, m = SDPA_MASK_BOOL, attn_mask.view(torch.uint8)
+    elif attn_mask.dtype == q.dtype:
+        kind, m = SDPA_MASK_ADD, attn_mask
+    elif attn_mask.dtype == torch.float32:
+        kind, m = SDPA_MASK_ADD_F32, attn_mask
+    else:
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    if not m.is_cuda or m.device != q.device or not 1 <= m.dim() <= (3 if no_heads else 4):
+        raise SdpaError(SDPA_ERR_INVALID)
+    if no_heads and m.dim() == 3:   # [B, Nq, Nk] for 3-D inputs: insert the head dim
+        m = m[:, None]
+    m = m.reshape((1,) * (4 - m.dim()) + tuple(m.shape)) if m.dim() < 4 else m
+    try:
+        m4 = m.expand(B, H, Nq, Nk)
+    except RuntimeError:
+        raise SdpaError(SDPA_ERR_INVALID) from None
+    eb = m.element_size()
+
+    def eff(t):   # strides with size-1 dimensions read at stride 0
+        return tuple(x if n > 1 else 0 for x, n in zip(t.stride()[:3], t.shape[:3]))
+
+    st = eff(m4)
+    if not (Nk % 4 == 0 and (m4.stride(3) == 1 or Nk == 1) and all(x % 4 == 0 for x in st)
+            and m4.data_ptr() % (4 * eb) == 0):
+        nk4 = -(-Nk // 4) * 4
+        pad = torch.zeros(tuple(m.shape[:3]) + (nk4,), dtype=m.dtype, device=m.device)
+        pad[..., :Nk] = m.expand(tuple(m.shape[:3]) + (Nk,))
+        m4 = pad.expand(B, H, Nq, nk4)
+        st = eff(m4)
+    return m4, kind, st
+
+
+def _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype, return_lse,
+                    stream, out):
+    import torch
+    squeeze = query.dim() == 3
+    q, k, v = (query[:, None], key[:, None], value[:, None]) if squeeze else (query, key, value)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[:2] != (B, H) or v.shape != k.shape or k.shape[3] != d:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if odt not in (q.dtype, torch.float32):
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    if not _strided_ok(q, 8):
+        q = q.contiguous()
+    if not (k.stride() == v.stride() and _strided_ok(k, 8) and _strided_ok(v, 8)):
+        k, v = k.contiguous(), v.contiguous()
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    else:
+        out = out[:, None] if squeeze else out
+        if (tuple(out.shape) != (B, H, Nq, d) or out.dtype != odt or out.device != q.device
+                or not _strided_ok(out, 4)):
+            raise SdpaError(SDPA_ERR_INVALID)
+    m4, kind, mst = _mask_operand(attn_mask, q, B, H, Nq, Nk, no_heads=squeeze)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        sdpa_fwd_masked(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3], k.stride()[:3],
+                        out.stride()[:3], scale, bool(is_causal), m4, kind, mst, _code(q.dtype),
+                        _code(odt) if odt != q.dtype else SDPA_SAME, stream)
+    if squeeze:
+        out = out[:, 0]
+        if lse is not None:
+            lse = lse[:, 0]
     return (out, lse) if return_lse else out
 
 

@@ -11,9 +11,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa.so"
 SDPA_F16, SDPA_BF16, SDPA_F32, SDPA_SAME = 0, 1, 2, 255
 SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVICE = range(5)
 SDPA_BLOCK_SPARSE_BLOCK = 128
+SDPA_MASK_BOOL, SDPA_MASK_ADD, SDPA_MASK_ADD_F32 = 0, 1, 2
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
+EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
            "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
@@ -35,6 +36,10 @@ def lib() -> ctypes.CDLL:
     L.sdpa_fwd_strided.restype = ctypes.c_int
     L.sdpa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_fwd_masked.restype = ctypes.c_int
+    L.sdpa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                  ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
+                                  ctypes.c_int, ctypes.c_int, vp]
     L.sdpa_fwd_block_sparse.restype = ctypes.c_int
     L.sdpa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                         ctypes.c_float, ctypes.c_int, vp, i64, ctypes.c_int,

@@ -104,13 +104,27 @@ struct MfmaParams {
   // drop_t; kept weights are scaled by drop_scale = 1 / (1 - p)
   uint32_t seed_lo, seed_hi, drop_offset, drop_t;
   float drop_scale;
+  // elementwise-mask launches: mask element (b, h, i, j) at
+  // amask + (b*am_bs + h*am_hs + i*am_rs + j) elements (strides may be 0)
+  const void* amask;
+  int64_t am_bs, am_hs;
+  int am_rs;
 };
 
 // Block size of block-sparse masks (query rows x keys).
 constexpr int kSparseBlock = 128;
 
-// Kernel variants: plain, block-sparse, dropout on the attention weights.
-enum FwdVariant : int { kPlain = 0, kBlockSparse = 1, kDropout = 2 };
+// Kernel variants: plain, block-sparse, dropout on the attention weights,
+// and an elementwise attention mask: boolean (one byte per pair, nonzero =
+// attend), or additive in the input type or in f32.
+enum FwdVariant : int {
+  kPlain = 0,
+  kBlockSparse = 1,
+  kDropout = 2,
+  kMaskBool = 3,
+  kMaskAdd = 4,
+  kMaskAddF32 = 5
+};
 
 // Build option: raise the wave priority while it issues matrix-core work
 // (measured a few percent faster on MI355X).
@@ -170,6 +184,9 @@ template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bo
 struct MfmaFwd {
   static constexpr bool BSP = VAR == kBlockSparse;
   static constexpr bool DROP = VAR == kDropout;
+  static constexpr bool MASK = VAR >= kMaskBool;
+  // mask element bytes = 32-bit words a lane loads per group of 4 keys
+  static constexpr int MW = VAR == kMaskBool ? 1 : VAR == kMaskAdd ? 2 : 4;
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
   static constexpr int KB = BN / 32;       // 32-key blocks per step
   static constexpr int DS = D / 16;        // k-steps of S = Q K^T
@@ -188,6 +205,7 @@ struct MfmaFwd {
   // tile never straddles two mask columns
   static_assert(!BSP || (NW * NB * 32 == kSparseBlock && kSparseBlock % BN == 0 && !VARLEN),
                 "block-sparse tile shape");
+  static_assert(!MASK || !VARLEN, "elementwise masks take dense layouts");
 
   struct __attribute__((aligned(16))) Smem {
     uint16_t k[2][BN * KROW];
@@ -196,6 +214,9 @@ struct MfmaFwd {
 
   struct KRegs { u32x4 k[KPT]; };
   struct VRegs { u32x4 v0[VPT], v1[VPT]; };
+  // a lane's mask elements of one tile: per 32-key block, per query block,
+  // the 4 groups of 4 keys it owns (keys 8g + 4hl + 0..3)
+  struct MaskRegs { uint32_t w[KB][NB][4][MW]; };
 
   // per-thread constant addressing of the staging copies
   struct Staging {
@@ -344,10 +365,61 @@ struct MfmaFwd {
     uint64_t mbits;            // block-sparse: those columns, bit set = kept
     uint32_t unit;             // dropout: b*H + h (packed: sequence*H + h)
     uint32_t seed_lo, seed_hi, doff, dt;   // dropout: key, offset, threshold
+    const char* mbase;         // mask: row wq0 of the unit's mask
+    int mbytes;                // mask: readable bytes from mbase
+    int moff[NB];              // mask: byte offset of the lane's row, key 4hl
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
     return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
+  }
+
+  // Elementwise mask: the lane's elements of tile t.  The view ends at the
+  // wave's last row (keys rounded up to a group of 4), so loads past it read
+  // zeros; elements past the last key are never used.
+  static __device__ __forceinline__ void load_mask(MaskRegs& r, const Ctx& x, int t) {
+    const __amdgpu_buffer_rsrc_t mr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x.mbase, (short)0, x.mbytes, kBufferWord3);
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int off = x.moff[qb] + (t * BN + kk * 32 + 8 * g) * MW;
+          if (MW == 1) {
+            r.w[kk][qb][g][0] = __builtin_amdgcn_raw_buffer_load_b32(mr, off, 0, 0);
+          } else if (MW == 2) {
+            const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mr, off, 0, 0));
+#pragma unroll
+            for (int i = 0; i < MW; ++i) r.w[kk][qb][g][i] = w[i];
+          } else {
+            const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off, 0, 0));
+#pragma unroll
+            for (int i = 0; i < MW; ++i) r.w[kk][qb][g][i] = w[i];
+          }
+        }
+  }
+
+  // Score r of the lane (key 8(r/4) + 4hl + r%4 of its block) in log2
+  // units relative to the reference: s c + a log2(e) - mref for an additive
+  // mask a, s c - mref or -inf for a boolean one.
+  static __device__ __forceinline__ float mask_score(float s, float c, float mref,
+                                                     const uint32_t (&w)[4][MW], int r) {
+    const int g = r / 4, e = r % 4;
+    if (VAR == kMaskBool) {
+      const uint32_t byte = (w[g][0] >> (8 * e)) & 0xffu;
+      return byte != 0u ? __builtin_fmaf(s, c, -mref) : -INFINITY;
+    }
+    float a;
+    if (VAR == kMaskAdd) {
+      const uint32_t h = (w[g][e / 2] >> (16 * (e & 1))) & 0xffffu;
+      a = BF16 ? __uint_as_float(h << 16)
+               : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    } else {
+      a = __uint_as_float(w[g][e]);
+    }
+    return __builtin_fmaf(s, c, __builtin_fmaf(a, 1.4426950408889634f, -mref));
   }
 
   // Block-sparse: the first tile >= t whose key block the mask row keeps
@@ -464,15 +536,42 @@ struct MfmaFwd {
   // block's exponentials are redone.
   static __device__ __forceinline__ void tile(const Smem& sm, int buf, int kb, bool first,
                                               bool masked, const Ctx& x, const u32x4 (&qf)[NB][DS],
-                                              State& S) {
+                                              State& S, const MaskRegs& mr) {
     f32x16 sc[NB], sn[NB];
     scores(sc, sm, buf, 0, x.ln, qf);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
       const bool pending = kk + 1 < KB;
-      if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+      if (masked && !MASK) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
       if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf);
-      if (BSP) {
+      if (MASK) {
+        // the mask's bias is folded into the scaled scores first; pairs the
+        // causal rule or the key tail excludes are then set to -inf whatever
+        // the mask holds there.  A row's reference is set by the first block
+        // in which it has a finite score.
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float mref = S.m[qb] == -INFINITY ? 0.f : S.m[qb];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sc[qb][r] = mask_score(sc[qb][r], x.c, mref, mr.w[kk][qb], r);
+        }
+        if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+        bool unset = false;
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) {
+            const float mm = row_max(sc[qb]);
+            const bool set_now = S.m[qb] == -INFINITY && mm > -INFINITY;
+            const float sub = set_now ? mm : 0.f;
+            if (set_now) S.m[qb] = mm;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[qb][r] -= sub;
+          }
+        }
+      } else if (BSP) {
         // block-sparse: a row's reference is set by the first block in
         // which it sees a key (its first visible block can be anywhere)
         bool unset = false;
@@ -489,12 +588,14 @@ struct MfmaFwd {
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
       }
+      if (!MASK) {
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        // rows that have not seen a key yet have only -inf scores here
-        const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
+        for (int qb = 0; qb < NB; ++qb) {
+          // rows that have not seen a key yet have only -inf scores here
+          const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
+          for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
+        }
       }
       float bs[NB][2];
       u32x4 pf[NB][2];
@@ -548,15 +649,20 @@ struct MfmaFwd {
                                               const u32x4 (&qf)[NB][DS], int j, int jn) {
     KRegs kr;
     VRegs vr;
+    MaskRegs mr;
     const bool nxt = jn < x.ntiles;
+    const bool live = !skip_tile(x, j);
+    // the mask of tile j is requested before the next tile's K and V, so
+    // its wait does not include theirs
+    if (MASK && live) load_mask(mr, x, j);
     if (nxt) {
       load_k(kr, x.st, x.hd, jn, x.tid);
       load_v(vr, x.st, x.hd, jn, x.tid);
     }
-    if (!skip_tile(x, j)) {
+    if (live) {
       const int kb = j * BN;
       const bool masked = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
-      tile(sm, B, kb, !BSP && j == 0, masked, x, qf, S);
+      tile(sm, B, kb, !BSP && j == 0, masked, x, qf, S, mr);
     }
     if (nxt) {
       store_k(sm, B ^ 1, kr, x.st, x.tid);
@@ -626,6 +732,14 @@ struct MfmaFwd {
       x.doff = p.drop_offset;
       x.dt = p.drop_t;
     }
+    if (MASK && x.wave_live) {
+      const int rows = min(NB * 32, nq - x.wq0);
+      x.mbase = reinterpret_cast<const char*>(p.amask) +
+                ((int64_t)b * p.am_bs + (int64_t)h * p.am_hs + (int64_t)x.wq0 * p.am_rs) * MW;
+      x.mbytes = (int)(((int64_t)(rows - 1) * p.am_rs + ((nk + 3) & ~3)) * MW);
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) x.moff[qb] = ((qb * 32 + x.l32) * p.am_rs + 4 * x.hl) * MW;
+    }
     if (BSP) {
       x.mrow = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + (int64_t)qt * p.bm_nkb;
       x.nkb = p.bm_nkb;
@@ -647,7 +761,7 @@ struct MfmaFwd {
     State S;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
-      S.m[qb] = BSP ? -INFINITY : 0.f;
+      S.m[qb] = (BSP || MASK) ? -INFINITY : 0.f;
       S.l[qb] = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -693,8 +807,8 @@ struct MfmaFwd {
     for (int qb = 0; qb < NB; ++qb) {
       const int qi = x.wq0 + qb * 32 + x.l32;
       const float lt = pair_sum(S.l[qb]);
-      // block-sparse rows that saw no key: O = 0, lse = -inf
-      const float inv = (BSP && !(lt > 0.f)) ? 0.f : (DROP ? p.drop_scale : 1.f) / lt;
+      // block-sparse or masked rows that saw no key: O = 0, lse = -inf
+      const float inv = ((BSP || MASK) && !(lt > 0.f)) ? 0.f : (DROP ? p.drop_scale : 1.f) / lt;
       if (qi < nq) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -764,9 +878,24 @@ constexpr int kBspWavesPerSimd =
 template <int D>
 constexpr int kDropWavesPerSimd =
     D == 32 ? SDPA_DROP_WAVES_D32 : D == 64 ? SDPA_DROP_WAVES_D64 : SDPA_DROP_WAVES_D128;
+// the elementwise-mask kernels (a tile's mask elements are held in
+// registers while it is processed)
+#ifndef SDPA_MASK_WAVES_D32
+#define SDPA_MASK_WAVES_D32 4
+#endif
+#ifndef SDPA_MASK_WAVES_D64
+#define SDPA_MASK_WAVES_D64 3
+#endif
+#ifndef SDPA_MASK_WAVES_D128
+#define SDPA_MASK_WAVES_D128 2
+#endif
+template <int D>
+constexpr int kMaskWavesPerSimd =
+    D == 32 ? SDPA_MASK_WAVES_D32 : D == 64 ? SDPA_MASK_WAVES_D64 : SDPA_MASK_WAVES_D128;
 template <int D, int VAR>
 constexpr int kVariantWavesPerSimd = VAR == kBlockSparse ? kBspWavesPerSimd<D>
                                      : VAR == kDropout   ? kDropWavesPerSimd<D>
+                                     : VAR >= kMaskBool  ? kMaskWavesPerSimd<D>
                                                          : kWavesPerSimd<D>;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,

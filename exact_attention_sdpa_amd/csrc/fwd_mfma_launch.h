@@ -99,6 +99,10 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.drop_offset = a.drop_offset;
   p.drop_t = a.drop_t;
   p.drop_scale = a.drop_scale;
+  p.amask = a.amask;
+  p.am_bs = a.am_str[0];
+  p.am_hs = a.am_str[1];
+  p.am_rs = (int)a.am_str[2];
   hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
@@ -141,6 +145,26 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
   SDPA_CASE(true, true, false)
   SDPA_CASE(true, true, true)
 #undef SDPA_CASE
+  return hipErrorInvalidValue;
+}
+
+// Elementwise-mask launches (dense layouts, any strides): the dense tile
+// shapes, one instantiation per mask kind, causal flag and output type.
+template <bool BF16, int D>
+hipError_t launch_mfma_masked_d(const FwdArgs& a) {
+  if (a.cu != nullptr || a.amask == nullptr) return hipErrorInvalidValue;
+#define SDPA_MCASE(KIND, VAR)                                                          \
+  if (a.amask_kind == KIND) {                                                         \
+    if (a.causal)                                                                     \
+      return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, VAR>(a)         \
+                       : launch_mfma_inst<BF16, D, true, false, false, VAR>(a);       \
+    return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, VAR>(a)          \
+                     : launch_mfma_inst<BF16, D, false, false, false, VAR>(a);        \
+  }
+  SDPA_MCASE(SDPA_MASK_BOOL, kMaskBool)
+  SDPA_MCASE(SDPA_MASK_ADD, kMaskAdd)
+  SDPA_MCASE(SDPA_MASK_ADD_F32, kMaskAddF32)
+#undef SDPA_MCASE
   return hipErrorInvalidValue;
 }
 

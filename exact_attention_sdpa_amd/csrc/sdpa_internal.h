@@ -33,6 +33,9 @@ struct FwdArgs {
   uint32_t drop_offset;     // last Philox counter word
   uint32_t drop_t;          // keep iff the 16-bit number < drop_t
   float drop_scale;         // 1 / (1 - p)
+  const void* amask;        // elementwise mask, or null
+  int amask_kind;           // sdpa_mask_kind
+  int64_t am_str[3];        // mask (batch, head, row) strides, elements
 };
 
 // Validated arguments of one backward call (dense layouts only).
@@ -81,6 +84,13 @@ sdpa_status validate_strides(const int64_t* q_strides, const int64_t* kv_strides
 // [mask_heads][ceil(Nq/128)][ceil(Nk/128)] bytes clear of out and lse.
 sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs* a);
 
+// Adds an elementwise mask to validated dense forward arguments: kind
+// known, f16/bf16 inputs, strides non-negative multiples of 4, base aligned
+// to 4 elements, a workgroup's rows within 32-bit offsets, and the mask
+// clear of out and lse.
+sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
+                               const int64_t* mask_strides, FwdArgs* a);
+
 // Adds dropout to validated backward arguments (same rules as the forward).
 sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a);
 
@@ -103,6 +113,8 @@ int path_for(sdpa_dtype dtype, int64_t d);
 hipError_t launch_fwd_mfma_f16(const FwdArgs& a);
 hipError_t launch_fwd_mfma_bf16(const FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_fwd_mfma_masked_f16(const FwdArgs& a);
+hipError_t launch_fwd_mfma_masked_bf16(const FwdArgs& a);
 hipError_t launch_bwd_mfma_f16(const BwdArgs& a);
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a);
 

@@ -154,6 +154,9 @@ sdpa_status validate(const void* q, const void* k, const void* v, void* out, flo
   a->drop_offset = 0;
   a->drop_t = 65536;
   a->drop_scale = 1.f;
+  a->amask = nullptr;
+  a->amask_kind = SDPA_MASK_BOOL;
+  a->am_str[0] = a->am_str[1] = a->am_str[2] = 0;
   return SDPA_OK;
 }
 
@@ -205,6 +208,37 @@ sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs
   if (a->lse && overlap(mask, mb, a->lse, a->B * a->H * a->Nq * 4)) return SDPA_ERR_INVALID;
   a->bmask = mask;
   a->mask_heads = mask_heads;
+  return SDPA_OK;
+}
+
+sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
+                               const int64_t* mask_strides, FwdArgs* a) {
+  if (mask == nullptr || mask_strides == nullptr) return SDPA_ERR_INVALID;
+  if (kind != SDPA_MASK_BOOL && kind != SDPA_MASK_ADD && kind != SDPA_MASK_ADD_F32)
+    return SDPA_ERR_INVALID;
+  if (a->cu != nullptr) return SDPA_ERR_INVALID;
+  if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
+  const int64_t eb = kind == SDPA_MASK_BOOL ? 1 : kind == SDPA_MASK_ADD ? 2 : 4;
+  const int64_t lim = (int64_t)1 << 40;
+  for (int i = 0; i < 3; ++i)
+    if (mask_strides[i] < 0 || mask_strides[i] > lim || mask_strides[i] % 4 != 0)
+      return SDPA_ERR_INVALID;
+  if (!aligned(mask, (uintptr_t)(4 * eb))) return SDPA_ERR_INVALID;
+  const int64_t nk4 = (a->Nk + 3) / 4 * 4;
+  // a workgroup reads its rows through 32-bit byte offsets
+  if ((256 * mask_strides[2] + nk4) * eb > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
+  const __int128 span = ((__int128)(a->B - 1) * mask_strides[0] +
+                         (__int128)(a->H - 1) * mask_strides[1] +
+                         (__int128)(a->Nq - 1) * mask_strides[2] + nk4) * eb;
+  if (span > (__int128)(INT64_MAX / 2)) return SDPA_ERR_INVALID;
+  const int64_t ob = a->out_f32 ? 4 : elem_bytes(a->dtype);
+  const int64_t os = span_bytes(a->B, a->H, a->Nq, a->d, a->o_str, ob);
+  if (os < 0 || overlap(mask, (int64_t)span, a->out, os)) return SDPA_ERR_INVALID;
+  if (a->lse && overlap(mask, (int64_t)span, a->lse, a->B * a->H * a->Nq * 4))
+    return SDPA_ERR_INVALID;
+  a->amask = mask;
+  a->amask_kind = kind;
+  for (int i = 0; i < 3; ++i) a->am_str[i] = mask_strides[i];
   return SDPA_OK;
 }
 

@@ -42,6 +42,7 @@ import numpy as np
 
 # tensor ids for SeedSequence
 _TID_Q, _TID_K, _TID_V, _TID_LEN, _TID_FORCE, _TID_ROWS, _TID_DO, _TID_MASK = range(8)
+_TID_AMASK, _TID_AMASK_DROP = 8, 9
 
 # largest float16 strictly below 1.0; uniform draws are clamped here so that
 # rounding to f16 never produces 1.0 (the pages' torch.rand is [0, 1)).
@@ -256,6 +257,29 @@ def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False
 
 CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long",
                 6: "block_sparse"}
+
+
+def make_attn_mask(shape, kind: str, keep: float = 0.75, bias_std: float = 2.0, seed=0,
+                   cfg=0, dtype="f16") -> np.ndarray:
+    """A seeded elementwise attention mask of ``shape``.
+
+    kind "bool": uint8 0/1, each pair kept (1) with probability ``keep``.
+    kind "add":  additive values ~ N(0, bias_std) rounded to ``dtype``
+                 ("f16", "bf16" as uint16 bits, or "f32"), and -inf where an
+                 independent draw drops the pair (probability 1 - keep)."""
+    drop = _rng(seed, cfg, _TID_AMASK_DROP).random(shape) >= keep
+    if kind == "bool":
+        return (~drop).astype(np.uint8)
+    a = (_rng(seed, cfg, _TID_AMASK).standard_normal(shape) * bias_std).astype(np.float32)
+    a[drop] = -np.inf
+    return to_storage(a, dtype)
+
+
+def key_padding_mask(lens, max_len: int) -> np.ndarray:
+    """uint8 [B, 1, 1, max_len]: key j of batch b is kept iff j < lens[b]
+    (a padded dense batch of the NestedTensor recipe's sequences)."""
+    lens = np.asarray(lens)
+    return (np.arange(max_len)[None, :] < lens[:, None]).astype(np.uint8)[:, None, None, :]
 
 
 def make_config(i: int, seed: int = 0) -> Workload:

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 6
+#define SDPA_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -139,6 +139,52 @@ SDPA_API sdpa_status sdpa_fwd_strided(const void* q, const void* k, const void* 
                                       const int64_t* kv_strides, const int64_t* out_strides,
                                       float scale, int is_causal, sdpa_dtype dtype,
                                       sdpa_dtype out_dtype, void* stream);
+
+/* Element types of an elementwise attention mask (sdpa_fwd_masked). */
+typedef enum {
+  SDPA_MASK_BOOL = 0,    /* one byte per pair (torch.bool storage): nonzero = attend */
+  SDPA_MASK_ADD = 1,     /* additive, in the input element type (f16 or bf16)    */
+  SDPA_MASK_ADD_F32 = 2  /* additive, f32                                          */
+} sdpa_mask_kind;
+
+/* Forward with an elementwise attention mask.  The SDPA tutorial's
+ * functional call takes an `attn_mask` argument (its CausalSelfAttention
+ * passes None; "Fused implementations" and "Causal self-attention") but the
+ * pages do not define it; the reading taken is the functional API's
+ * convention.  A boolean mask says which (query, key) pairs take part; an
+ * additive mask a is added to the scaled scores before the softmax:
+ *     s_ij = scale * <q_i, k_j> + a_ij    (a_ij = 0 or -inf for a boolean mask)
+ * then out and lse as sdpa_fwd, over the keys the causal rule leaves when
+ * is_causal is set (both restrictions apply).  A row whose every score is
+ * -inf gets out = 0 and lse = -inf.
+ *
+ * mask       device pointer; element (b, h, i, j) lives at
+ *            mask + b*ms[0] + h*ms[1] + i*ms[2] + j (elements).  Base aligned
+ *            to 4 elements.  Rows are read in groups of 4 elements: elements
+ *            j in [Nk, roundup(Nk, 4)) of every row must be readable (their
+ *            values are ignored).  Additive values must be finite or -inf.
+ * mask_kind  SDPA_MASK_BOOL, SDPA_MASK_ADD (the input type) or
+ *            SDPA_MASK_ADD_F32.
+ * mask_strides  host array of 3 int64 (ms[0..2]: batch, head, row), each a
+ *            non-negative multiple of 4; 0 broadcasts that dimension (e.g.
+ *            a key-padding mask [B, 1, 1, Nk] has ms[1] = ms[2] = 0).
+ * q_strides, kv_strides, out_strides  all NULL (contiguous layouts, as
+ *            sdpa_fwd) or all given (as sdpa_fwd_strided).
+ * Other arguments as sdpa_fwd; dense layouts only, dtype SDPA_F16 or
+ * SDPA_BF16.  The mask must not overlap out or lse.
+ *
+ * Returns SDPA_ERR_INVALID for a null mask or strides, an unknown kind,
+ * misaligned mask or strides, or overlap; SDPA_ERR_UNSUPPORTED for f32
+ * inputs or rows too far apart for 32-bit offsets (256 * ms[2] elements
+ * beyond 2^31 bytes); otherwise as sdpa_fwd / sdpa_fwd_strided.
+ */
+SDPA_API sdpa_status sdpa_fwd_masked(const void* q, const void* k, const void* v, void* out,
+                                     float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                     int64_t d, const int64_t* q_strides,
+                                     const int64_t* kv_strides, const int64_t* out_strides,
+                                     float scale, int is_causal, const void* mask,
+                                     sdpa_mask_kind mask_kind, const int64_t* mask_strides,
+                                     sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
 
 /* Block size of block-sparse masks: 128 query rows x 128 keys. */
 #define SDPA_BLOCK_SPARSE_BLOCK 128

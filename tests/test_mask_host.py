@@ -1,0 +1,68 @@
+"""Host-side checks of the elementwise-mask entry point (sdpa_fwd_masked):
+every malformed call is rejected before any device work."""
+import ctypes
+
+import pytest
+
+from exact_attention_sdpa_amd import _lib
+
+OK, INVALID, UNSUPPORTED, LAUNCH, DEVICE = range(5)
+F16, BF16, F32, SAME = 0, 1, 2, 255
+MBOOL, MADD, MF32 = 0, 1, 2
+
+# fake, distinct, aligned addresses (never dereferenced on these paths)
+Q, K, V, O, L, M = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x6000000, 0x10000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def arr(s):
+    return None if s is None else ctypes.cast((ctypes.c_int64 * 3)(*s), ctypes.c_void_p)
+
+
+def call(lib, ms=(4 * 128 * 128, 128 * 128, 128), kind=MBOOL, mask=M, B=2, H=4, N=128, d=64,
+         dt=F16, strides=None, o=O, lse=L, causal=0):
+    qs = ks = os_ = strides
+    return lib.sdpa_fwd_masked(Q, K, V, o, lse, B, H, N, N, d, arr(qs), arr(ks), arr(os_),
+                               0.125, causal, mask, kind, arr(ms), dt, SAME, None)
+
+
+def test_valid_masked_calls_reach_the_device_check(lib):
+    for kind in (MBOOL, MADD, MF32):
+        assert call(lib, kind=kind) in (OK, DEVICE)
+        assert call(lib, kind=kind, causal=1) in (OK, DEVICE)
+    # broadcasts: one mask for every head and batch, a key-padding row
+    assert call(lib, ms=(0, 0, 128)) in (OK, DEVICE)
+    assert call(lib, ms=(128, 0, 0)) in (OK, DEVICE)
+    # with explicit q/k/v/out strides (packed QKV layout)
+    assert call(lib, strides=(128 * 768, 64, 768), o=0x8000000,
+                lse=0x9000000) in (OK, DEVICE)
+
+
+def test_masked_calls_rejected_on_host(lib):
+    assert call(lib, mask=None) == INVALID
+    assert lib.sdpa_fwd_masked(Q, K, V, O, L, 2, 4, 128, 128, 64, None, None, None, 0.125, 0,
+                               M, MBOOL, None, F16, SAME, None) == INVALID   # no mask strides
+    assert call(lib, kind=7) == INVALID
+    assert call(lib, ms=(-4, 0, 128)) == INVALID
+    assert call(lib, ms=(0, 0, 130)) == INVALID          # row stride not a multiple of 4
+    assert call(lib, kind=MF32, mask=M + 4) == INVALID   # f32 mask not 16-byte aligned
+    assert call(lib, kind=MADD, mask=M + 4) == INVALID   # 16-bit mask not 8-byte aligned
+    assert call(lib, kind=MBOOL, mask=M + 4) in (OK, DEVICE)   # bytes: 4-byte aligned is fine
+    assert call(lib, kind=MBOOL, mask=M + 2) == INVALID
+    assert call(lib, dt=F32) == UNSUPPORTED               # f32 inputs
+    # the mask must not overlap the output or the logsumexp
+    assert call(lib, mask=O) == INVALID
+    assert call(lib, mask=L) == INVALID
+    # rows too far apart for a workgroup's 32-bit offsets
+    assert call(lib, kind=MF32, ms=(0, 0, 1 << 21)) == UNSUPPORTED
+    # only some of q/k/v/out strides given
+    assert lib.sdpa_fwd_masked(Q, K, V, O, L, 2, 4, 128, 128, 64, arr((128 * 768, 64, 768)),
+                               None, None, 0.125, 0, M, MBOOL, arr((0, 0, 128)), F16, SAME,
+                               None) == INVALID
+    # errors of the dense forward still apply
+    assert call(lib, d=48) == UNSUPPORTED
+    assert call(lib, N=0) == INVALID

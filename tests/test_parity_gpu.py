@@ -289,6 +289,16 @@ def test_unsupported_raises():
     with pytest.raises(S.SdpaError):     # dropout needs f16/bf16 inputs
         q32 = q[..., :32].float()
         S.scaled_dot_product_attention(q32, q32, q32, dropout_p=0.1)
-    with pytest.raises(S.SdpaError):
-        S.scaled_dot_product_attention(q[..., :32], q[..., :32], q[..., :32],
-                                       attn_mask=torch.ones(8, 8, device="cuda"))
+    q32h = q[..., :32].contiguous()
+    with pytest.raises(S.SdpaError):     # masks: bool, the input dtype or f32 only
+        S.scaled_dot_product_attention(q32h, q32h, q32h,
+                                       attn_mask=torch.ones(8, 8, dtype=torch.float64,
+                                                            device="cuda"))
+    with pytest.raises(S.SdpaError):     # a mask together with dropout
+        S.scaled_dot_product_attention(q32h, q32h, q32h, dropout_p=0.1,
+                                       attn_mask=torch.ones(8, 8, dtype=torch.bool,
+                                                            device="cuda"))
+    with pytest.raises(S.SdpaError):     # a mask that does not broadcast to [B,H,Nq,Nk]
+        S.scaled_dot_product_attention(q32h, q32h, q32h,
+                                       attn_mask=torch.ones(7, 8, dtype=torch.bool,
+                                                            device="cuda"))
