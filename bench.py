@@ -11,7 +11,9 @@ benchmark).  Prints one JSON line.
 
 Throughput counts 4*B*H*Nq*Nk*d FLOPs per step (halved when causal; summed
 per sequence for packed batches; 4*d per visible (query, key) pair for the
-block-sparse workload, which calls sdpa_fwd_block_sparse).  `--dropout P`
+block-sparse workload, which calls sdpa_fwd_block_sparse; every pair for the
+elementwise-mask workloads, which call sdpa_fwd_masked and compute every
+pair).  `--dropout P`
 times sdpa_fwd_dropout instead (same FLOPs).  `roofline.achieved` divides the
 same FLOPs by the kernel's own average duration from HIP events recorded around
 each launch on the launch stream; the peak is MI355X's published dense
@@ -38,7 +40,9 @@ PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak (published)
 # unstated): 2262.901 us -> 4*32*32*1024*1024*32 / 2262.901e-6 = 60.74 TFLOP/s
 PAGES_FLASH_TFLOPS = 137.438953472e9 / 2262.901e-6 / 1e12
 
-WORKLOADS = {"noncausal": 2, "causal": 3, "varlen": 4, "long": 5, "block_sparse": 6}
+WORKLOADS = {"noncausal": 2, "causal": 3, "varlen": 4, "long": 5, "block_sparse": 6,
+             "masked": 7, "padded": 8}
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E (published)
 
 
 def _code_only(src: str) -> str:
@@ -93,7 +97,36 @@ def describe(w, name, dropout=0.0):
         cfg["block_mask"] = (f"{w.block_mask.shape[0]} x {w.block_mask.shape[1]} x "
                              f"{w.block_mask.shape[2]} blocks of 128x128, p=1/4 + diagonal, "
                              f"{100 * float(w.block_mask.mean()):.2f}% kept")
+    if w.attn_mask is not None:
+        import numpy as np
+
+        from exact_attention_sdpa_amd import inputs
+        shape = "x".join(str(x) for x in w.attn_mask.shape)
+        cfg["workload"] += f" {w.mask_kind} mask [{shape}]"
+        cfg["attn_mask"] = (f"{w.mask_kind} [{shape}]"
+                            + (f" {w.dtype}, N(0,2), {100 * float(np.mean(np.isneginf(inputs.storage_to_f64(w.attn_mask, w.dtype)))):.1f}% -inf"
+                               if w.mask_kind == "add" else
+                               f", {100 * float(np.mean(w.attn_mask)):.1f}% of keys kept"))
     return cfg
+
+
+def mask_bytes(w) -> int:
+    """Bytes of the elementwise mask as stored (read once per launch)."""
+    if w.attn_mask is None:
+        return 0
+    return int(w.attn_mask.size) * (1 if w.mask_kind == "bool" else
+                                    (4 if w.dtype == "f32" else 2))
+
+
+def algorithmic_bytes(w):
+    """(read, written) bytes per launch: q, k, v and the mask read once; out
+    and lse written once (bf16 inputs write an f32 out)."""
+    el = 2 if w.dtype != "f32" else 4
+    rows_q = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nq
+    rows_k = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nk
+    out_el = 4 if w.dtype == "bf16" else el
+    return ((rows_q + 2 * rows_k) * w.H * w.d * el + mask_bytes(w),
+            rows_q * w.H * (w.d * out_el + 4))
 
 
 def cpu_baseline(w, budget_s: float, dropout: float = 0.0):
@@ -113,6 +146,8 @@ def cpu_baseline(w, budget_s: float, dropout: float = 0.0):
         return _cpu_baseline_block_sparse(w, budget_s, threads)
     if dropout > 0:
         return _cpu_baseline_dropout(w, budget_s, threads, dropout)
+    if w.attn_mask is not None:
+        return _cpu_baseline_masked(w, budget_s, threads)
     flops = 0.0
     n = 0
     t0 = time.perf_counter()
@@ -175,6 +210,35 @@ def _cpu_baseline_block_sparse(w, budget_s, threads):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units, last 256 "
                                         f"query rows each",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _cpu_baseline_masked(w, budget_s, threads):
+    """The fp64 masked oracle on whole (batch, head) units in turn, FLOPs
+    counted as the metric does (every pair)."""
+    import numpy as np
+
+    from exact_attention_sdpa_amd import inputs
+    from oracle import masked as om
+    m = w.attn_mask
+    m = m.reshape((1,) * (4 - m.ndim) + m.shape)
+    flops, n = 0.0, 0
+    units = [(b, h) for b in range(w.B) for h in range(w.H)]
+    t0 = time.perf_counter()
+    for b, h in units:
+        dec = lambda x: inputs.storage_to_f64(x[b:b + 1, h:h + 1], w.dtype)
+        mu = m[b % m.shape[0], h % m.shape[1]]
+        mu = mu if w.mask_kind == "bool" else inputs.storage_to_f64(mu, w.dtype)
+        mu = np.broadcast_to(mu, (w.Nq, w.Nk))
+        om.sdpa_fwd_masked(dec(w.q), dec(w.k), dec(w.v), mu[None, None], w.mask_kind,
+                           w.scale, w.is_causal)
+        flops += 4.0 * w.Nq * w.Nk * w.d / (2 if w.is_causal else 1)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units",
             "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -296,12 +360,7 @@ def summarize(a) -> int:
     write_b = write * wfac * 1024
     from exact_attention_sdpa_amd import inputs
     w = inputs.make_config(WORKLOADS[a.workload])
-    el = 2 if w.dtype != "f32" else 4
-    rows_q = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nq
-    rows_k = int(w.cu_seqlens[-1]) if w.varlen else w.B * w.Nk
-    out_el = 4 if w.dtype == "bf16" else el
-    alg_read = (rows_q + 2 * rows_k) * w.H * w.d * el
-    alg_write = rows_q * w.H * (w.d * out_el + 4)
+    alg_read, alg_write = algorithmic_bytes(w)
     name = k["Name"].split("(")[0].replace("void ", "").replace("sdpa::", "")
     tag = f"fwd_mfma_{a.workload}" + ("_dropout" if a.dropout > 0 else "")
     dflag = f" --dropout {a.dropout:g}" if a.dropout > 0 else ""
@@ -328,7 +387,7 @@ def summarize(a) -> int:
         f"  kernel: FETCH_SIZE {fetch:.0f} KiB/dispatch ({nf} dispatches), WRITE_SIZE {write:.0f} "
         f"KiB/dispatch ({nw})",
         f"  -> {read_b / 1e6:.2f} MB read + {write_b / 1e6:.2f} MB written per launch",
-        f"  algorithmic (q,k,v read once; out and lse written once): {alg_read / 1e6:.2f} MB read + "
+        f"  algorithmic (q,k,v{', mask' if w.attn_mask is not None else ''} read once; out and lse written once): {alg_read / 1e6:.2f} MB read + "
         f"{alg_write / 1e6:.2f} MB written",
         f"  measured / algorithmic: read {read_b / alg_read:.3f}, write {write_b / alg_write:.3f}",
         f"  achieved HBM rate at the average duration: {(read_b + write_b) / avg_ns:.1f} GB/s",
@@ -448,8 +507,28 @@ def main(argv=None) -> int:
             if st != 0:
                 raise sdpa.SdpaError(st)
 
+    if w.attn_mask is not None:
+        import ctypes
+        if a.dropout > 0:
+            print("bench.py: dropout with an elementwise mask is not supported", file=sys.stderr)
+            return 2
+        m = w.attn_mask
+        m = m.reshape((1,) * (4 - m.ndim) + m.shape)
+        mt = (torch.from_numpy(np.ascontiguousarray(m)).cuda() if w.mask_kind == "bool"
+              else up(m))
+        mstr = tuple(st if n > 1 else 0 for st, n in zip(mt.stride()[:3], mt.shape[:3]))
+        mstr_c = (ctypes.c_int64 * 3)(*mstr)
+        mkind = sdpa.SDPA_MASK_BOOL if w.mask_kind == "bool" else sdpa.SDPA_MASK_ADD
+        margs = args[:10] + [None, None, None, float(w.scale), int(w.is_causal), mt.data_ptr(),
+                             mkind, ctypes.cast(mstr_c, ctypes.c_void_p), dt, odt, handle]
+
+        def step():  # noqa: F811 -- the elementwise-mask entry point
+            st = L.sdpa_fwd_masked(*margs)
+            if st != 0:
+                raise sdpa.SdpaError(st)
+
     if a.which == "bwd":
-        if w.varlen or w.block_mask is not None:
+        if w.varlen or w.block_mask is not None or w.attn_mask is not None:
             print("bench.py: the backward pass takes dense, unmasked inputs only",
                   file=sys.stderr)
             return 2
@@ -507,6 +586,20 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / a.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kmean * 1e-3) / 1e12
+    # the elementwise-mask workload reads a mask as large as the score
+    # matrix: its kernel is bound by HBM, so its roofline is bytes / time
+    hbm_bound = a.workload == "masked" and a.which == "fwd"
+    if hbm_bound:
+        alg_bytes = sum(algorithmic_bytes(w))
+        roof = {"bound": "hbm", "achieved": round(alg_bytes / (kmean * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(alg_bytes / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes": alg_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4)}
+    roof["traffic"] = (stored_traffic(a.workload + ("_dropout" if a.dropout > 0 else ""))
+                       if a.which == "fwd" else None)
     rec = {
         "metric": METRIC if a.which == "fwd" else METRIC_BWD,
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -519,10 +612,7 @@ def main(argv=None) -> int:
         "kernel_ms": {"mean": round(kmean, 4), "median_single": round(float(np.median(kern_ms)), 4),
                       "min_single": round(float(np.min(kern_ms)), 4),
                       "stdev_single": round(float(np.std(kern_ms)), 4)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": (stored_traffic(a.workload + ("_dropout" if a.dropout > 0 else ""))
-                                 if a.which == "fwd" else None)},
+        "roofline": roof,
     }
     if a.which == "bwd":
         rec["kernels"] = "rowdot + dq + dkdv (kernel_ms spans all three)"

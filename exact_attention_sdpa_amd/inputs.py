@@ -6,7 +6,8 @@ exactly.  The oracle and the GPU path both consume what it produces.
 
 Every tensor comes from ``numpy.random.default_rng(SeedSequence([seed, cfg,
 tensor_id]))`` with tensor ids q=0, k=1, v=2, lengths=3, forced index=4,
-sampled rows=5, upstream gradient dO=6, block mask=7, so a workload is reproducible on any
+sampled rows=5, upstream gradient dO=6, block mask=7, elementwise mask values=8
+and drops=9, so a workload is reproducible on any
 machine with no torch
 RNG involved.  Values are drawn in float32 and rounded to the storage dtype
 with round-to-nearest-even (bf16 rounding is done on the bit pattern).
@@ -31,6 +32,16 @@ Workloads (each stands in for a workload printed on the pages):
                 d=64, bf16, non-causal, one mask per head over 128x128
                 blocks, each block kept with probability 1/4 and the
                 diagonal blocks always kept (the pages give no mask).
+7. masked    -- the tutorial's functional call with an ``attn_mask`` (its
+                module passes None; the pages give no mask): the causal
+                workload's shape, non-causal, with an additive f16 bias per
+                (batch, head, query, key) ~ N(0, 2), a quarter of the pairs
+                set to -inf.
+8. padded    -- the dense side of the tutorial's NestedTensor comparison:
+                workload 4's lengths in a dense [32, 8, 512, 64] f16 batch
+                padded to 512, keys past each length masked by a boolean
+                key-padding mask [32, 1, 1, 512] (padding rows hold random
+                values: the kernel computes them like any other row).
 """
 from __future__ import annotations
 
@@ -125,6 +136,8 @@ class Workload:
     cu_seqlens: Optional[np.ndarray] = None
     rows: Optional[np.ndarray] = None  # sampled query rows (dense only)
     block_mask: Optional[np.ndarray] = None  # uint8 [Hm, nqb, nkb] (dense only)
+    attn_mask: Optional[np.ndarray] = None   # elementwise mask, broadcast to [B,H,Nq,Nk]
+    mask_kind: Optional[str] = None          # "bool" or "add" (stored in ``dtype``)
 
     @property
     def varlen(self) -> bool:
@@ -255,7 +268,8 @@ def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False
     return m
 
 
-CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long",
+CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long", 7: "masked",
+                8: "padded",
                 6: "block_sparse"}
 
 
@@ -267,10 +281,10 @@ def make_attn_mask(shape, kind: str, keep: float = 0.75, bias_std: float = 2.0, 
     kind "add":  additive values ~ N(0, bias_std) rounded to ``dtype``
                  ("f16", "bf16" as uint16 bits, or "f32"), and -inf where an
                  independent draw drops the pair (probability 1 - keep)."""
-    drop = _rng(seed, cfg, _TID_AMASK_DROP).random(shape) >= keep
+    drop = _rng(seed, cfg, _TID_AMASK_DROP).random(shape, dtype=np.float32) >= keep
     if kind == "bool":
         return (~drop).astype(np.uint8)
-    a = (_rng(seed, cfg, _TID_AMASK).standard_normal(shape) * bias_std).astype(np.float32)
+    a = _rng(seed, cfg, _TID_AMASK).standard_normal(shape, dtype=np.float32) * np.float32(bias_std)
     a[drop] = -np.inf
     return to_storage(a, dtype)
 
@@ -305,5 +319,21 @@ def make_config(i: int, seed: int = 0) -> Workload:
                        name="block_sparse")
         w.block_mask = make_block_mask(16, 65536, 65536, 0.25, diagonal=True, seed=seed, cfg=6)
         w.rows = sample_rows(65536, 256, seed, 6)
+        return w
+    if i == 7:
+        # an additive f16 bias per (batch, head, query, key), a quarter of
+        # the pairs dropped with -inf, on the causal workload's shape
+        w = make_dense(32, 8, 1024, 1024, 64, "f16", "normal", False, seed, 7, name="masked")
+        w.attn_mask = make_attn_mask((32, 8, 1024, 1024), "add", keep=0.75, bias_std=2.0,
+                                     seed=seed, cfg=7, dtype="f16")
+        w.mask_kind = "add"
+        return w
+    if i == 8:
+        # the NestedTensor recipe's sequences as a padded dense batch with a
+        # key-padding mask (the dense side of the tutorial's comparison)
+        lens = nested_lengths(32, 512, 0.5, seed, 4)
+        w = make_dense(32, 8, 512, 512, 64, "f16", "normal", False, seed, 8, name="padded")
+        w.attn_mask = key_padding_mask(lens, 512)
+        w.mask_kind = "bool"
         return w
     raise ValueError(f"no config {i}")

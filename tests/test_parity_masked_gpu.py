@@ -197,3 +197,32 @@ def test_all_true_mask_matches_plain_kernel():
     torch.cuda.synchronize()
     G.assert_parity(a.double().cpu().numpy(), b.double().cpu().numpy(), "f16", "all-true",
                     la.double().cpu().numpy(), lb.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_bench_workloads_sampled_units(cfg):
+    # the masked and padded workloads at full size, in the launch the
+    # benchmark times (sdpa_fwd_masked, same mask layout and output type);
+    # whole (batch, head) units sampled against the fp64 oracle
+    w = inputs.make_config(cfg)
+    q, k, v = (G.to_device(x, w.dtype) for x in (w.q, w.k, w.v))
+    m = w.attn_mask
+    mt = (torch.from_numpy(m).cuda().bool() if w.mask_kind == "bool"
+          else G.to_device(m, w.dtype))
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, attn_mask=mt, is_causal=w.is_causal,
+                                                 scale=float(w.scale), return_lse=True)
+    torch.cuda.synchronize()
+    m4 = m.reshape((1,) * (4 - m.ndim) + m.shape)
+    rng = np.random.default_rng(cfg)
+    units = [(0, 0), (w.B - 1, w.H - 1)] + [tuple(x) for x in
+                                           zip(rng.integers(0, w.B, 4), rng.integers(0, w.H, 4))]
+    for b, h in units:
+        mu = m4[b % m4.shape[0], h % m4.shape[1]]
+        mu = mu if w.mask_kind == "bool" else inputs.storage_to_f64(mu, w.dtype)
+        mu = np.broadcast_to(mu, (w.Nq, w.Nk))[None, None]
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        ref, lref = oracle.sdpa_fwd_masked(sl(w.q64), sl(w.k64), sl(w.v64), mu, w.mask_kind,
+                                           w.scale, w.is_causal)
+        G.assert_parity(out[b:b + 1, h:h + 1].double().cpu().numpy(), ref, w.dtype,
+                        f"{w.name} unit ({b}, {h})", lse[b:b + 1, h:h + 1].double().cpu().numpy(),
+                        lref)
