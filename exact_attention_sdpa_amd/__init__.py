@@ -346,8 +346,9 @@ def _mask_operand(attn_mask, q, B, H, Nq, Nk, no_heads=False):
     """(tensor, kind, strides) for sdpa_fwd_masked: the mask viewed as
     [B,H,Nq,Nk] with broadcast dimensions at stride 0.  A mask whose layout
     the kernel cannot read in place (key stride not 1, other strides not
-    multiples of 4, misaligned base, or Nk not a multiple of 4) is copied
-    into rows padded to a multiple of 4 elements."""
+    multiples of 4, misaligned base, or Nk not a multiple of 16: rows are
+    read in blocks of 16) is copied into rows padded to a multiple of 16
+    elements."""
     import torch
     if attn_mask.dtype == torch.bool:
         kind, m = SDPA_MASK_BOOL, attn_mask.view(torch.uint8)
@@ -372,12 +373,12 @@ def _mask_operand(attn_mask, q, B, H, Nq, Nk, no_heads=False):
         return tuple(x if n > 1 else 0 for x, n in zip(t.stride()[:3], t.shape[:3]))
 
     st = eff(m4)
-    if not (Nk % 4 == 0 and (m4.stride(3) == 1 or Nk == 1) and all(x % 4 == 0 for x in st)
+    if not (Nk % 16 == 0 and m4.stride(3) == 1 and all(x % 4 == 0 for x in st)
             and m4.data_ptr() % (4 * eb) == 0):
-        nk4 = -(-Nk // 4) * 4
-        pad = torch.zeros(tuple(m.shape[:3]) + (nk4,), dtype=m.dtype, device=m.device)
+        nk16 = -(-Nk // 16) * 16
+        pad = torch.zeros(tuple(m.shape[:3]) + (nk16,), dtype=m.dtype, device=m.device)
         pad[..., :Nk] = m.expand(tuple(m.shape[:3]) + (Nk,))
-        m4 = pad.expand(B, H, Nq, nk4)
+        m4 = pad.expand(B, H, Nq, nk16)
         st = eff(m4)
     return m4, kind, st
 

@@ -367,38 +367,71 @@ struct MfmaFwd {
     uint32_t seed_lo, seed_hi, doff, dt;   // dropout: key, offset, threshold
     const char* mbase;         // mask: row wq0 of the unit's mask
     int mbytes;                // mask: readable bytes from mbase
-    int moff[NB];              // mask: byte offset of the lane's row, key 4hl
+    int moff[NB];              // mask: byte offset of the lane's row and first key
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
     return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
   }
 
-  // Elementwise mask: the lane's elements of tile t.  The view ends at the
-  // wave's last row (keys rounded up to a group of 4), so loads past it read
-  // zeros; elements past the last key are never used.
+  // Elementwise mask: the lane's elements of tile t, by 32-key block.  The
+  // view ends at the wave's last row (keys rounded up to 16), so loads past
+  // it read zeros; elements past the last key are never used.
+  //   bool, 16-bit: the lane pair (l, l^32) reads the row's block as two
+  //   contiguous halves (keys 16hl..16hl+15: one 16-byte load for bytes, two
+  //   for 16-bit values), then v_permlane32_swap trades the 4-key groups each
+  //   lane does not own for those it does, so that a load instruction
+  //   touches each row's cache line once per half block rather than once
+  //   per group.
+  //   f32: one 16-byte load per 4-key group (a group is 16 bytes already).
   static __device__ __forceinline__ void load_mask(MaskRegs& r, const Ctx& x, int t) {
     const __amdgpu_buffer_rsrc_t mr =
         __builtin_amdgcn_make_buffer_rsrc((void*)x.mbase, (short)0, x.mbytes, kBufferWord3);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb)
+      for (int qb = 0; qb < NB; ++qb) {
+        const int off = x.moff[qb] + (t * BN + kk * 32) * MW;
+        uint32_t(&w)[4][MW] = r.w[kk][qb];
+        if constexpr (MW == 1) {
+          // d[i] = keys 16hl + 4i..4i+3; after the swaps lane hl holds
+          // groups g = 0, 2 in d0, d1 and g = 1, 3 in d2, d3
+          const u32x4 d = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off, 0, 0));
+          const auto s01 = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
+          const auto s23 = __builtin_amdgcn_permlane32_swap(d[2], d[3], false, false);
+          w[0][0] = s01[0];
+          w[2][0] = s01[1];
+          w[1][0] = s23[0];
+          w[3][0] = s23[1];
+        } else if constexpr (MW == 2) {
+          // a = keys 16hl + 0..7, b = keys 16hl + 8..15 (2 per word); after
+          // the swaps words 0-1 of a and b hold groups 0 and 1, words 2-3
+          // groups 2 and 3
+          const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off, 0, 0));
+          const u32x4 b =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off + 16, 0, 0));
+          const auto a0 = __builtin_amdgcn_permlane32_swap(a[0], a[2], false, false);
+          const auto a1 = __builtin_amdgcn_permlane32_swap(a[1], a[3], false, false);
+          const auto b0 = __builtin_amdgcn_permlane32_swap(b[0], b[2], false, false);
+          const auto b1 = __builtin_amdgcn_permlane32_swap(b[1], b[3], false, false);
+          w[0][0] = a0[0];
+          w[0][1] = a1[0];
+          w[2][0] = a0[1];
+          w[2][1] = a1[1];
+          w[1][0] = b0[0];
+          w[1][1] = b1[0];
+          w[3][0] = b0[1];
+          w[3][1] = b1[1];
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int off = x.moff[qb] + (t * BN + kk * 32 + 8 * g) * MW;
-          if (MW == 1) {
-            r.w[kk][qb][g][0] = __builtin_amdgcn_raw_buffer_load_b32(mr, off, 0, 0);
-          } else if (MW == 2) {
-            const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mr, off, 0, 0));
+          for (int g = 0; g < 4; ++g) {
+            const u32x4 v = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off + 32 * g, 0, 0));
 #pragma unroll
-            for (int i = 0; i < MW; ++i) r.w[kk][qb][g][i] = w[i];
-          } else {
-            const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, off, 0, 0));
-#pragma unroll
-            for (int i = 0; i < MW; ++i) r.w[kk][qb][g][i] = w[i];
+            for (int i = 0; i < MW; ++i) w[g][i] = v[i];
           }
         }
+      }
   }
 
   // Score r of the lane (key 8(r/4) + 4hl + r%4 of its block) in log2
@@ -653,7 +686,8 @@ struct MfmaFwd {
     const bool nxt = jn < x.ntiles;
     const bool live = !skip_tile(x, j);
     // the mask of tile j is requested before the next tile's K and V, so
-    // its wait does not include theirs
+    // its wait does not include theirs (requesting it a step ahead, into a
+    // second register set, measured slower)
     if (MASK && live) load_mask(mr, x, j);
     if (nxt) {
       load_k(kr, x.st, x.hd, jn, x.tid);
@@ -736,9 +770,12 @@ struct MfmaFwd {
       const int rows = min(NB * 32, nq - x.wq0);
       x.mbase = reinterpret_cast<const char*>(p.amask) +
                 ((int64_t)b * p.am_bs + (int64_t)h * p.am_hs + (int64_t)x.wq0 * p.am_rs) * MW;
-      x.mbytes = (int)(((int64_t)(rows - 1) * p.am_rs + ((nk + 3) & ~3)) * MW);
+      x.mbytes = (int)(((int64_t)(rows - 1) * p.am_rs + ((nk + 15) & ~15)) * MW);
+      // bool / 16-bit: the lane's half block starts at key 16hl; f32: its
+      // first group at key 4hl
+      const int k0 = MW == 4 ? 4 * x.hl : 16 * x.hl;
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) x.moff[qb] = ((qb * 32 + x.l32) * p.am_rs + 4 * x.hl) * MW;
+      for (int qb = 0; qb < NB; ++qb) x.moff[qb] = ((qb * 32 + x.l32) * p.am_rs + k0) * MW;
     }
     if (BSP) {
       x.mrow = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + (int64_t)qt * p.bm_nkb;
@@ -889,13 +926,26 @@ constexpr int kDropWavesPerSimd =
 #ifndef SDPA_MASK_WAVES_D128
 #define SDPA_MASK_WAVES_D128 2
 #endif
-template <int D>
+// boolean masks hold a quarter of the registers of f32 ones (4 waves per
+// SIMD at d = 64 spill a few registers and still measure 13% faster than 3)
+#ifndef SDPA_MASKB_WAVES_D32
+#define SDPA_MASKB_WAVES_D32 4
+#endif
+#ifndef SDPA_MASKB_WAVES_D64
+#define SDPA_MASKB_WAVES_D64 4
+#endif
+#ifndef SDPA_MASKB_WAVES_D128
+#define SDPA_MASKB_WAVES_D128 2
+#endif
+template <int D, int VAR>
 constexpr int kMaskWavesPerSimd =
-    D == 32 ? SDPA_MASK_WAVES_D32 : D == 64 ? SDPA_MASK_WAVES_D64 : SDPA_MASK_WAVES_D128;
+    VAR == kMaskBool
+        ? (D == 32 ? SDPA_MASKB_WAVES_D32 : D == 64 ? SDPA_MASKB_WAVES_D64 : SDPA_MASKB_WAVES_D128)
+        : (D == 32 ? SDPA_MASK_WAVES_D32 : D == 64 ? SDPA_MASK_WAVES_D64 : SDPA_MASK_WAVES_D128);
 template <int D, int VAR>
 constexpr int kVariantWavesPerSimd = VAR == kBlockSparse ? kBspWavesPerSimd<D>
                                      : VAR == kDropout   ? kDropWavesPerSimd<D>
-                                     : VAR >= kMaskBool  ? kMaskWavesPerSimd<D>
+                                     : VAR >= kMaskBool  ? kMaskWavesPerSimd<D, VAR>
                                                          : kWavesPerSimd<D>;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,

@@ -60,10 +60,27 @@ template <> struct DropShape<32> : ShapeOf<SDPA_DROP_SHAPE_D32> {};
 template <> struct DropShape<64> : ShapeOf<SDPA_DROP_SHAPE_D64> {};
 template <> struct DropShape<128> : ShapeOf<SDPA_DROP_SHAPE_D128> {};
 
+// Elementwise-mask shapes.
+#ifndef SDPA_MASK_SHAPE_D32
+#define SDPA_MASK_SHAPE_D32 SDPA_SHAPE_D32
+#endif
+#ifndef SDPA_MASK_SHAPE_D64
+#define SDPA_MASK_SHAPE_D64 SDPA_SHAPE_D64
+#endif
+#ifndef SDPA_MASK_SHAPE_D128
+#define SDPA_MASK_SHAPE_D128 SDPA_SHAPE_D128
+#endif
+template <int D> struct MaskShape;
+template <> struct MaskShape<32> : ShapeOf<SDPA_MASK_SHAPE_D32> {};
+template <> struct MaskShape<64> : ShapeOf<SDPA_MASK_SHAPE_D64> {};
+template <> struct MaskShape<128> : ShapeOf<SDPA_MASK_SHAPE_D128> {};
+
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, int VAR = kPlain>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
-  using S = std::conditional_t<VAR == kBlockSparse, BspShape<D>,
-                               std::conditional_t<VAR == kDropout, DropShape<D>, MfmaShape<D>>>;
+  using S = std::conditional_t<
+      VAR == kBlockSparse, BspShape<D>,
+      std::conditional_t<VAR == kDropout, DropShape<D>,
+                         std::conditional_t<(VAR >= kMaskBool), MaskShape<D>, MfmaShape<D>>>>;
   constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   MfmaParams p;

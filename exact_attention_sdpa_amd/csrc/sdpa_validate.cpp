@@ -224,12 +224,13 @@ sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
     if (mask_strides[i] < 0 || mask_strides[i] > lim || mask_strides[i] % 4 != 0)
       return SDPA_ERR_INVALID;
   if (!aligned(mask, (uintptr_t)(4 * eb))) return SDPA_ERR_INVALID;
-  const int64_t nk4 = (a->Nk + 3) / 4 * 4;
+  // rows are read in blocks of 16 elements
+  const int64_t nk16 = (a->Nk + 15) / 16 * 16;
   // a workgroup reads its rows through 32-bit byte offsets
-  if ((256 * mask_strides[2] + nk4) * eb > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
+  if ((256 * mask_strides[2] + nk16) * eb > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
   const __int128 span = ((__int128)(a->B - 1) * mask_strides[0] +
                          (__int128)(a->H - 1) * mask_strides[1] +
-                         (__int128)(a->Nq - 1) * mask_strides[2] + nk4) * eb;
+                         (__int128)(a->Nq - 1) * mask_strides[2] + nk16) * eb;
   if (span > (__int128)(INT64_MAX / 2)) return SDPA_ERR_INVALID;
   const int64_t ob = a->out_f32 ? 4 : elem_bytes(a->dtype);
   const int64_t os = span_bytes(a->B, a->H, a->Nq, a->d, a->o_str, ob);

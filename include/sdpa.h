@@ -160,8 +160,8 @@ typedef enum {
  *
  * mask       device pointer; element (b, h, i, j) lives at
  *            mask + b*ms[0] + h*ms[1] + i*ms[2] + j (elements).  Base aligned
- *            to 4 elements.  Rows are read in groups of 4 elements: elements
- *            j in [Nk, roundup(Nk, 4)) of every row must be readable (their
+ *            to 4 elements.  Rows are read in blocks of 16 elements: elements
+ *            j in [Nk, roundup(Nk, 16)) of every row must be readable (their
  *            values are ignored).  Additive values must be finite or -inf.
  * mask_kind  SDPA_MASK_BOOL, SDPA_MASK_ADD (the input type) or
  *            SDPA_MASK_ADD_F32.
