@@ -14,8 +14,10 @@
 //            rows); the block index is remapped so that each of the eight
 //            XCDs (dispatched round-robin) owns a contiguous range of tiles,
 //            and the tiles of one head run back to back on one XCD, sharing
-//            K/V in that XCD's L2.  Causal tiles of a head run heaviest
-//            first.
+//            K/V in that XCD's L2.  Causal dense grids instead run every
+//            head's heaviest query tile first, then the next heaviest, and
+//            so on (longest-processing-time order), each XCD keeping its own
+//            heads.
 //   waves    NW waves; wave w owns NB blocks of 32 query rows.
 //   tile     BN keys per step, read with buffer loads whose range check
 //            returns zeros past the last key, staged through double-buffered
@@ -130,6 +132,10 @@ enum FwdVariant : int {
 // (measured a few percent faster on MI355X).
 #ifndef SDPA_SETPRIO
 #define SDPA_SETPRIO 1
+#endif
+// Build option: causal dense grids in longest-processing-time order.
+#ifndef SDPA_CAUSAL_LPT
+#define SDPA_CAUSAL_LPT 1
 #endif
 
 // A lane whose tile sum of P exceeds this redoes the tile with a raised
@@ -714,15 +720,34 @@ struct MfmaFwd {
     x.l32 = lane % 32;
     x.c = p.c;
 
-    // ---- which tile: XCD-contiguous ranges, heads' tiles back to back
-    int tile = blockIdx.x;
-    if ((p.total & 7) == 0) {
-      const int per = p.total >> 3;
-      tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
+    int qt, bh;
+    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT) {
+      // causal: every head's heaviest query tiles first, then the next
+      // heaviest of every head, ... (longest-processing-time order, which
+      // shortens the tail when many heads have few tiles); each XCD keeps
+      // its own eighth of the heads when the head count allows
+      const int nbh = p.total / p.n_qtiles;
+      int rank;
+      if ((nbh & 7) == 0) {
+        const int hp = nbh >> 3, j = blockIdx.x >> 3;
+        bh = (blockIdx.x & 7) * hp + j % hp;
+        rank = j / hp;
+      } else {
+        bh = blockIdx.x % nbh;
+        rank = blockIdx.x / nbh;
+      }
+      qt = p.n_qtiles - 1 - rank;
+    } else {
+      int tile = blockIdx.x;
+      if ((p.total & 7) == 0) {
+        const int per = p.total >> 3;
+        tile = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+      }
+      qt = tile % p.n_qtiles;
+      bh = tile / p.n_qtiles;
+      if (CAUSAL) qt = p.n_qtiles - 1 - qt;
     }
-    int qt = tile % p.n_qtiles;
-    const int bh = tile / p.n_qtiles;
-    if (CAUSAL) qt = p.n_qtiles - 1 - qt;
     const int b = bh / p.H, h = bh % p.H;
 
     int nq, nk;
