@@ -117,6 +117,28 @@ __device__ __forceinline__ int bwd_tile_of_block(int total) {
   return t;
 }
 
+// Build option: causal grids in longest-processing-time order.
+#ifndef SDPA_BWD_CAUSAL_LPT
+#define SDPA_BWD_CAUSAL_LPT 1
+#endif
+
+// Causal grids: rank r of head bh, where rank 0 is every head's heaviest
+// tile, rank 1 the next heaviest, ... (longest-processing-time order, which
+// shortens the grid's tail); each XCD keeps its own eighth of the heads
+// when the head count allows.
+__device__ __forceinline__ void bwd_causal_rank_of_block(int total, int n_tiles, int& bh,
+                                                         int& rank) {
+  const int nbh = total / n_tiles;
+  if ((nbh & 7) == 0) {
+    const int hp = nbh >> 3, j = blockIdx.x >> 3;
+    bh = (blockIdx.x & 7) * hp + j % hp;
+    rank = j / hp;
+  } else {
+    bh = blockIdx.x % nbh;
+    rank = blockIdx.x / nbh;
+  }
+}
+
 // Buffer view of `rows` rows of a head starting at row r0; rows past `nrows`
 // read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* head, int r0, int nrows,
@@ -207,8 +229,16 @@ struct BwdDq {
   static __device__ void run(const BwdParams& p, Smem& sm) {
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int l32 = lane % 32, hl = lane / 32;
-    const int tile = bwd_tile_of_block(p.total);
-    const int qt = tile % p.n_tiles, bh = tile / p.n_tiles;
+    int qt, bh;
+    if (CAUSAL && SDPA_BWD_CAUSAL_LPT) {   // the last query tiles see the most keys
+      int rank;
+      bwd_causal_rank_of_block(p.total, p.n_tiles, bh, rank);
+      qt = p.n_tiles - 1 - rank;
+    } else {
+      const int tile = bwd_tile_of_block(p.total);
+      qt = tile % p.n_tiles;
+      bh = tile / p.n_tiles;
+    }
     const int nq = p.Nq, nk = p.Nk;
     const int rs_bytes = D * 2;
     const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
@@ -442,8 +472,14 @@ struct BwdDkdv {
   static __device__ void run(const BwdParams& p, Smem& sm) {
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int l32 = lane % 32, hl = lane / 32;
-    const int tile = bwd_tile_of_block(p.total);
-    const int kt = tile % p.n_tiles, bh = tile / p.n_tiles;
+    int kt, bh;
+    if (CAUSAL && SDPA_BWD_CAUSAL_LPT) {   // the first key tiles are seen by the most queries
+      bwd_causal_rank_of_block(p.total, p.n_tiles, bh, kt);
+    } else {
+      const int tile = bwd_tile_of_block(p.total);
+      kt = tile % p.n_tiles;
+      bh = tile / p.n_tiles;
+    }
     const int nq = p.Nq, nk = p.Nk;
     const int rs_bytes = D * 2;
     const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
