@@ -336,6 +336,44 @@ def _counter_kib(d, kernel_match):
     return sum(vals) / len(vals), len(vals)
 
 
+def summarize_bwd(a) -> int:
+    """Turn the rocprofv3 kernel trace of a backward run (bench.py --pass bwd)
+    into profiles/bwd_<workload>[_dropout].txt: each backward kernel's
+    average duration and share, and the pass's TFLOP/s from their sum."""
+    stats = _csv_rows(a.trace_dir, "kernel_stats.csv")
+    ker = [r for r in stats if "bwd_" in r["Name"] or "fwd_mfma" in r["Name"]]
+    if not ker:
+        raise SystemExit("no attention kernel in the kernel trace")
+    from exact_attention_sdpa_amd import inputs
+    w = inputs.make_config(WORKLOADS[a.workload])
+    short = lambda n: n.split("(")[0].replace("void ", "").replace("sdpa::", "")
+    bwd = [r for r in ker if "bwd_" in r["Name"]]
+    total_us = sum(float(r["AverageNs"]) for r in bwd) / 1e3
+    flops = 2.5 * w.flops()
+    tag = f"bwd_{a.workload}" + ("_dropout" if a.dropout > 0 else "")
+    dflag = f" --dropout {a.dropout:g}" if a.dropout > 0 else ""
+    txt = [f"# {tag}: rocprofv3 summary of the backward pass, workload "
+           f"{describe(w, a.workload, a.dropout)['workload']}", "",
+           f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- python3 bench.py "
+           f"--pass bwd --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
+           f"--cpu-budget 0",
+           "  (the forward runs once first to produce out and lse; it is listed for completeness)",
+           "", f"{'kernel':62s}{'calls':>7s}{'average us':>13s}   share of backward"]
+    for r in sorted(ker, key=lambda r: -float(r["TotalDurationNs"])):
+        us = float(r["AverageNs"]) / 1e3
+        share = f"{100 * us / total_us:9.1f}%" if "bwd_" in r["Name"] else "        -"
+        txt.append(f"  {short(r['Name'])[:60]:60s}{r['Calls']:>7s}{us:13.2f}  {share}")
+    txt += ["", f"backward FLOPs per call (2.5x the forward's {w.flops():.4g}): {flops:.3g}",
+            f"sum of the backward kernels' averages: {total_us:.2f} us -> "
+            f"{flops / total_us / 1e6:.1f} TFLOP/s ({100 * flops / total_us / 1e6 / PEAK_TFLOPS:.1f}% "
+            f"of {PEAK_TFLOPS:.0f})", "",
+            f"kernel sources digest (bwd_*): {kernel_sources_digest('bwd_')}"]
+    with open(os.path.join(ROOT, "profiles", f"{tag}.txt"), "w") as f:
+        f.write("\n".join(txt) + "\n")
+    print("\n".join(txt))
+    return 0
+
+
 def summarize(a) -> int:
     """Turn rocprofv3 outputs of the commands printed below into the text
     summary profiles/<kernel>_<workload>.txt and the HBM-traffic record
@@ -441,7 +479,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-write-dir")
     a = ap.parse_args(argv)
     if a.summarize:
-        return summarize(a)
+        return summarize_bwd(a) if a.which == "bwd" else summarize(a)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the path shards by (batch, head) "
               "with no exchange, so --gpus N > 1 is not measured here.", file=sys.stderr)

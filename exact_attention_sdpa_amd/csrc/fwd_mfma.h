@@ -14,10 +14,10 @@
 //            rows); the block index is remapped so that each of the eight
 //            XCDs (dispatched round-robin) owns a contiguous range of tiles,
 //            and the tiles of one head run back to back on one XCD, sharing
-//            K/V in that XCD's L2.  Causal dense grids instead run every
-//            head's heaviest query tile first, then the next heaviest, and
-//            so on (longest-processing-time order), each XCD keeping its own
-//            heads.
+//            K/V in that XCD's L2.  Causal dense grids of up to 16 query
+//            tiles per head instead run every head's heaviest query tile
+//            first, then the next heaviest, and so on (longest-processing-
+//            time order), each XCD keeping its own heads.
 //   waves    NW waves; wave w owns NB blocks of 32 query rows.
 //   tile     BN keys per step, read with buffer loads whose range check
 //            returns zeros past the last key, staged through double-buffered
@@ -722,11 +722,14 @@ struct MfmaFwd {
 
     // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
     int qt, bh;
-    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT) {
-      // causal: every head's heaviest query tiles first, then the next
-      // heaviest of every head, ... (longest-processing-time order, which
-      // shortens the tail when many heads have few tiles); each XCD keeps
-      // its own eighth of the heads when the head count allows
+    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
+      // causal, short sequences: every head's heaviest query tiles first,
+      // then the next heaviest of every head, ... (longest-processing-time
+      // order, which shortens the tail when many heads have few tiles);
+      // each XCD keeps its own eighth of the heads when the head count
+      // allows.  Long sequences keep a head's tiles back to back: their
+      // order is already near the ideal, and interleaving heads doubles the
+      // K/V re-reads that reach past L2.
       const int nbh = p.total / p.n_qtiles;
       int rank;
       if ((nbh & 7) == 0) {
