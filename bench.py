@@ -286,6 +286,20 @@ def cpu_baseline_bwd(w, budget_s, cfg, dropout=0.0):
     t0 = time.perf_counter()
     units = [(b, h) for b in range(w.B) for h in range(w.H)]
     for (b, h) in units:
+        if w.varlen:   # (sequence, head) units of the packed batch
+            s0, s1 = int(w.cu_seqlens[b]), int(w.cu_seqlens[b + 1])
+            dec = lambda x: inputs.storage_to_f64(x[s0:s1, h], w.dtype)
+            if dropout > 0:
+                oracle.attention_grads_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale,
+                                               w.is_causal, dropout, 2023, 0, b * w.H + h)
+            else:
+                oracle.attention_grads(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale,
+                                       w.is_causal)
+            flops += 2.5 * 4.0 * (s1 - s0) ** 2 * w.d / (2 if w.is_causal else 1)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+            continue
         dec = lambda x: inputs.storage_to_f64(x[b:b + 1, h:h + 1], w.dtype)
         if dropout > 0:
             oracle.sdpa_bwd_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal,
@@ -298,7 +312,8 @@ def cpu_baseline_bwd(w, budget_s, cfg, dropout=0.0):
             break
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "sample": f"{n} of {len(units)} (batch, head) units",
+            "kind": "oracle",
+            "sample": f"{n} of {len(units)} ({'sequence' if w.varlen else 'batch'}, head) units",
             "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -566,15 +581,15 @@ def main(argv=None) -> int:
                 raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
-        if w.varlen or w.block_mask is not None or w.attn_mask is not None:
-            print("bench.py: the backward pass takes dense, unmasked inputs only",
+        if w.block_mask is not None or w.attn_mask is not None:
+            print("bench.py: the backward pass takes unmasked inputs only",
                   file=sys.stderr)
             return 2
         step()   # the forward's out and lse feed the backward
         g = up(inputs.make_grad_out(w, cfg=WORKLOADS[a.workload]))
         gdt = torch.float32 if out_f32 else q.dtype
         dq, dk, dv = (torch.empty(x.shape, dtype=gdt, device="cuda") for x in (q, k, v))
-        work = torch.empty((w.B, H, w.Nq), dtype=torch.float32, device="cuda")
+        work = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
         bargs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), g.data_ptr(),
                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), work.data_ptr(),
                  w.B, H, w.Nq, w.Nk, w.d, float(w.scale), int(w.is_causal), dt, odt,
@@ -587,6 +602,17 @@ def main(argv=None) -> int:
             st = (L.sdpa_bwd_dropout if a.dropout > 0 else L.sdpa_bwd)(*bargs)
             if st != 0:
                 raise sdpa.SdpaError(st)
+
+        if w.varlen:
+            T = int(w.cu_seqlens[-1])
+            pargs = bargs[:10] + [w.B, H, T, w.Nq, w.d, float(w.scale), int(w.is_causal),
+                                  cu.data_ptr(), float(a.dropout), 2023, 0, dt, odt,
+                                  sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME, handle]
+
+            def step():  # noqa: F811 -- the packed-batch backward
+                st = L.sdpa_bwd_packed(*pargs)
+                if st != 0:
+                    raise sdpa.SdpaError(st)
 
     for _ in range(a.warmup):
         step()

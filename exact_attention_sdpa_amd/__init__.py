@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_MASK_ADD, SDPA_MASK_ADD_F32, SDPA_MASK_BOOL, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -149,6 +149,22 @@ def sdpa_bwd_dropout(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, N
         _ptr(dv), _ptr(workspace), int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
         int(is_causal), float(dropout_p), int(seed), int(offset), int(dtype), int(out_dtype),
         int(grad_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_bwd_packed(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, T, max_seqlen, d,
+                    scale, is_causal, cu_seqlens, dropout_p, seed, offset, dtype, out_dtype,
+                    grad_dtype, stream):
+    """Call the packed-batch backward C entry point (same conventions as
+    sdpa_fwd; dropout_p 0 for none)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_bwd_packed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), int(B), int(H), int(T), int(max_seqlen), int(d), float(scale),
+        int(is_causal), _ptr(cu_seqlens), float(dropout_p), int(seed), int(offset), int(dtype),
+        int(out_dtype), int(grad_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -430,15 +446,21 @@ def _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype, r
 def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
                                           is_causal=False, scale=None, grad_dtype=None,
                                           stream=None, dropout_p=0.0, dropout_seed=None,
-                                          dropout_offset=0):
+                                          dropout_offset=0, cu_seqlens=None, max_seqlen=None):
     """Gradients (dq, dk, dv) of sum(grad_out * out) for dense inputs
-    [B,H,N,d], given the forward's out and lse.  ``grad_out`` is cast to the
-    input dtype (the matrix cores consume it); ``grad_dtype`` None keeps the
-    input dtype, torch.float32 requests f32 gradients.  After a dropout
-    forward, pass its ``dropout_p``, ``dropout_seed`` and ``dropout_offset``."""
+    [B,H,N,d], or packed inputs [T,H,d] with ``cu_seqlens`` and
+    ``max_seqlen`` (as the forward), given the forward's out and lse.
+    ``grad_out`` is cast to the input dtype (the matrix cores consume it);
+    ``grad_dtype`` None keeps the input dtype, torch.float32 requests f32
+    gradients.  After a dropout forward, pass its ``dropout_p``,
+    ``dropout_seed`` and ``dropout_offset``."""
     import torch
     if not (query.dtype == key.dtype == value.dtype):
         raise SdpaError(SDPA_ERR_INVALID)
+    if cu_seqlens is not None:
+        return _packed_backward(query, key, value, out, lse, grad_out, is_causal, scale,
+                                grad_dtype, stream, dropout_p, dropout_seed, dropout_offset,
+                                cu_seqlens, max_seqlen)
     q, k, v, o = _contig(query), _contig(key), _contig(value), _contig(out)
     if q.dim() != 4 or k.dim() != 4 or o.shape != q.shape or grad_out.shape != q.shape:
         raise SdpaError(SDPA_ERR_INVALID)
@@ -477,28 +499,67 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
     return dq, dk, dv
 
 
+def _packed_backward(query, key, value, out, lse, grad_out, is_causal, scale, grad_dtype,
+                     stream, dropout_p, dropout_seed, dropout_offset, cu_seqlens, max_seqlen):
+    import torch
+    q, k, v, o = _contig(query), _contig(key), _contig(value), _contig(out)
+    if (q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or o.shape != q.shape
+            or grad_out.shape != q.shape or max_seqlen is None):
+        raise SdpaError(SDPA_ERR_INVALID)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+        raise SdpaError(SDPA_ERR_INVALID)
+    T, H, d = q.shape
+    B = cu_seqlens.numel() - 1
+    if lse is None or lse.shape != (T, H) or lse.dtype != torch.float32:
+        raise SdpaError(SDPA_ERR_INVALID)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    if gdt not in (q.dtype, torch.float32) or o.dtype not in (q.dtype, torch.float32):
+        raise SdpaError(SDPA_ERR_UNSUPPORTED)
+    if dropout_p > 0.0 and dropout_seed is None:
+        raise SdpaError(SDPA_ERR_INVALID)   # the forward's seed is needed
+    do = _contig(grad_out.to(q.dtype))
+    lse = _contig(lse)
+    dq, dk, dv = (torch.zeros(q.shape, dtype=gdt, device=q.device) for _ in range(3))
+    work = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        sdpa_bwd_packed(q, k, v, o, do, lse, dq, dk, dv, work, B, H, T, int(max_seqlen), d,
+                        scale, bool(is_causal), cu_seqlens, float(dropout_p),
+                        int(dropout_seed or 0), int(dropout_offset), _code(q.dtype),
+                        SDPA_F32 if o.dtype != q.dtype else SDPA_SAME,
+                        SDPA_F32 if gdt != q.dtype else SDPA_SAME, stream)
+    return dq, dk, dv
+
+
 def _autograd_function():
     import torch
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, is_causal, scale, dropout_p, seed, offset):
+        def forward(ctx, q, k, v, is_causal, scale, dropout_p, seed, offset, cu, max_seqlen):
             out, lse = scaled_dot_product_attention(q, k, v, is_causal=is_causal, scale=scale,
                                                     dropout_p=dropout_p, dropout_seed=seed,
-                                                    dropout_offset=offset, return_lse=True)
+                                                    dropout_offset=offset, return_lse=True,
+                                                    cu_seqlens=cu, max_seqlen=max_seqlen)
             ctx.save_for_backward(q, k, v, out, lse)
             ctx.is_causal, ctx.scale = is_causal, scale
             ctx.drop = (dropout_p, seed, offset)
+            ctx.packed = (cu, max_seqlen)
             return out
 
         @staticmethod
         def backward(ctx, grad_out):
             q, k, v, out, lse = ctx.saved_tensors
             p, seed, offset = ctx.drop
+            cu, max_seqlen = ctx.packed
             dq, dk, dv = scaled_dot_product_attention_backward(
                 q, k, v, out, lse, grad_out, is_causal=ctx.is_causal, scale=ctx.scale,
-                dropout_p=p, dropout_seed=seed, dropout_offset=offset)
-            return dq, dk, dv, None, None, None, None, None
+                dropout_p=p, dropout_seed=seed, dropout_offset=offset, cu_seqlens=cu,
+                max_seqlen=max_seqlen)
+            return dq, dk, dv, None, None, None, None, None, None, None
 
     return _Attention
 
@@ -507,9 +568,10 @@ _ATTN = None
 
 
 def attention(query, key, value, is_causal=False, scale=None, dropout_p=0.0, dropout_seed=None,
-              dropout_offset=0):
-    """Differentiable dense attention [B,H,N,d]: the forward and backward
-    both run in the HIP kernels.  With ``dropout_p`` > 0 the backward
+              dropout_offset=0, cu_seqlens=None, max_seqlen=None):
+    """Differentiable attention, dense [B,H,N,d] or packed [T,H,d] with
+    ``cu_seqlens`` and ``max_seqlen``: the forward and backward both run in
+    the HIP kernels.  With ``dropout_p`` > 0 the backward
     regenerates the forward's mask from the same seed (drawn from torch's
     CPU generator when None) and offset."""
     global _ATTN
@@ -519,4 +581,5 @@ def attention(query, key, value, is_causal=False, scale=None, dropout_p=0.0, dro
         import torch
         dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
     return _ATTN.apply(query, key, value, bool(is_causal), scale, float(dropout_p), dropout_seed,
-                       int(dropout_offset))
+                       int(dropout_offset), cu_seqlens,
+                       None if max_seqlen is None else int(max_seqlen))

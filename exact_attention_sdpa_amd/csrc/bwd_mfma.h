@@ -40,12 +40,13 @@ struct BwdParams {
   const uint16_t* v;
   const void* out;        // forward output O (input dtype or f32)
   const uint16_t* dout;   // upstream gradient dO (input dtype)
-  const float* lse;       // [B,H,Nq], natural log
-  float* dsum;            // [B,H,Nq] workspace: <dO_i, O_i>
+  const float* lse;       // [B,H,Nq] dense, [T,H] packed; natural log
+  float* dsum;            // workspace of the same layout: <dO_i, O_i>
+  const int32_t* cu;      // packed batches: B+1 sequence offsets
   void* dq;
   void* dk;
   void* dv;
-  int H, Nq, Nk;
+  int H, Nq, Nk;          // packed: Nq = Nk = the longest sequence
   int n_tiles;            // tiles per head of the launched kernel
   int total;              // grid size
   float c;                // scale * log2(e)
@@ -122,6 +123,39 @@ __device__ __forceinline__ int bwd_tile_of_block(int total) {
 #define SDPA_BWD_CAUSAL_LPT 1
 #endif
 
+// The rows of one (batch, head) unit -- or (sequence, head) of a packed
+// batch, whose rows are cu[s]..cu[s+1]-1 of [T, H, d] tensors (row stride
+// H*d): row counts, row stride in elements, element offsets of the first
+// q and k/v rows, and the index of the first row in the lse / workspace
+// layout ([B,H,N] dense, [T,H] packed) with its stride per row.
+struct BwdUnit {
+  int nq, nk, rs, ls;
+  int64_t qoff, kvoff, l0;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ BwdUnit bwd_unit(const BwdParams& p, int bh, int D) {
+  BwdUnit u;
+  if (VARLEN) {
+    const int s = bh / p.H, h = bh % p.H;
+    const int s0 = p.cu[s];
+    u.nq = u.nk = p.cu[s + 1] - s0;
+    u.rs = p.H * D;
+    u.l0 = (int64_t)s0 * p.H + h;
+    u.qoff = u.kvoff = u.l0 * D;
+    u.ls = p.H;
+  } else {
+    u.nq = p.Nq;
+    u.nk = p.Nk;
+    u.rs = D;
+    u.qoff = (int64_t)bh * p.Nq * D;
+    u.kvoff = (int64_t)bh * p.Nk * D;
+    u.l0 = (int64_t)bh * p.Nq;
+    u.ls = 1;
+  }
+  return u;
+}
+
 // Causal grids: rank r of head bh, where rank 0 is every head's heaviest
 // tile, rank 1 the next heaviest, ... (longest-processing-time order, which
 // shortens the grid's tail); each XCD keeps its own eighth of the heads
@@ -195,7 +229,8 @@ __device__ __forceinline__ void store_rows(void* base, int64_t off0, int64_t rs,
 }
 
 // ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
-template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false>
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false,
+          bool VARLEN = false>
 struct BwdDq {
   static constexpr int BM = NW * 32;
   static constexpr int KB = BN / 32;
@@ -239,10 +274,12 @@ struct BwdDq {
       qt = tile % p.n_tiles;
       bh = tile / p.n_tiles;
     }
-    const int nq = p.Nq, nk = p.Nk;
-    const int rs_bytes = D * 2;
-    const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
+    const BwdUnit un = bwd_unit<VARLEN>(p, bh, D);
+    const int nq = un.nq, nk = un.nk;
+    const int rs_bytes = un.rs * 2;
+    const int64_t qoff = un.qoff, kvoff = un.kvoff;
     const int q0 = qt * BM, q0w = q0 + wave * 32;
+    if (VARLEN && q0 >= nq) return;   // whole workgroup: past the sequence end
     const int kend = CAUSAL ? min(nk, q0 + BM) : nk;
     const int ntiles = (kend + BN - 1) / BN;
 
@@ -257,8 +294,9 @@ struct BwdDq {
       gf[ds] = ld16(gr, qi, ds * 16 + hl * 8, rs_bytes);
     }
     const bool qok = qi < nq;
-    const float lse2 = qok ? p.lse[(int64_t)bh * nq + qi] * 1.4426950408889634f : 0.f;
-    const float dd = qok ? p.dsum[(int64_t)bh * nq + qi] : 0.f;
+    const int64_t li = un.l0 + (int64_t)qi * un.ls;
+    const float lse2 = qok ? p.lse[li] * 1.4426950408889634f : 0.f;
+    const float dd = qok ? p.dsum[li] : 0.f;
 
     Stage st;
 #pragma unroll
@@ -387,7 +425,7 @@ struct BwdDq {
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
     }
-    store_rows<BF16, GF32, DB>(p.dq, qoff, D, qi, nq, hl, acc, p.scale);
+    store_rows<BF16, GF32, DB>(p.dq, qoff, un.rs, qi, nq, hl, acc, p.scale);
   }
 };
 
@@ -439,7 +477,8 @@ __device__ __forceinline__ uint32_t keep_bits_of_key(int q0, int key0, int l32, 
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)v);
 }
 
-template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP = false>
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP = false,
+          bool VARLEN = false>
 struct BwdDkdv {
   static constexpr int BK = NW * 32;
   static constexpr int KB = BQ / 32;
@@ -480,10 +519,12 @@ struct BwdDkdv {
       kt = tile % p.n_tiles;
       bh = tile / p.n_tiles;
     }
-    const int nq = p.Nq, nk = p.Nk;
-    const int rs_bytes = D * 2;
-    const int64_t qoff = (int64_t)bh * nq * D, kvoff = (int64_t)bh * nk * D;
+    const BwdUnit un = bwd_unit<VARLEN>(p, bh, D);
+    const int nq = un.nq, nk = un.nk;
+    const int rs_bytes = un.rs * 2;
+    const int64_t qoff = un.qoff, kvoff = un.kvoff;
     const int k0 = kt * BK, k0w = k0 + wave * 32;
+    if (VARLEN && k0 >= nk) return;   // whole workgroup: past the sequence end
     const int ki = k0w + l32;
     const int nqt = (nq + BQ - 1) / BQ;
     // causal: query tiles before the one holding query k0 see none of the
@@ -526,8 +567,9 @@ struct BwdDkdv {
       if (tid < BQ) {
         const int row = r0 + tid;
         const bool ok = row < nq;
-        r.l2 = ok ? -p.lse[(int64_t)bh * nq + row] * 1.4426950408889634f / p.c : -INFINITY;
-        r.dd = ok ? -p.dsum[(int64_t)bh * nq + row] : 0.f;
+        const int64_t li = un.l0 + (int64_t)row * un.ls;
+        r.l2 = ok ? -p.lse[li] * 1.4426950408889634f / p.c : -INFINITY;
+        r.dd = ok ? -p.dsum[li] : 0.f;
       }
     };
     auto store = [&](int buf, const Regs& r) {
@@ -652,8 +694,8 @@ struct BwdDkdv {
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
     }
-    store_rows<BF16, GF32, DB>(p.dk, kvoff, D, ki, nk, hl, dk, p.scale);
-    store_rows<BF16, GF32, DB>(p.dv, kvoff, D, ki, nk, hl, dv, 1.f);
+    store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);
+    store_rows<BF16, GF32, DB>(p.dv, kvoff, un.rs, ki, nk, hl, dv, 1.f);
   }
 };
 
@@ -667,10 +709,10 @@ constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64
 template <int D>
 constexpr int kBwdDqDropWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 
-template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP>
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D>)
 void bwd_dq_kernel(BwdParams p) {
-  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP>;
+  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
@@ -682,10 +724,10 @@ constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 template <int D>
 constexpr int kBwdKvDropWavesPerSimd = D == 32 ? 3 : D == 64 ? 2 : 1;
 
-template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP>
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvWavesPerSimd<D>)
 void bwd_dkdv_kernel(BwdParams p) {
-  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP>;
+  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

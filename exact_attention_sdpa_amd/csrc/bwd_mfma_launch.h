@@ -11,19 +11,19 @@ namespace sdpa {
 constexpr int kBwdDqWaves = 4, kBwdDqKeys = 32;
 constexpr int kBwdKvWaves = 4, kBwdKvRows = 32;
 
-template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP>
+template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
-  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP>;
-  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP>;
+  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN>;
+  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN>;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP>),
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN>),
                      dim3(p.total), dim3(kBwdDqWaves * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN>),
                      dim3(p.total), dim3(kBwdKvWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -44,6 +44,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   p.H = (int)a.H;
   p.Nq = (int)a.Nq;
   p.Nk = (int)a.Nk;
+  p.cu = a.cu;
   // scale 0 is carried as a tiny positive multiplier, as in the forward
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   p.scale = a.scale;
@@ -54,7 +55,8 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   p.drop_scale = a.drop_scale;
   // D_i = <dO_i, O_i> (with dropout O is the dropped output, and D is still
   // sum_j P_ij dP_ij with dP the gradient of the undropped weights)
-  const int64_t rows = a.B * a.H * a.Nq;
+  // rows of O / dO: [B,H,Nq] dense, [T,H] packed (both flat, row stride d)
+  const int64_t rows = a.cu != nullptr ? a.T * a.H : a.B * a.H * a.Nq;
   const dim3 grid((unsigned)((rows + 255) / 256));
   if (a.out_f32)
     hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, true>), grid, dim3(256), 0, a.stream, p, rows);
@@ -62,17 +64,22 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-#define SDPA_BCASE(C, G, X)                                                   \
-  if (a.causal == C && a.grad_f32 == G && a.dropout == X)                     \
-    return launch_bwd_tiles<BF16, D, C, G, X>(a, p);
-  SDPA_BCASE(false, false, false)
-  SDPA_BCASE(false, true, false)
-  SDPA_BCASE(true, false, false)
-  SDPA_BCASE(true, true, false)
-  SDPA_BCASE(false, false, true)
-  SDPA_BCASE(false, true, true)
-  SDPA_BCASE(true, false, true)
-  SDPA_BCASE(true, true, true)
+  const bool varlen = a.cu != nullptr;
+#define SDPA_BCASE(C, G, X, V)                                                \
+  if (a.causal == C && a.grad_f32 == G && a.dropout == X && varlen == V)      \
+    return launch_bwd_tiles<BF16, D, C, G, X, V>(a, p);
+#define SDPA_BCASES(V)        \
+  SDPA_BCASE(false, false, false, V) \
+  SDPA_BCASE(false, true, false, V)  \
+  SDPA_BCASE(true, false, false, V)  \
+  SDPA_BCASE(true, true, false, V)   \
+  SDPA_BCASE(false, false, true, V)  \
+  SDPA_BCASE(false, true, true, V)   \
+  SDPA_BCASE(true, false, true, V)   \
+  SDPA_BCASE(true, true, true, V)
+  SDPA_BCASES(false)
+  SDPA_BCASES(true)
+#undef SDPA_BCASES
 #undef SDPA_BCASE
   return hipErrorInvalidValue;
 }

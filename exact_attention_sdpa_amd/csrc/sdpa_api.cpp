@@ -155,6 +155,26 @@ sdpa_status sdpa_bwd_dropout(const void* q, const void* k, const void* v, const 
   return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+sdpa_status sdpa_bwd_packed(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            float* workspace, int64_t B, int64_t H, int64_t T,
+                            int64_t max_seqlen, int64_t d, float scale, int is_causal,
+                            const int32_t* cu_seqlens, float dropout_p, uint64_t seed,
+                            uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
+                            sdpa_dtype grad_dtype, void* stream) {
+  sdpa::BwdArgs a;
+  const sdpa_status st = sdpa::validate_bwd_packed(
+      q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, T, max_seqlen, d, scale, is_causal,
+      cu_seqlens, dtype, out_dtype, grad_dtype, stream, &a);
+  if (st != SDPA_OK) return st;
+  const sdpa_status sd = sdpa::validate_bwd_dropout(dropout_p, seed, offset, &a);
+  if (sd != SDPA_OK) return sd;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  const hipError_t e =
+      dtype == SDPA_BF16 ? sdpa::launch_bwd_mfma_bf16(a) : sdpa::launch_bwd_mfma_f16(a);
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 int64_t sdpa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   if (B < 0 || H < 0 || Nq < 0) return -1;
   if (B != 0 && H > INT64_MAX / B) return -1;

@@ -49,8 +49,10 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* work;              // B*H*Nq floats
-  int64_t B, H, Nq, Nk, d;
+  float* work;              // B*H*Nq floats (packed: T*H)
+  const int32_t* cu;        // packed batches: B+1 sequence offsets, else null
+  int64_t T;                // packed batches: total rows
+  int64_t B, H, Nq, Nk, d;  // packed: Nq == Nk == the longest sequence
   float scale;
   bool causal;
   bool out_f32;             // O is f32 (else the input type)
@@ -98,6 +100,16 @@ sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArg
 // plain kernel), f16/bf16 inputs; the keep threshold floor((1-p) 65536 + 1/2)
 // and the scale 1/(1-p) are computed here, in double.
 sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a);
+
+// Host-only checks of a packed-batch backward call (q, k, v, out, dout,
+// dq, dk, dv [T,H,d]; lse and workspace [T,H]).  Fills `a` on success.
+sdpa_status validate_bwd_packed(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* workspace, int64_t B, int64_t H, int64_t T,
+                                int64_t max_seqlen, int64_t d, float scale, int is_causal,
+                                const int32_t* cu_seqlens, sdpa_dtype dtype,
+                                sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream,
+                                BwdArgs* a);
 
 sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void* out,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,

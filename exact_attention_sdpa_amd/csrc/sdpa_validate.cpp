@@ -337,6 +337,8 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
   a->dk = dk;
   a->dv = dv;
   a->work = workspace;
+  a->cu = nullptr;
+  a->T = 0;
   a->B = B;
   a->H = H;
   a->Nq = Nq;
@@ -353,6 +355,35 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
   a->drop_offset = 0;
   a->drop_t = 65536;
   a->drop_scale = 1.f;
+  return SDPA_OK;
+}
+
+sdpa_status validate_bwd_packed(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                float* workspace, int64_t B, int64_t H, int64_t T,
+                                int64_t max_seqlen, int64_t d, float scale, int is_causal,
+                                const int32_t* cu_seqlens, sdpa_dtype dtype,
+                                sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream,
+                                BwdArgs* a) {
+  if (cu_seqlens == nullptr || !aligned(cu_seqlens, 4)) return SDPA_ERR_INVALID;
+  if (B < 1 || max_seqlen < 1 || T < 1) return SDPA_ERR_INVALID;
+  const int64_t lim = (int64_t)1 << 30;
+  if (B > lim || max_seqlen > lim || T > lim) return SDPA_ERR_INVALID;
+  // the [T,H,d] tensors as one unit of T rows: null pointers, types,
+  // alignment, sizes and every overlap between outputs and inputs
+  const sdpa_status st =
+      validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, 1, H, T, T, d, scale,
+                   is_causal, dtype, out_dtype, grad_dtype, stream, a);
+  if (st != SDPA_OK) return st;
+  int64_t units;
+  if (!mul_ok(B, H, &units) || units * ((max_seqlen + 31) / 32) > INT32_MAX)
+    return SDPA_ERR_INVALID;
+  // one sequence's rows (row stride H*d) within 32-bit buffer offsets
+  if ((max_seqlen + 256) * H * d * 2 > (int64_t)INT32_MAX) return SDPA_ERR_UNSUPPORTED;
+  a->cu = cu_seqlens;
+  a->T = T;
+  a->B = B;
+  a->Nq = a->Nk = max_seqlen;
   return SDPA_OK;
 }
 

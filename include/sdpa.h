@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 7
+#define SDPA_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -287,6 +287,42 @@ SDPA_API sdpa_status sdpa_bwd_dropout(const void* q, const void* k, const void* 
                                       int is_causal, float dropout_p, uint64_t seed,
                                       uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
                                       sdpa_dtype grad_dtype, void* stream);
+
+/* Backward pass of a packed variable-length batch: the gradients of
+ * sdpa_fwd (or sdpa_fwd_dropout) with cu_seqlens, the chain rule of
+ * sdpa_bwd applied to each (sequence, head) unit.  The tutorial's
+ * NestedTensor batches ("NestedTensor and dense tensor support") run its
+ * module in training as well as in inference.
+ *
+ * q, k, v, out, dout  [T, H, d] as in the packed forward (out in
+ *           out_dtype, dout in dtype); sequence s owns rows
+ *           cu_seqlens[s] .. cu_seqlens[s+1]-1.
+ * lse       the packed forward's [T, H] logsumexp.
+ * dq, dk, dv  outputs [T, H, d] in grad_dtype; every row of a sequence is
+ *           written (rows outside every sequence are not touched).
+ * workspace T*H floats owned by the caller (sdpa_bwd_workspace_bytes(1, H,
+ *           T)); overwritten.
+ * B         number of sequences; cu_seqlens holds B+1 int32 offsets (device
+ *           memory, as in sdpa_fwd: cu_seqlens[0] = 0, non-decreasing,
+ *           cu_seqlens[B] = T, every length <= max_seqlen).
+ * T         total rows (the tensors' first dimension).
+ * max_seqlen  the longest sequence; sizes the grid.
+ * dropout_p, seed, offset  the packed forward's dropout contract (p = 0:
+ *           none); unit u = s*H + h, rows counted from the sequence start.
+ * Other arguments as sdpa_bwd.  Returns SDPA_ERR_INVALID for a null or
+ * misaligned cu_seqlens, B, T or max_seqlen < 1, a bad dropout_p, or the
+ * conditions of sdpa_bwd on [T, H, d] tensors; SDPA_ERR_UNSUPPORTED when a
+ * sequence's rows exceed 32-bit offsets ((max_seqlen + 256) * H * d * 2
+ * bytes beyond 2^31) or as sdpa_bwd.
+ */
+SDPA_API sdpa_status sdpa_bwd_packed(const void* q, const void* k, const void* v,
+                                     const void* out, const void* dout, const float* lse,
+                                     void* dq, void* dk, void* dv, float* workspace, int64_t B,
+                                     int64_t H, int64_t T, int64_t max_seqlen, int64_t d,
+                                     float scale, int is_causal, const int32_t* cu_seqlens,
+                                     float dropout_p, uint64_t seed, uint32_t offset,
+                                     sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                     sdpa_dtype grad_dtype, void* stream);
 
 /* Bytes of the workspace sdpa_bwd needs (B*H*Nq floats), or -1 if the sizes
  * overflow.  Pure host function. */
