@@ -50,12 +50,43 @@ struct BwdParams {
   int n_tiles;            // tiles per head of the launched kernel
   int total;              // grid size
   float c;                // scale * log2(e)
+  float rc;               // 1 / c
   float scale;
   // dropout (the forward's Philox contract): key, last counter word, keep
   // threshold on the 16-bit numbers, 1 / (1 - p)
   uint32_t seed_lo, seed_hi, drop_offset, drop_t;
   float drop_scale;
+  // elementwise mask (dense layouts): element (b, h, i, j) at
+  // amask + (b*am_bs + h*am_hs + i*am_rs + j) elements; bool bytes, or an
+  // additive bias in the input type or f32
+  const void* amask;
+  int64_t am_bs, am_hs;
+  int am_rs;
 };
+
+// Buffer view of one unit's mask (rows 0..nq-1, keys rounded up to 16), and
+// the bias in log2 units of element `e` (0..3) of the 4-element group held
+// in w: bool -> 0 or -inf, additive -> a*log2(e).
+template <int MK>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_unit_rsrc(const BwdParams& p, int b, int h,
+                                                                 int nq, int nk) {
+  constexpr int EB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
+  const char* base = reinterpret_cast<const char*>(p.amask) +
+                     ((int64_t)b * p.am_bs + (int64_t)h * p.am_hs) * EB;
+  const int bytes = (int)(((int64_t)(nq - 1) * p.am_rs + ((nk + 15) & ~15)) * EB);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferWord3);
+}
+
+template <int MK, bool BF16>
+__device__ __forceinline__ float mask_bias2(uint32_t word, int half) {
+  if (MK == kMaskBool) return ((word >> (8 * half)) & 0xffu) != 0u ? 0.f : -INFINITY;
+  if (MK == kMaskAdd) {
+    const uint32_t hb = (word >> (16 * half)) & 0xffffu;
+    const float a = BF16 ? __uint_as_float(hb << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)hb);
+    return a * 1.4426950408889634f;
+  }
+  return __uint_as_float(word) * 1.4426950408889634f;
+}
 
 // 1/(1-p) if the 16-bit number u is below the keep threshold, else 0: the
 // sign of u - T (T <= 65536) selects the bits of the scale.
@@ -230,7 +261,7 @@ __device__ __forceinline__ void store_rows(void* base, int64_t off0, int64_t rs,
 
 // ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false,
-          bool VARLEN = false>
+          bool VARLEN = false, int MK = kPlain>
 struct BwdDq {
   static constexpr int BM = NW * 32;
   static constexpr int KB = BN / 32;
@@ -295,8 +326,19 @@ struct BwdDq {
     }
     const bool qok = qi < nq;
     const int64_t li = un.l0 + (int64_t)qi * un.ls;
-    const float lse2 = qok ? p.lse[li] * 1.4426950408889634f : 0.f;
+    float lse2 = qok ? p.lse[li] * 1.4426950408889634f : 0.f;
+    // masks: a row that saw no key (lse = -inf) has P = 0 everywhere
+    if (MK != kPlain && lse2 == -INFINITY) lse2 = INFINITY;
     const float dd = qok ? p.dsum[li] : 0.f;
+    // masks: the lane's row of the unit's mask; each 4-key group is one
+    // load of 4 elements (keys 8g + 4hl .. +3 of a 32-key block)
+    constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
+    __amdgpu_buffer_rsrc_t mrs;
+    int moff = 0;
+    if (MK != kPlain) {
+      mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
+      moff = (qi * p.am_rs + 4 * hl) * MW;
+    }
 
     Stage st;
 #pragma unroll
@@ -379,6 +421,34 @@ struct BwdDq {
             dp = BF16 ? mfma_bf16(va, gf[ds], dp) : mfma_f16(va, gf[ds], dp);
           }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          // masks: s becomes log2 units relative to the row's lse, in place,
+          // plus the mask's bias (the plain kernel forms that in the exp)
+          if (MK != kPlain) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], p.c, -lse2);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int off = moff + (kb + kk * 32 + 8 * g) * MW;
+              uint32_t mw[4];
+              if (MW == 1) {
+                mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, off, 0, 0);
+              } else if (MW == 2) {
+                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mrs, off, 0, 0));
+                mw[0] = x[0];
+                mw[1] = x[1];
+              } else {
+                const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mw[e] = x[e];
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t word = MW == 1 ? mw[0] : MW == 2 ? mw[e / 2] : mw[e];
+                const int half = MW == 1 ? e : MW == 2 ? (e & 1) : 0;
+                s[4 * g + e] += mask_bias2<MK, BF16>(word, half);
+              }
+            }
+          }
           if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -399,8 +469,10 @@ struct BwdDq {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 8 * hs + 2 * i;
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -lse2));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], p.c, -lse2));
+              const float p0 = __builtin_amdgcn_exp2f(
+                  MK != kPlain ? s[r] : __builtin_fmaf(s[r], p.c, -lse2));
+              const float p1 = __builtin_amdgcn_exp2f(
+                  MK != kPlain ? s[r + 1] : __builtin_fmaf(s[r + 1], p.c, -lse2));
               float d0 = dp[r] - dd, d1 = dp[r + 1] - dd;
               if (DROP) {
                 d0 = __builtin_fmaf(keep_scale(rr[i] & 0xffffu, p.drop_t, p.drop_scale), dp[r], -dd);
@@ -478,7 +550,7 @@ __device__ __forceinline__ uint32_t keep_bits_of_key(int q0, int key0, int l32, 
 }
 
 template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP = false,
-          bool VARLEN = false>
+          bool VARLEN = false, int MK = kPlain>
 struct BwdDkdv {
   static constexpr int BK = NW * 32;
   static constexpr int KB = BQ / 32;
@@ -531,6 +603,10 @@ struct BwdDkdv {
     // workgroup's keys
     const int i0 = CAUSAL ? min(k0 / BQ, nqt) : 0;
 
+    // masks: the unit's mask (read one element per (query, key) below)
+    __amdgpu_buffer_rsrc_t mrs;
+    if (MK != kPlain) mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
+
     // this wave's K and V rows as B operands
     const __amdgpu_buffer_rsrc_t kr = rows_rsrc(p.k + kvoff, 0, nk, rs_bytes, D);
     const __amdgpu_buffer_rsrc_t vr = rows_rsrc(p.v + kvoff, 0, nk, rs_bytes, D);
@@ -568,7 +644,10 @@ struct BwdDkdv {
         const int row = r0 + tid;
         const bool ok = row < nq;
         const int64_t li = un.l0 + (int64_t)row * un.ls;
-        r.l2 = ok ? -p.lse[li] * 1.4426950408889634f / p.c : -INFINITY;
+        // masks: a row that saw no key (lse = -inf) has P = 0 everywhere
+        r.l2 = (ok && (MK == kPlain || p.lse[li] > -INFINITY))
+                   ? -p.lse[li] * 1.4426950408889634f / p.c
+                   : -INFINITY;
         r.dd = ok ? -p.dsum[li] : 0.f;
       }
     };
@@ -644,6 +723,26 @@ struct BwdDkdv {
             dp = BF16 ? mfma_bf16(ga, vf[ds], dp) : mfma_f16(ga, vf[ds], dp);
           }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+          // masks: add the bias in the units of s (the exponent is c s)
+          if (MK != kPlain) {
+            // the lane's key column of the mask for its 16 query rows; the
+            // 32 lanes of a half read 32 consecutive keys of one row
+            constexpr int EB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int query = qb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+              const int off = (query * p.am_rs + ki) * EB;
+              uint32_t word;
+              if (EB == 1) {
+                word = __builtin_amdgcn_raw_buffer_load_b8(mrs, off, 0, 0);
+              } else if (EB == 2) {
+                word = __builtin_amdgcn_raw_buffer_load_b16(mrs, off, 0, 0);
+              } else {
+                word = __builtin_amdgcn_raw_buffer_load_b32(mrs, off, 0, 0);
+              }
+              s[r] += mask_bias2<MK, BF16>(word, 0) * p.rc;
+            }
+          }
           if (masked) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -709,10 +808,11 @@ constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64
 template <int D>
 constexpr int kBwdDqDropWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 
-template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
+template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
+          int MK>
 __global__ __launch_bounds__(NW * 64, DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D>)
 void bwd_dq_kernel(BwdParams p) {
-  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN>;
+  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN, MK>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
@@ -724,10 +824,11 @@ constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 template <int D>
 constexpr int kBwdKvDropWavesPerSimd = D == 32 ? 3 : D == 64 ? 2 : 1;
 
-template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
+template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
+          int MK>
 __global__ __launch_bounds__(NW * 64, DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvWavesPerSimd<D>)
 void bwd_dkdv_kernel(BwdParams p) {
-  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN>;
+  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN, MK>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -11,25 +11,54 @@ namespace sdpa {
 constexpr int kBwdDqWaves = 4, kBwdDqKeys = 32;
 constexpr int kBwdKvWaves = 4, kBwdKvRows = 32;
 
-template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN>
+template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN, int MK = kPlain>
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
-  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN>;
-  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN>;
+  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN, MK>;
+  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN, MK>;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN>),
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys, CAUSAL, GF32, DROP, VARLEN, MK>),
                      dim3(p.total), dim3(kBwdDqWaves * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows, CAUSAL, GF32, DROP, VARLEN, MK>),
                      dim3(p.total), dim3(kBwdKvWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
+// Elementwise-mask backward (dense layouts, no dropout): one instantiation
+// per mask kind, causal flag and gradient type.  Defined in
+// bwd_mfma_mask_*.hip.
 template <bool BF16, int D>
-hipError_t launch_bwd_d(const BwdArgs& a) {
+hipError_t launch_bwd_masked_tiles(const BwdArgs& a, const BwdParams& p);
+template <> hipError_t launch_bwd_masked_tiles<false, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_tiles<false, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_tiles<false, 128>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_tiles<true, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_tiles<true, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_tiles<true, 128>(const BwdArgs&, const BwdParams&);
+
+template <bool BF16, int D>
+hipError_t launch_bwd_masked_tiles_impl(const BwdArgs& a, const BwdParams& p) {
+#define SDPA_MBCASE(KIND, MK)                                                             \
+  if (a.amask_kind == KIND) {                                                            \
+    if (a.causal)                                                                        \
+      return a.grad_f32 ? launch_bwd_tiles<BF16, D, true, true, false, false, MK>(a, p)   \
+                        : launch_bwd_tiles<BF16, D, true, false, false, false, MK>(a, p); \
+    return a.grad_f32 ? launch_bwd_tiles<BF16, D, false, true, false, false, MK>(a, p)    \
+                      : launch_bwd_tiles<BF16, D, false, false, false, false, MK>(a, p);  \
+  }
+  SDPA_MBCASE(SDPA_MASK_BOOL, kMaskBool)
+  SDPA_MBCASE(SDPA_MASK_ADD, kMaskAdd)
+  SDPA_MBCASE(SDPA_MASK_ADD_F32, kMaskAddF32)
+#undef SDPA_MBCASE
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16, int D>
+hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
   BwdParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -47,12 +76,17 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
   p.cu = a.cu;
   // scale 0 is carried as a tiny positive multiplier, as in the forward
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
+  p.rc = 1.f / p.c;
   p.scale = a.scale;
   p.seed_lo = (uint32_t)(a.drop_seed & 0xffffffffu);
   p.seed_hi = (uint32_t)(a.drop_seed >> 32);
   p.drop_offset = a.drop_offset;
   p.drop_t = a.drop_t;
   p.drop_scale = a.drop_scale;
+  p.amask = a.amask;
+  p.am_bs = a.am_str[0];
+  p.am_hs = a.am_str[1];
+  p.am_rs = (int)a.am_str[2];
   // D_i = <dO_i, O_i> (with dropout O is the dropped output, and D is still
   // sum_j P_ij dP_ij with dP the gradient of the undropped weights)
   // rows of O / dO: [B,H,Nq] dense, [T,H] packed (both flat, row stride d)
@@ -64,6 +98,7 @@ hipError_t launch_bwd_d(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (with_mask) return launch_bwd_masked_tiles<BF16, D>(a, p);
   const bool varlen = a.cu != nullptr;
 #define SDPA_BCASE(C, G, X, V)                                                \
   if (a.causal == C && a.grad_f32 == G && a.dropout == X && varlen == V)      \

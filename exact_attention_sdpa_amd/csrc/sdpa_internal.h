@@ -64,6 +64,9 @@ struct BwdArgs {
   uint32_t drop_offset;
   uint32_t drop_t;
   float drop_scale;
+  const void* amask;        // elementwise mask, or null
+  int amask_kind;           // sdpa_mask_kind
+  int64_t am_str[3];        // mask (batch, head, row) strides, elements
 };
 
 // Host-only argument checks (no HIP calls).  Fills `a` on success.
@@ -92,6 +95,12 @@ sdpa_status validate_block_mask(const uint8_t* mask, int64_t mask_heads, FwdArgs
 // clear of out and lse.
 sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
                                const int64_t* mask_strides, FwdArgs* a);
+
+// Adds an elementwise mask to validated dense backward arguments: as
+// validate_attn_mask, with each (batch, head) unit's mask rows within
+// 32-bit offsets, and the mask clear of dq, dk, dv and the workspace.
+sdpa_status validate_bwd_attn_mask(const void* mask, sdpa_mask_kind kind,
+                                   const int64_t* mask_strides, BwdArgs* a);
 
 // Adds dropout to validated backward arguments (same rules as the forward).
 sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a);
@@ -129,5 +138,7 @@ hipError_t launch_fwd_mfma_masked_f16(const FwdArgs& a);
 hipError_t launch_fwd_mfma_masked_bf16(const FwdArgs& a);
 hipError_t launch_bwd_mfma_f16(const BwdArgs& a);
 hipError_t launch_bwd_mfma_bf16(const BwdArgs& a);
+hipError_t launch_bwd_mfma_masked_f16(const BwdArgs& a);
+hipError_t launch_bwd_mfma_masked_bf16(const BwdArgs& a);
 
 }  // namespace sdpa

@@ -243,6 +243,38 @@ sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
   return SDPA_OK;
 }
 
+sdpa_status validate_bwd_attn_mask(const void* mask, sdpa_mask_kind kind,
+                                   const int64_t* mask_strides, BwdArgs* a) {
+  if (mask == nullptr || mask_strides == nullptr) return SDPA_ERR_INVALID;
+  if (kind != SDPA_MASK_BOOL && kind != SDPA_MASK_ADD && kind != SDPA_MASK_ADD_F32)
+    return SDPA_ERR_INVALID;
+  if (a->cu != nullptr) return SDPA_ERR_INVALID;
+  const int64_t eb = kind == SDPA_MASK_BOOL ? 1 : kind == SDPA_MASK_ADD ? 2 : 4;
+  const int64_t lim = (int64_t)1 << 40;
+  for (int i = 0; i < 3; ++i)
+    if (mask_strides[i] < 0 || mask_strides[i] > lim || mask_strides[i] % 4 != 0)
+      return SDPA_ERR_INVALID;
+  if (!aligned(mask, (uintptr_t)(4 * eb))) return SDPA_ERR_INVALID;
+  const int64_t nk16 = (a->Nk + 15) / 16 * 16;
+  // a unit's whole mask is read through 32-bit byte offsets
+  if ((a->Nq + 256) * mask_strides[2] * eb + nk16 * eb > (int64_t)INT32_MAX)
+    return SDPA_ERR_UNSUPPORTED;
+  const __int128 span = ((__int128)(a->B - 1) * mask_strides[0] +
+                         (__int128)(a->H - 1) * mask_strides[1] +
+                         (__int128)(a->Nq - 1) * mask_strides[2] + nk16) * eb;
+  if (span > (__int128)(INT64_MAX / 2)) return SDPA_ERR_INVALID;
+  const int64_t gb = a->grad_f32 ? 4 : 2;
+  const int64_t eq = a->B * a->H * a->Nq * a->d, ek = a->B * a->H * a->Nk * a->d;
+  if (overlap(mask, (int64_t)span, a->dq, eq * gb) || overlap(mask, (int64_t)span, a->dk, ek * gb) ||
+      overlap(mask, (int64_t)span, a->dv, ek * gb) ||
+      overlap(mask, (int64_t)span, a->work, a->B * a->H * a->Nq * 4))
+    return SDPA_ERR_INVALID;
+  a->amask = mask;
+  a->amask_kind = kind;
+  for (int i = 0; i < 3; ++i) a->am_str[i] = mask_strides[i];
+  return SDPA_OK;
+}
+
 sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a) {
   if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;   // NaN fails too
   if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
@@ -339,6 +371,9 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
   a->work = workspace;
   a->cu = nullptr;
   a->T = 0;
+  a->amask = nullptr;
+  a->amask_kind = SDPA_MASK_BOOL;
+  a->am_str[0] = a->am_str[1] = a->am_str[2] = 0;
   a->B = B;
   a->H = H;
   a->Nq = Nq;

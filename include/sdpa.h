@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 8
+#define SDPA_ABI_VERSION 9
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -287,6 +287,28 @@ SDPA_API sdpa_status sdpa_bwd_dropout(const void* q, const void* k, const void* 
                                       int is_causal, float dropout_p, uint64_t seed,
                                       uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
                                       sdpa_dtype grad_dtype, void* stream);
+
+/* Backward pass of sdpa_fwd_masked: the gradients of sum(dout * out) for
+ * attention with an elementwise mask, the chain rule of sdpa_bwd with the
+ * mask's bias a constant (not differentiated):
+ *     P = softmax(scale q k^T + a),  dV = P^T dO,  dP = dO V^T,
+ *     dS = P (dP - rowsum(dO * O)),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Rows the forward found empty (lse = -inf) contribute nothing.
+ *
+ * mask, mask_kind, mask_strides  as sdpa_fwd_masked (the same mask the
+ *           forward used); in addition one (batch, head) unit's mask,
+ *           (Nq + 256) * mask_strides[2] elements plus a row, must fit
+ *           32-bit byte offsets (else SDPA_ERR_UNSUPPORTED).
+ * Other arguments as sdpa_bwd: dense contiguous layouts, f16/bf16.  The
+ * mask must not overlap dq, dk, dv or the workspace.
+ */
+SDPA_API sdpa_status sdpa_bwd_masked(const void* q, const void* k, const void* v,
+                                     const void* out, const void* dout, const float* lse,
+                                     void* dq, void* dk, void* dv, float* workspace, int64_t B,
+                                     int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                     int is_causal, const void* mask, sdpa_mask_kind mask_kind,
+                                     const int64_t* mask_strides, sdpa_dtype dtype,
+                                     sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
 
 /* Backward pass of a packed variable-length batch: the gradients of
  * sdpa_fwd (or sdpa_fwd_dropout) with cu_seqlens, the chain rule of

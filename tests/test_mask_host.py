@@ -66,3 +66,26 @@ def test_masked_calls_rejected_on_host(lib):
     # errors of the dense forward still apply
     assert call(lib, d=48) == UNSUPPORTED
     assert call(lib, N=0) == INVALID
+
+
+def bcall(lib, ms=(4 * 128 * 128, 128 * 128, 128), kind=MBOOL, mask=M, dt=F16, N=128,
+          work=0x9000000, dq=0x7000000):
+    return lib.sdpa_bwd_masked(Q, K, V, O, 0x5000000, L, dq, 0x7800000, 0x8000000, work, 2, 4,
+                               N, N, 64, 0.125, 0, mask, kind, arr(ms), dt, SAME, SAME, None)
+
+
+def test_masked_backward_rejected_on_host(lib):
+    for kind in (MBOOL, MADD, MF32):
+        assert bcall(lib, kind=kind) in (OK, DEVICE)
+    assert bcall(lib, mask=None) == INVALID
+    assert lib.sdpa_bwd_masked(Q, K, V, O, 0x5000000, L, 0x7000000, 0x7800000, 0x8000000,
+                               0x9000000, 2, 4, 128, 128, 64, 0.125, 0, M, MBOOL, None, F16,
+                               SAME, SAME, None) == INVALID
+    assert bcall(lib, kind=9) == INVALID
+    assert bcall(lib, ms=(0, 0, 130)) == INVALID
+    assert bcall(lib, kind=MF32, mask=M + 4) == INVALID
+    assert bcall(lib, dt=F32) == UNSUPPORTED
+    assert bcall(lib, mask=0x9000000) == INVALID      # overlaps the workspace
+    assert bcall(lib, mask=0x7000000) == INVALID      # overlaps dq
+    # a unit's mask beyond 32-bit offsets
+    assert bcall(lib, kind=MF32, ms=(0, 0, 1 << 19), N=1024) == UNSUPPORTED
