@@ -301,7 +301,14 @@ def cpu_baseline_bwd(w, budget_s, cfg, dropout=0.0):
                 break
             continue
         dec = lambda x: inputs.storage_to_f64(x[b:b + 1, h:h + 1], w.dtype)
-        if dropout > 0:
+        if w.attn_mask is not None:   # the masked gradient oracle on the unit's mask
+            m4 = w.attn_mask.reshape((1,) * (4 - w.attn_mask.ndim) + w.attn_mask.shape)
+            mu = m4[b % m4.shape[0], h % m4.shape[1]]
+            mu = mu if w.mask_kind == "bool" else inputs.storage_to_f64(mu, w.dtype)
+            oracle.sdpa_bwd_masked(dec(w.q), dec(w.k), dec(w.v), dec(do),
+                                   np.broadcast_to(mu, (w.Nq, w.Nk))[None, None], w.mask_kind,
+                                   w.scale, w.is_causal)
+        elif dropout > 0:
             oracle.sdpa_bwd_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal,
                                     dropout, 2023, 0)
         else:
@@ -581,8 +588,8 @@ def main(argv=None) -> int:
                 raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
-        if w.block_mask is not None or w.attn_mask is not None:
-            print("bench.py: the backward pass takes unmasked inputs only",
+        if w.block_mask is not None:
+            print("bench.py: the backward pass takes no block-sparse mask",
                   file=sys.stderr)
             return 2
         step()   # the forward's out and lse feed the backward
@@ -602,6 +609,16 @@ def main(argv=None) -> int:
             st = (L.sdpa_bwd_dropout if a.dropout > 0 else L.sdpa_bwd)(*bargs)
             if st != 0:
                 raise sdpa.SdpaError(st)
+
+        if w.attn_mask is not None:   # the elementwise-mask backward, same mask layout
+            margs_b = bargs[:17] + [mt.data_ptr(), mkind, ctypes.cast(mstr_c, ctypes.c_void_p),
+                                    dt, odt, sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME,
+                                    handle]
+
+            def step():  # noqa: F811 -- the masked backward
+                st = L.sdpa_bwd_masked(*margs_b)
+                if st != 0:
+                    raise sdpa.SdpaError(st)
 
         if w.varlen:
             T = int(w.cu_seqlens[-1])
