@@ -378,7 +378,7 @@ def summarize_bwd(a) -> int:
            f"{describe(w, a.workload, a.dropout)['workload']}", "",
            f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- python3 bench.py "
            f"--pass bwd --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
-           f"--cpu-budget 0",
+           f"--cpu-budget 0 --cold-reps 0",
            "  (the forward runs once first to produce out and lse; it is listed for completeness)",
            "", f"{'kernel':62s}{'calls':>7s}{'average us':>13s}   share of backward"]
     for r in sorted(ker, key=lambda r: -float(r["TotalDurationNs"])):
@@ -430,7 +430,7 @@ def summarize(a) -> int:
         "Kernel trace (average over the profiled launches):",
         f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- "
         f"python3 bench.py --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
-        f"--cpu-budget 0",
+        f"--cpu-budget 0 --cold-reps 0",
         f"  kernel:  {k['Name']}",
         f"  calls {k['Calls']}  average {avg_ns / 1e3:.2f} us  min {float(k['MinNs']) / 1e3:.2f} us"
         f"  max {float(k['MaxNs']) / 1e3:.2f} us",
@@ -439,7 +439,7 @@ def summarize(a) -> int:
         "",
         "HBM traffic (separate counter passes, one counter block each):",
         f"  commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
-        f"--workload {a.workload}{dflag} --steps 5 --warmup 1 --cpu-budget 0",
+        f"--workload {a.workload}{dflag} --steps 5 --warmup 1 --cpu-budget 0 --cold-reps 0",
         "            rocprofv3 --pmc WRITE_SIZE (same program)",
         "            rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 bench.py --calibrate-copy",
         f"  copy of 1 GiB reads FETCH_SIZE {cfetch:.0f} KiB, WRITE_SIZE {cwrite:.0f} KiB"
@@ -487,6 +487,9 @@ def main(argv=None) -> int:
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout rate on the attention weights (sdpa_fwd_dropout; dense and "
                          "packed workloads)")
+    ap.add_argument("--cold-reps", type=int, default=None,
+                    help="launches timed with cold caches (a 512 MiB write before each); "
+                         "default 50, 10 for the 64k-token workloads, 0 = skip")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU work for the oracle baseline (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -500,6 +503,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-fetch-dir")
     ap.add_argument("--copy-write-dir")
     a = ap.parse_args(argv)
+    if a.cold_reps is None:
+        a.cold_reps = 10 if a.workload in ("long", "block_sparse") else 50
     if a.summarize:
         return summarize_bwd(a) if a.which == "bwd" else summarize(a)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -661,6 +666,23 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
 
+    # Cold caches: before each of these launches a 512 MiB write evicts L2
+    # and the Infinity Cache (256 MB); the events bracket the attention
+    # launch only.  Untimed by the step clock.
+    kern_cold = []
+    if a.cold_reps > 0:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(a.cold_reps)]
+        for i, (e0, e1) in enumerate(evc):
+            scrub.fill_(i & 0xff)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        kern_cold = [e0.elapsed_time(e1) for e0, e1 in evc]
+        del scrub
+
     # backward: the usual convention of 2.5x the forward's FLOPs (five
     # products of the forward's size: S, dP, dV, dK, dQ)
     flops = w.flops() * (2.5 if a.which == "bwd" else 1.0)
@@ -693,6 +715,13 @@ def main(argv=None) -> int:
         "kernel_ms": {"mean": round(kmean, 4), "median_single": round(float(np.median(kern_ms)), 4),
                       "min_single": round(float(np.min(kern_ms)), 4),
                       "stdev_single": round(float(np.std(kern_ms)), 4)},
+        **({"kernel_ms_cold": {"mean": round(float(np.mean(kern_cold)), 4),
+                               "median": round(float(np.median(kern_cold)), 4),
+                               "min": round(float(np.min(kern_cold)), 4),
+                               "stdev": round(float(np.std(kern_cold)), 4),
+                               "reps": len(kern_cold),
+                               "note": "512 MiB write before each launch"}}
+           if kern_cold else {}),
         "roofline": roof,
     }
     if a.which == "bwd":
