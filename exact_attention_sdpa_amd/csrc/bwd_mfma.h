@@ -563,6 +563,13 @@ struct BwdDkdv {
   static constexpr int PAIRS = (BQ / 2) * NC;   // Q and dO: (2 rows x 16 bytes) tasks
   static constexpr int PPT = (PAIRS + NT - 1) / NT;
   static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NT, "shape");
+  // masks: the step's [BQ queries x BK keys] mask tile is staged through LDS
+  // with the Q and dO rows (16-byte chunks, rows padded by 16 bytes)
+  static constexpr bool HASM = MK != kPlain;
+  static constexpr int MEB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
+  static constexpr int MROWB = BK * MEB + 16;            // LDS row, bytes
+  static constexpr int MCPR = BK * MEB / 16;             // 16-byte chunks per row
+  static constexpr int MPT = HASM ? (BQ * MCPR + NT - 1) / NT : 1;
 
   struct __attribute__((aligned(16))) Buf {
     uint16_t q[BQ * KROW];
@@ -571,12 +578,14 @@ struct BwdDkdv {
     uint32_t gt[D * TW];       // dO^T, likewise
     float nl[BQ];              // -lse * log2(e) / c; -inf past the last row
     float nd[BQ];              // -<dO_i, O_i>; 0 past the last row
+    uint32_t mk[HASM ? BQ * MROWB / 4 : 4];   // mask tile (masked kernels)
   };
   struct __attribute__((aligned(16))) Smem {
     Buf b[2];
   };
   struct Regs {
     u32x4 q0[PPT], q1[PPT], g0[PPT], g1[PPT];
+    u32x4 m[MPT];
     float l2, dd;
   };
 
@@ -603,7 +612,7 @@ struct BwdDkdv {
     // workgroup's keys
     const int i0 = CAUSAL ? min(k0 / BQ, nqt) : 0;
 
-    // masks: the unit's mask (read one element per (query, key) below)
+    // masks: the unit's mask, read a [BQ x BK] tile per step
     __amdgpu_buffer_rsrc_t mrs;
     if (MK != kPlain) mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
 
@@ -640,6 +649,17 @@ struct BwdDkdv {
           r.g0[t] = ld16(gv, pg[t], pc[t], rs_bytes);
           r.g1[t] = ld16(gv, pg[t] + 1, pc[t], rs_bytes);
         }
+      if (HASM) {
+#pragma unroll
+        for (int t = 0; t < MPT; ++t) {
+          const int c = tid + t * NT;
+          if ((BQ * MCPR) % NT == 0 || c < BQ * MCPR) {
+            const int row = c / MCPR, cc = c % MCPR;
+            const int off = (r0 + row) * p.am_rs * MEB + k0 * MEB + cc * 16;
+            r.m[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
+          }
+        }
+      }
       if (tid < BQ) {
         const int row = r0 + tid;
         const bool ok = row < nq;
@@ -666,6 +686,16 @@ struct BwdDkdv {
       if (tid < BQ) {
         b.nl[tid] = r.l2;
         b.nd[tid] = r.dd;
+      }
+      if (HASM) {
+#pragma unroll
+        for (int t = 0; t < MPT; ++t) {
+          const int c = tid + t * NT;
+          if ((BQ * MCPR) % NT == 0 || c < BQ * MCPR) {
+            const int row = c / MCPR, cc = c % MCPR;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(b.mk) + row * MROWB + cc * 16) = r.m[t];
+          }
+        }
       }
     };
 
@@ -725,21 +755,15 @@ struct BwdDkdv {
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
           // masks: add the bias in the units of s (the exponent is c s)
           if (MK != kPlain) {
-            // the lane's key column of the mask for its 16 query rows; the
-            // 32 lanes of a half read 32 consecutive keys of one row
-            constexpr int EB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
+            // the lane's key column of the staged mask tile, its 16 rows
+            const char* mcol = reinterpret_cast<const char*>(b.mk) + (wave * 32 + l32) * MEB;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int query = qb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-              const int off = (query * p.am_rs + ki) * EB;
-              uint32_t word;
-              if (EB == 1) {
-                word = __builtin_amdgcn_raw_buffer_load_b8(mrs, off, 0, 0);
-              } else if (EB == 2) {
-                word = __builtin_amdgcn_raw_buffer_load_b16(mrs, off, 0, 0);
-              } else {
-                word = __builtin_amdgcn_raw_buffer_load_b32(mrs, off, 0, 0);
-              }
+              const int row = kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
+              const char* e = mcol + row * MROWB;
+              const uint32_t word = MEB == 1   ? (uint32_t)*reinterpret_cast<const uint8_t*>(e)
+                                    : MEB == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(e)
+                                               : *reinterpret_cast<const uint32_t*>(e);
               s[r] += mask_bias2<MK, BF16>(word, 0) * p.rc;
             }
           }

@@ -256,8 +256,9 @@ sdpa_status validate_bwd_attn_mask(const void* mask, sdpa_mask_kind kind,
       return SDPA_ERR_INVALID;
   if (!aligned(mask, (uintptr_t)(4 * eb))) return SDPA_ERR_INVALID;
   const int64_t nk16 = (a->Nk + 15) / 16 * 16;
-  // a unit's whole mask is read through 32-bit byte offsets
-  if ((a->Nq + 256) * mask_strides[2] * eb + nk16 * eb > (int64_t)INT32_MAX)
+  // a unit's whole mask (plus a tile of slack) is read through 32-bit byte
+  // offsets
+  if ((a->Nq + 256) * mask_strides[2] * eb + (nk16 + 256) * eb > (int64_t)INT32_MAX)
     return SDPA_ERR_UNSUPPORTED;
   const __int128 span = ((__int128)(a->B - 1) * mask_strides[0] +
                          (__int128)(a->H - 1) * mask_strides[1] +
