@@ -77,6 +77,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mask_unit_rsrc(const BwdParams
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufferWord3);
 }
 
+// The 4-key groups g (keys 8g + 4hl .. +3 of a 32-key block) of one mask
+// row, as the forward reads them: bool and 16-bit masks as two contiguous
+// half blocks per lane pair (keys 16hl .. 16hl+15 at byte offset `off`),
+// exchanged through v_permlane32_swap; f32 masks one 16-byte load per group
+// (`off` at key 4hl).  w[g] holds group g's elements (1, 2 or 4 words).
+template <int MK>
+__device__ __forceinline__ void load_mask_groups(__amdgpu_buffer_rsrc_t r, int off,
+                                                 uint32_t (&w)[4][MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4]) {
+  if constexpr (MK == kMaskBool) {
+    const u32x4 d = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const auto s01 = __builtin_amdgcn_permlane32_swap(d[0], d[1], false, false);
+    const auto s23 = __builtin_amdgcn_permlane32_swap(d[2], d[3], false, false);
+    w[0][0] = s01[0];
+    w[2][0] = s01[1];
+    w[1][0] = s23[0];
+    w[3][0] = s23[1];
+  } else if constexpr (MK == kMaskAdd) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    const auto a0 = __builtin_amdgcn_permlane32_swap(a[0], a[2], false, false);
+    const auto a1 = __builtin_amdgcn_permlane32_swap(a[1], a[3], false, false);
+    const auto b0 = __builtin_amdgcn_permlane32_swap(b[0], b[2], false, false);
+    const auto b1 = __builtin_amdgcn_permlane32_swap(b[1], b[3], false, false);
+    w[0][0] = a0[0];
+    w[0][1] = a1[0];
+    w[2][0] = a0[1];
+    w[2][1] = a1[1];
+    w[1][0] = b0[0];
+    w[1][1] = b1[0];
+    w[3][0] = b0[1];
+    w[3][1] = b1[1];
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 32 * g, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[g][e] = v[e];
+    }
+  }
+}
+
 template <int MK, bool BF16>
 __device__ __forceinline__ float mask_bias2(uint32_t word, int half) {
   if (MK == kMaskBool) return ((word >> (8 * half)) & 0xffu) != 0u ? 0.f : -INFINITY;
@@ -330,14 +371,14 @@ struct BwdDq {
     // masks: a row that saw no key (lse = -inf) has P = 0 everywhere
     if (MK != kPlain && lse2 == -INFINITY) lse2 = INFINITY;
     const float dd = qok ? p.dsum[li] : 0.f;
-    // masks: the lane's row of the unit's mask; each 4-key group is one
-    // load of 4 elements (keys 8g + 4hl .. +3 of a 32-key block)
+    // masks: the lane's row of the unit's mask, read per 32-key block as
+    // the forward reads it (load_mask_groups)
     constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
     __amdgpu_buffer_rsrc_t mrs;
     int moff = 0;
     if (MK != kPlain) {
       mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
-      moff = (qi * p.am_rs + 4 * hl) * MW;
+      moff = (qi * p.am_rs + (MW == 4 ? 4 : 16) * hl) * MW;
     }
 
     Stage st;
@@ -426,21 +467,11 @@ struct BwdDq {
           if (MK != kPlain) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], p.c, -lse2);
+            uint32_t gw[4][MW];
+            load_mask_groups<MK>(mrs, moff + (kb + kk * 32) * MW, gw);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int off = moff + (kb + kk * 32 + 8 * g) * MW;
-              uint32_t mw[4];
-              if (MW == 1) {
-                mw[0] = __builtin_amdgcn_raw_buffer_load_b32(mrs, off, 0, 0);
-              } else if (MW == 2) {
-                const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(mrs, off, 0, 0));
-                mw[0] = x[0];
-                mw[1] = x[1];
-              } else {
-                const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mw[e] = x[e];
-              }
+              const uint32_t* mw = gw[g];
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const uint32_t word = MW == 1 ? mw[0] : MW == 2 ? mw[e / 2] : mw[e];
