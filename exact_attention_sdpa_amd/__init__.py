@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_MASK_ADD, SDPA_MASK_ADD_F32, SDPA_MASK_BOOL, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -183,6 +183,21 @@ def sdpa_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk
         _ptr(dv), _ptr(workspace), int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
         int(is_causal), _ptr(mask), int(mask_kind), ctypes.cast(ms, ctypes.c_void_p), int(dtype),
         int(out_dtype), int(grad_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_bwd_block_sparse(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d,
+                          scale, is_causal, block_mask, mask_heads, dtype, out_dtype,
+                          grad_dtype, stream):
+    """Call the block-sparse backward C entry point."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_bwd_block_sparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
+        int(is_causal), _ptr(block_mask), int(mask_heads), int(dtype), int(out_dtype),
+        int(grad_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -465,19 +480,22 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
                                           is_causal=False, scale=None, grad_dtype=None,
                                           stream=None, dropout_p=0.0, dropout_seed=None,
                                           dropout_offset=0, cu_seqlens=None, max_seqlen=None,
-                                          attn_mask=None):
+                                          attn_mask=None, block_mask=None):
     """Gradients (dq, dk, dv) of sum(grad_out * out) for dense inputs
     [B,H,N,d], or packed inputs [T,H,d] with ``cu_seqlens`` and
     ``max_seqlen`` (as the forward), given the forward's out and lse.
     ``grad_out`` is cast to the input dtype (the matrix cores consume it);
     ``grad_dtype`` None keeps the input dtype, torch.float32 requests f32
     gradients.  After a dropout forward, pass its ``dropout_p``,
-    ``dropout_seed`` and ``dropout_offset``; after a masked forward, the same
-    ``attn_mask`` (dense inputs, no dropout)."""
+    ``dropout_seed`` and ``dropout_offset``; after a masked or block-sparse
+    forward, the same ``attn_mask`` or ``block_mask`` (dense inputs, no
+    dropout)."""
     import torch
     if not (query.dtype == key.dtype == value.dtype):
         raise SdpaError(SDPA_ERR_INVALID)
-    if attn_mask is not None and (cu_seqlens is not None or dropout_p > 0.0):
+    if (attn_mask is not None or block_mask is not None) and (
+            cu_seqlens is not None or dropout_p > 0.0
+            or (attn_mask is not None and block_mask is not None)):
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
     if cu_seqlens is not None:
         return _packed_backward(query, key, value, out, lse, grad_out, is_causal, scale,
@@ -509,6 +527,17 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
     odc = SDPA_F32 if o.dtype != q.dtype else SDPA_SAME
     gdc = SDPA_F32 if gdt != q.dtype else SDPA_SAME
     with torch.cuda.device(q.device):
+        if block_mask is not None:
+            bm = block_mask[None] if block_mask.dim() == 2 else block_mask
+            blk = SDPA_BLOCK_SPARSE_BLOCK
+            if (bm.dim() != 3 or bm.dtype != torch.uint8 or not bm.is_cuda
+                    or bm.shape[0] not in (1, H)
+                    or tuple(bm.shape[1:]) != (-(-Nq // blk), -(-Nk // blk))):
+                raise SdpaError(SDPA_ERR_INVALID)
+            bm = bm.contiguous()
+            sdpa_bwd_block_sparse(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
+                                  bool(is_causal), bm, bm.shape[0], dt, odc, gdc, stream)
+            return dq, dk, dv
         if attn_mask is not None:
             m4, kind, mst = _mask_operand(attn_mask, q, B, H, Nq, Nk)
             sdpa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
@@ -567,13 +596,13 @@ def _autograd_function():
     class _Attention(torch.autograd.Function):
         @staticmethod
         def forward(ctx, q, k, v, is_causal, scale, dropout_p, seed, offset, cu, max_seqlen,
-                    attn_mask):
+                    attn_mask, block_mask):
             out, lse = scaled_dot_product_attention(q, k, v, is_causal=is_causal, scale=scale,
                                                     dropout_p=dropout_p, dropout_seed=seed,
                                                     dropout_offset=offset, return_lse=True,
                                                     cu_seqlens=cu, max_seqlen=max_seqlen,
-                                                    attn_mask=attn_mask)
-            ctx.attn_mask = attn_mask
+                                                    attn_mask=attn_mask, block_mask=block_mask)
+            ctx.attn_mask, ctx.block_mask = attn_mask, block_mask
             ctx.save_for_backward(q, k, v, out, lse)
             ctx.is_causal, ctx.scale = is_causal, scale
             ctx.drop = (dropout_p, seed, offset)
@@ -588,8 +617,8 @@ def _autograd_function():
             dq, dk, dv = scaled_dot_product_attention_backward(
                 q, k, v, out, lse, grad_out, is_causal=ctx.is_causal, scale=ctx.scale,
                 dropout_p=p, dropout_seed=seed, dropout_offset=offset, cu_seqlens=cu,
-                max_seqlen=max_seqlen, attn_mask=ctx.attn_mask)
-            return dq, dk, dv, None, None, None, None, None, None, None, None
+                max_seqlen=max_seqlen, attn_mask=ctx.attn_mask, block_mask=ctx.block_mask)
+            return dq, dk, dv, None, None, None, None, None, None, None, None, None
 
     return _Attention
 
@@ -598,11 +627,12 @@ _ATTN = None
 
 
 def attention(query, key, value, is_causal=False, scale=None, dropout_p=0.0, dropout_seed=None,
-              dropout_offset=0, cu_seqlens=None, max_seqlen=None, attn_mask=None):
+              dropout_offset=0, cu_seqlens=None, max_seqlen=None, attn_mask=None,
+              block_mask=None):
     """Differentiable attention, dense [B,H,N,d] or packed [T,H,d] with
     ``cu_seqlens`` and ``max_seqlen``, optionally with an elementwise
-    ``attn_mask`` (dense; the mask is not differentiated): the forward and
-    backward both run in the HIP kernels.  With ``dropout_p`` > 0 the backward
+    ``attn_mask`` or a ``block_mask`` (dense; masks are not differentiated):
+    the forward and backward both run in the HIP kernels.  With ``dropout_p`` > 0 the backward
     regenerates the forward's mask from the same seed (drawn from torch's
     CPU generator when None) and offset."""
     global _ATTN
@@ -613,4 +643,4 @@ def attention(query, key, value, is_causal=False, scale=None, dropout_p=0.0, dro
         dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
     return _ATTN.apply(query, key, value, bool(is_causal), scale, float(dropout_p), dropout_seed,
                        int(dropout_offset), cu_seqlens,
-                       None if max_seqlen is None else int(max_seqlen), attn_mask)
+                       None if max_seqlen is None else int(max_seqlen), attn_mask, block_mask)

@@ -15,7 +15,7 @@ SDPA_MASK_BOOL, SDPA_MASK_ADD, SDPA_MASK_ADD_F32 = 0, 1, 2
 
 # every symbol include/sdpa.h declares
 EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
-           "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
+           "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
 
@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.sdpa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                   i64, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_bwd_block_sparse.restype = ctypes.c_int
+    L.sdpa_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                        i64, i64, ctypes.c_float, ctypes.c_int, vp, i64,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.sdpa_bwd_workspace_bytes.restype = i64
     L.sdpa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     L.sdpa_supports.restype = ctypes.c_int

@@ -62,7 +62,39 @@ struct BwdParams {
   const void* amask;
   int64_t am_bs, am_hs;
   int am_rs;
+  // block-sparse mask (dense layouts): uint8 [Hm][nqb][nkb] over 128x128
+  // blocks, nonzero = the block's pairs are visible
+  const uint8_t* bmask;
+  int bm_hstride, bm_nqb, bm_nkb;
 };
+
+// Block-sparse scan: the first tile index >= t whose 128x128 mask block is
+// kept, tiles of 128/tpb rows or keys, mask entries base[b * stride] for
+// blocks b < n.  A wave reads 64 entries per ballot into a wave-uniform bit
+// set, so a scan waits on memory once per 64 blocks.  Every wave of a
+// workgroup computes the same sequence.
+struct BlockScan {
+  const uint8_t* base;
+  int stride, n, chunk;
+  uint64_t bits;
+};
+
+__device__ __forceinline__ int block_scan_next(BlockScan& sc, int t, int tpb, int ntiles,
+                                               int lane) {
+  while (t < ntiles) {
+    const int blk = t / tpb;
+    const int chunk = blk >> 6;
+    if (chunk != sc.chunk) {
+      const int c = chunk * 64 + lane;
+      sc.bits = __builtin_amdgcn_ballot_w64(c < sc.n && sc.base[(int64_t)c * sc.stride] != 0);
+      sc.chunk = chunk;
+    }
+    const uint64_t rest = sc.bits >> (blk & 63);
+    if (rest != 0) return max(t, (blk + (int)__builtin_ctzll(rest)) * tpb);
+    t = (chunk + 1) * 64 * tpb;
+  }
+  return t;
+}
 
 // Buffer view of one unit's mask (rows 0..nq-1, keys rounded up to 16), and
 // the bias in log2 units of element `e` (0..3) of the 4-element group held
@@ -368,7 +400,7 @@ struct BwdDq {
     const bool qok = qi < nq;
     const int64_t li = un.l0 + (int64_t)qi * un.ls;
     float lse2 = qok ? p.lse[li] * 1.4426950408889634f : 0.f;
-    // masks: a row that saw no key (lse = -inf) has P = 0 everywhere
+    // masks, block-sparse: a row that saw no key (lse = -inf) has P = 0
     if (MK != kPlain && lse2 == -INFINITY) lse2 = INFINITY;
     const float dd = qok ? p.dsum[li] : 0.f;
     // masks: the lane's row of the unit's mask, read per 32-key block as
@@ -376,7 +408,7 @@ struct BwdDq {
     constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
     __amdgpu_buffer_rsrc_t mrs;
     int moff = 0;
-    if (MK != kPlain) {
+    if (MK >= kMaskBool) {
       mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
       moff = (qi * p.am_rs + (MW == 4 ? 4 : 16) * hl) * MW;
     }
@@ -432,19 +464,37 @@ struct BwdDq {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    {
+    // block-sparse: only the key tiles the workgroup's mask row keeps (the
+    // workgroup's BM = 128 rows are one mask row)
+    constexpr bool BSP = MK == kBlockSparse;
+    static_assert(!BSP || (BM == kSparseBlock && kSparseBlock % BN == 0 && !VARLEN && !DROP),
+                  "block-sparse dQ shape");
+    BlockScan bsc;
+    if (BSP) {
+      bsc.base = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + (int64_t)qt * p.bm_nkb;
+      bsc.stride = 1;
+      bsc.n = p.bm_nkb;
+      bsc.chunk = -1;
+      bsc.bits = 0;
+    }
+    auto next_tile = [&](int t) {
+      return BSP ? block_scan_next(bsc, t, kSparseBlock / BN, ntiles, lane) : t;
+    };
+    int j = next_tile(0);
+    if (j < ntiles) {
       Regs r0;
-      load(r0, 0);
+      load(r0, j);
       store(0, r0);
     }
     __syncthreads();
 
     const int kl = l32 * KROW + hl * 8;
-    for (int j = 0; j < ntiles; ++j) {
-      const int buf = j & 1;
+    for (int step = 0; j < ntiles; ++step) {
+      const int buf = step & 1;
       Regs rn;
-      const bool nxt = j + 1 < ntiles;
-      if (nxt) load(rn, j + 1);
+      const int jn = next_tile(j + 1);
+      const bool nxt = jn < ntiles;
+      if (nxt) load(rn, jn);
       const int kb = j * BN;
       const bool live = !(CAUSAL && kb > q0w + 31);
       if (live) {
@@ -464,7 +514,7 @@ struct BwdDq {
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
           // masks: s becomes log2 units relative to the row's lse, in place,
           // plus the mask's bias (the plain kernel forms that in the exp)
-          if (MK != kPlain) {
+          if (MK >= kMaskBool) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], p.c, -lse2);
             uint32_t gw[4][MW];
@@ -501,9 +551,9 @@ struct BwdDq {
             for (int i = 0; i < 4; ++i) {
               const int r = 8 * hs + 2 * i;
               const float p0 = __builtin_amdgcn_exp2f(
-                  MK != kPlain ? s[r] : __builtin_fmaf(s[r], p.c, -lse2));
+                  MK >= kMaskBool ? s[r] : __builtin_fmaf(s[r], p.c, -lse2));
               const float p1 = __builtin_amdgcn_exp2f(
-                  MK != kPlain ? s[r + 1] : __builtin_fmaf(s[r + 1], p.c, -lse2));
+                  MK >= kMaskBool ? s[r + 1] : __builtin_fmaf(s[r + 1], p.c, -lse2));
               float d0 = dp[r] - dd, d1 = dp[r + 1] - dd;
               if (DROP) {
                 d0 = __builtin_fmaf(keep_scale(rr[i] & 0xffffu, p.drop_t, p.drop_scale), dp[r], -dd);
@@ -527,6 +577,7 @@ struct BwdDq {
       }
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
+      j = jn;
     }
     store_rows<BF16, GF32, DB>(p.dq, qoff, un.rs, qi, nq, hl, acc, p.scale);
   }
@@ -596,7 +647,7 @@ struct BwdDkdv {
   static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NT, "shape");
   // masks: the step's [BQ queries x BK keys] mask tile is staged through LDS
   // with the Q and dO rows (16-byte chunks, rows padded by 16 bytes)
-  static constexpr bool HASM = MK != kPlain;
+  static constexpr bool HASM = MK >= kMaskBool;
   static constexpr int MEB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
   static constexpr int MROWB = BK * MEB + 16;            // LDS row, bytes
   static constexpr int MCPR = BK * MEB / 16;             // 16-byte chunks per row
@@ -645,7 +696,7 @@ struct BwdDkdv {
 
     // masks: the unit's mask, read a [BQ x BK] tile per step
     __amdgpu_buffer_rsrc_t mrs;
-    if (MK != kPlain) mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
+    if (MK >= kMaskBool) mrs = mask_unit_rsrc<MK>(p, bh / p.H, bh % p.H, nq, nk);
 
     // this wave's K and V rows as B operands
     const __amdgpu_buffer_rsrc_t kr = rows_rsrc(p.k + kvoff, 0, nk, rs_bytes, D);
@@ -736,19 +787,37 @@ struct BwdDkdv {
 #pragma unroll
       for (int r = 0; r < 16; ++r) dk[db][r] = dv[db][r] = 0.f;
 
-    if (i0 < nqt) {
+    // block-sparse: only the query tiles whose mask block keeps the
+    // workgroup's keys (its BK = 128 keys are one mask column)
+    constexpr bool BSP = MK == kBlockSparse;
+    static_assert(!BSP || (BK == kSparseBlock && kSparseBlock % BQ == 0 && !VARLEN && !DROP),
+                  "block-sparse dK/dV shape");
+    BlockScan bsc;
+    if (BSP) {
+      bsc.base = p.bmask + (int64_t)(bh % p.H) * p.bm_hstride + kt;
+      bsc.stride = p.bm_nkb;
+      bsc.n = p.bm_nqb;
+      bsc.chunk = -1;
+      bsc.bits = 0;
+    }
+    auto next_tile = [&](int t) {
+      return BSP ? block_scan_next(bsc, t, kSparseBlock / BQ, nqt, lane) : t;
+    };
+    int i = next_tile(i0);
+    if (i < nqt) {
       Regs r0;
-      load(r0, i0);
+      load(r0, i);
       store(0, r0);
     }
     __syncthreads();
 
     const int ql = l32 * KROW + hl * 8;
-    for (int i = i0; i < nqt; ++i) {
-      const int buf = (i - i0) & 1;
+    for (int step = 0; i < nqt; ++step) {
+      const int buf = step & 1;
       Regs rn;
-      const bool nxt = i + 1 < nqt;
-      if (nxt) load(rn, i + 1);
+      const int in_ = next_tile(i + 1);
+      const bool nxt = in_ < nqt;
+      if (nxt) load(rn, in_);
       const int qb = i * BQ;
       const bool live = !(CAUSAL && qb + BQ - 1 < k0w);
       if (live) {
@@ -785,7 +854,7 @@ struct BwdDkdv {
           }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
           // masks: add the bias in the units of s (the exponent is c s)
-          if (MK != kPlain) {
+          if (MK >= kMaskBool) {
             // the lane's key column of the staged mask tile, its 16 rows
             const char* mcol = reinterpret_cast<const char*>(b.mk) + (wave * 32 + l32) * MEB;
 #pragma unroll
@@ -847,6 +916,7 @@ struct BwdDkdv {
       }
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
+      i = in_;
     }
     store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);
     store_rows<BF16, GF32, DB>(p.dv, kvoff, un.rs, ki, nk, hl, dv, 1.f);

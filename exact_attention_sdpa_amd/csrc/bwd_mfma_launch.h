@@ -40,6 +40,26 @@ template <> hipError_t launch_bwd_masked_tiles<true, 32>(const BwdArgs&, const B
 template <> hipError_t launch_bwd_masked_tiles<true, 64>(const BwdArgs&, const BwdParams&);
 template <> hipError_t launch_bwd_masked_tiles<true, 128>(const BwdArgs&, const BwdParams&);
 
+// Block-sparse backward (dense layouts, no dropout).  Defined in
+// bwd_mfma_mask_*.hip.
+template <bool BF16, int D>
+hipError_t launch_bwd_bsp_tiles(const BwdArgs& a, const BwdParams& p);
+template <> hipError_t launch_bwd_bsp_tiles<false, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_bsp_tiles<false, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_bsp_tiles<false, 128>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_bsp_tiles<true, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_bsp_tiles<true, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_bsp_tiles<true, 128>(const BwdArgs&, const BwdParams&);
+
+template <bool BF16, int D>
+hipError_t launch_bwd_bsp_tiles_impl(const BwdArgs& a, const BwdParams& p) {
+  if (a.causal)
+    return a.grad_f32 ? launch_bwd_tiles<BF16, D, true, true, false, false, kBlockSparse>(a, p)
+                      : launch_bwd_tiles<BF16, D, true, false, false, false, kBlockSparse>(a, p);
+  return a.grad_f32 ? launch_bwd_tiles<BF16, D, false, true, false, false, kBlockSparse>(a, p)
+                    : launch_bwd_tiles<BF16, D, false, false, false, false, kBlockSparse>(a, p);
+}
+
 template <bool BF16, int D>
 hipError_t launch_bwd_masked_tiles_impl(const BwdArgs& a, const BwdParams& p) {
 #define SDPA_MBCASE(KIND, MK)                                                             \
@@ -83,6 +103,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
   p.drop_offset = a.drop_offset;
   p.drop_t = a.drop_t;
   p.drop_scale = a.drop_scale;
+  p.bmask = a.bmask;
+  p.bm_nqb = (int)((a.Nq + kSparseBlock - 1) / kSparseBlock);
+  p.bm_nkb = (int)((a.Nk + kSparseBlock - 1) / kSparseBlock);
+  p.bm_hstride = a.mask_heads > 1 ? p.bm_nqb * p.bm_nkb : 0;
   p.amask = a.amask;
   p.am_bs = a.am_str[0];
   p.am_hs = a.am_str[1];
@@ -98,7 +122,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
     hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (with_mask) return launch_bwd_masked_tiles<BF16, D>(a, p);
+  if (with_mask)
+    return a.bmask != nullptr ? launch_bwd_bsp_tiles<BF16, D>(a, p)
+                              : launch_bwd_masked_tiles<BF16, D>(a, p);
   const bool varlen = a.cu != nullptr;
 #define SDPA_BCASE(C, G, X, V)                                                \
   if (a.causal == C && a.grad_f32 == G && a.dropout == X && varlen == V)      \

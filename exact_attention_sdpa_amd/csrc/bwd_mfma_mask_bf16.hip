@@ -1,4 +1,5 @@
-// Instantiations of the matrix-core backward with an elementwise mask:
+// Instantiations of the matrix-core backward with an elementwise or a
+// block-sparse mask:
 // bf16 inputs, every head dim.
 #include "bwd_mfma_launch.h"
 
@@ -14,5 +15,17 @@ hipError_t launch_bwd_masked_tiles<true, 64>(const BwdArgs& a, const BwdParams& 
 template <>
 hipError_t launch_bwd_masked_tiles<true, 128>(const BwdArgs& a, const BwdParams& p) {
   return launch_bwd_masked_tiles_impl<true, 128>(a, p);
+}
+template <>
+hipError_t launch_bwd_bsp_tiles<true, 32>(const BwdArgs& a, const BwdParams& p) {
+  return launch_bwd_bsp_tiles_impl<true, 32>(a, p);
+}
+template <>
+hipError_t launch_bwd_bsp_tiles<true, 64>(const BwdArgs& a, const BwdParams& p) {
+  return launch_bwd_bsp_tiles_impl<true, 64>(a, p);
+}
+template <>
+hipError_t launch_bwd_bsp_tiles<true, 128>(const BwdArgs& a, const BwdParams& p) {
+  return launch_bwd_bsp_tiles_impl<true, 128>(a, p);
 }
 }  // namespace sdpa

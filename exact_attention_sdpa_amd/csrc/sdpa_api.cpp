@@ -175,6 +175,25 @@ sdpa_status sdpa_bwd_masked(const void* q, const void* k, const void* v, const v
   return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+sdpa_status sdpa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, float* workspace, int64_t B, int64_t H, int64_t Nq,
+                                  int64_t Nk, int64_t d, float scale, int is_causal,
+                                  const uint8_t* block_mask, int64_t mask_heads, sdpa_dtype dtype,
+                                  sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream) {
+  sdpa::BwdArgs a;
+  const sdpa_status st =
+      sdpa::validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
+                         is_causal, dtype, out_dtype, grad_dtype, stream, &a);
+  if (st != SDPA_OK) return st;
+  const sdpa_status sm = sdpa::validate_bwd_block_mask(block_mask, mask_heads, &a);
+  if (sm != SDPA_OK) return sm;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bwd_mfma_masked_bf16(a)
+                                          : sdpa::launch_bwd_mfma_masked_f16(a);
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 sdpa_status sdpa_bwd_packed(const void* q, const void* k, const void* v, const void* out,
                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
                             float* workspace, int64_t B, int64_t H, int64_t T,

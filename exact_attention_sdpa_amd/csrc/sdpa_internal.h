@@ -67,6 +67,8 @@ struct BwdArgs {
   const void* amask;        // elementwise mask, or null
   int amask_kind;           // sdpa_mask_kind
   int64_t am_str[3];        // mask (batch, head, row) strides, elements
+  const uint8_t* bmask;     // block-sparse mask, or null
+  int64_t mask_heads;       // 1 (shared) or H
 };
 
 // Host-only argument checks (no HIP calls).  Fills `a` on success.
@@ -101,6 +103,10 @@ sdpa_status validate_attn_mask(const void* mask, sdpa_mask_kind kind,
 // 32-bit offsets, and the mask clear of dq, dk, dv and the workspace.
 sdpa_status validate_bwd_attn_mask(const void* mask, sdpa_mask_kind kind,
                                    const int64_t* mask_strides, BwdArgs* a);
+
+// Adds a block-sparse mask to validated dense backward arguments: as
+// validate_block_mask, and the mask clear of dq, dk, dv and the workspace.
+sdpa_status validate_bwd_block_mask(const uint8_t* mask, int64_t mask_heads, BwdArgs* a);
 
 // Adds dropout to validated backward arguments (same rules as the forward).
 sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a);

@@ -276,6 +276,23 @@ sdpa_status validate_bwd_attn_mask(const void* mask, sdpa_mask_kind kind,
   return SDPA_OK;
 }
 
+sdpa_status validate_bwd_block_mask(const uint8_t* mask, int64_t mask_heads, BwdArgs* a) {
+  if (mask == nullptr || (mask_heads != 1 && mask_heads != a->H)) return SDPA_ERR_INVALID;
+  if (a->cu != nullptr) return SDPA_ERR_INVALID;
+  constexpr int64_t blk = SDPA_BLOCK_SPARSE_BLOCK;
+  const int64_t nqb = (a->Nq + blk - 1) / blk, nkb = (a->Nk + blk - 1) / blk;
+  int64_t mb = 0;
+  if (!mul_ok(mask_heads * nqb, nkb, &mb) || mb > INT32_MAX) return SDPA_ERR_INVALID;
+  const int64_t gb = a->grad_f32 ? 4 : 2;
+  const int64_t eq = a->B * a->H * a->Nq * a->d, ek = a->B * a->H * a->Nk * a->d;
+  if (overlap(mask, mb, a->dq, eq * gb) || overlap(mask, mb, a->dk, ek * gb) ||
+      overlap(mask, mb, a->dv, ek * gb) || overlap(mask, mb, a->work, a->B * a->H * a->Nq * 4))
+    return SDPA_ERR_INVALID;
+  a->bmask = mask;
+  a->mask_heads = mask_heads;
+  return SDPA_OK;
+}
+
 sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a) {
   if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;   // NaN fails too
   if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
@@ -375,6 +392,8 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
   a->amask = nullptr;
   a->amask_kind = SDPA_MASK_BOOL;
   a->am_str[0] = a->am_str[1] = a->am_str[2] = 0;
+  a->bmask = nullptr;
+  a->mask_heads = 0;
   a->B = B;
   a->H = H;
   a->Nq = Nq;

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 9
+#define SDPA_ABI_VERSION 10
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -309,6 +309,28 @@ SDPA_API sdpa_status sdpa_bwd_masked(const void* q, const void* k, const void* v
                                      int is_causal, const void* mask, sdpa_mask_kind mask_kind,
                                      const int64_t* mask_strides, sdpa_dtype dtype,
                                      sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
+
+/* Backward pass of sdpa_fwd_block_sparse: the gradients of sum(dout * out)
+ * for exact attention restricted to the pairs the block mask keeps (the
+ * chain rule of sdpa_bwd over the visible pairs).  Only the tiles whose
+ * 128x128 mask block is kept are read or computed; rows that see no key
+ * (lse = -inf) contribute nothing, and keys no row sees get zero
+ * gradients.
+ *
+ * block_mask, mask_heads  as sdpa_fwd_block_sparse (the forward's mask).
+ * Other arguments as sdpa_bwd: dense contiguous layouts, f16/bf16, no
+ * dropout.  The mask must not overlap dq, dk, dv or the workspace.
+ * Returns SDPA_ERR_INVALID for a null mask or mask_heads not in {1, H},
+ * otherwise as sdpa_bwd.
+ */
+SDPA_API sdpa_status sdpa_bwd_block_sparse(const void* q, const void* k, const void* v,
+                                           const void* out, const void* dout, const float* lse,
+                                           void* dq, void* dk, void* dv, float* workspace,
+                                           int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                           int64_t d, float scale, int is_causal,
+                                           const uint8_t* block_mask, int64_t mask_heads,
+                                           sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                           sdpa_dtype grad_dtype, void* stream);
 
 /* Backward pass of a packed variable-length batch: the gradients of
  * sdpa_fwd (or sdpa_fwd_dropout) with cu_seqlens, the chain rule of

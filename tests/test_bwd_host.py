@@ -70,3 +70,20 @@ def test_invalid_dropout_rate_rejected_on_host(lib, pd, status):
                               a["dv"], a["w"], 2, 4, 128, 128, 64, 0.125, 0, pd, 1, 0, F16, SAME,
                               SAME, None)
     assert st == status
+
+
+def test_block_sparse_backward_rejected_on_host():
+    from exact_attention_sdpa_amd import _lib
+    lib = _lib.lib()
+    OK_, INVALID_, UNSUP_, DEVICE_ = 0, 1, 2, 4
+    Q, K, V, O, G, L, DQ, DK, DV, W, M = (0x1000000 * (i + 1) for i in range(11))
+
+    def call(mask=M, heads=1, dt=0, w=W):
+        return lib.sdpa_bwd_block_sparse(Q, K, V, O, G, L, DQ, DK, DV, w, 2, 4, 256, 256, 64,
+                                         0.125, 0, mask, heads, dt, 255, 255, None)
+    assert call() in (OK_, DEVICE_)
+    assert call(heads=4) in (OK_, DEVICE_)
+    assert call(mask=None) == INVALID_
+    assert call(heads=3) == INVALID_
+    assert call(dt=2) == UNSUP_
+    assert call(mask=DQ) == INVALID_        # overlaps an output

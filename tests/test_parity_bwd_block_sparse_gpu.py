@@ -1,0 +1,117 @@
+"""GPU parity of the block-sparse backward (sdpa_bwd_block_sparse) against
+the fp64 masked gradient oracle (oracle/grad.py: sdpa_bwd_masked) applied to
+the block mask expanded to (query, key) pairs (oracle/block_sparse.py:
+visibility), through the C ABI.  The forward runs on the GPU first with the
+same block mask.  The elementwise bound is the masked backward's (the dense
+backward's terms plus the f16 subnormal floor per visible pair), allowed
+twice over.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_sdpa_amd as sdpa
+from exact_attention_sdpa_amd import inputs
+from oracle import block_sparse as obsp
+from oracle import grad as ograd
+from oracle import masked as omask
+from tests.gpu_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+U, U_SUB, E_LSE = 2.0 ** -11, 2.0 ** -25, 1e-4
+U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}
+
+
+def _run(w, do, bm):
+    q, k, v = (to_device(x, w.dtype) for x in (w.q, w.k, w.v))
+    g = to_device(do, w.dtype)
+    bmt = torch.from_numpy(np.ascontiguousarray(bm)).cuda()
+    odt = torch.float32 if w.dtype == "bf16" else None
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, is_causal=w.is_causal,
+                                                 scale=float(w.scale), out_dtype=odt,
+                                                 return_lse=True, block_mask=bmt)
+    grads = sdpa.scaled_dot_product_attention_backward(
+        q, k, v, out, lse, g, is_causal=w.is_causal, scale=float(w.scale),
+        grad_dtype=torch.float32, block_mask=bmt)
+    torch.cuda.synchronize()
+    return [t.double().cpu().numpy() for t in grads]
+
+
+def _check(w, got, do, bm):
+    do64 = inputs.storage_to_f64(do, w.dtype)
+    sc = float(w.scale)
+    for b in range(w.B):
+        for h in range(w.H):
+            vis = obsp.visibility(w.Nq, w.Nk, bm[h % bm.shape[0]], 128, False)
+            ref = ograd.sdpa_bwd_masked(w.q64[b:b + 1, h:h + 1], w.k64[b:b + 1, h:h + 1],
+                                        w.v64[b:b + 1, h:h + 1], do64[b:b + 1, h:h + 1],
+                                        vis[None, None].astype(np.uint8), "bool", sc,
+                                        w.is_causal)
+            bias = np.where(vis, 0.0, -np.inf)
+            q, k, v, g = w.q64[b, h], w.k64[b, h], w.v64[b, h], do64[b, h]
+            o, _ = omask.attend_biased(q, k, v, sc, bias, w.is_causal)
+            s = sc * (q @ k.T) + bias
+            if w.is_causal:
+                s = np.where(np.arange(w.Nk)[None, :] <= np.arange(w.Nq)[:, None], s, -np.inf)
+            P = np.zeros_like(s)
+            live = np.any(s > -np.inf, axis=1)
+            e = np.exp(s[live] - np.max(s[live], axis=1, keepdims=True))
+            P[live] = e / np.sum(e, axis=1, keepdims=True)
+            seen = (s > -np.inf).astype(np.float64)
+            dp = g @ v.T
+            dd = np.sum(g * o, axis=1, keepdims=True)
+            e_d = np.sum(np.abs(g) * (U * (P @ np.abs(v)) + U_OUT[w.dtype] * np.abs(o)), axis=1,
+                         keepdims=True)
+            t = U * np.abs(P * (dp - dd)) + U_SUB * seen + P * (e_d + E_LSE * np.abs(dp - dd))
+            bounds = (sc * (t @ np.abs(k)), sc * (t.T @ np.abs(q)),
+                      ((U + E_LSE) * P + U_SUB * seen).T @ np.abs(g))
+            for name, gt, r, bd in zip(("dq", "dk", "dv"), got, ref, bounds):
+                gu, ru = gt[b, h], r[0, 0]
+                assert np.all(np.isfinite(gu)), f"({b},{h}) {name}: non-finite"
+                worst = float(np.max(np.abs(gu - ru) / (2.0 * bd + 1e-30)))
+                assert worst <= 1.0, f"({b},{h}) {name}: error {worst:.3f} x bound"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_block_sparse_ragged(dtype, d, causal):
+    B, H, Nq, Nk = 2, 2, 600, 530   # several blocks, ragged tails
+    w = inputs.make_dense(B, H, Nq, Nk, d, dtype, "normal", causal, seed=d, cfg=140)
+    do = inputs.make_grad_out(w, seed=d, cfg=140)
+    bm = inputs.make_block_mask(H, Nq, Nk, 0.5, diagonal=True, seed=d + causal, cfg=141)
+    _check(w, _run(w, do, bm), do, bm)
+
+
+def test_bwd_block_sparse_empty_rows_and_columns():
+    # a mask row with no kept block (rows see no key: zero dq) and a mask
+    # column with none (keys no row sees: zero dk, dv)
+    B, H, N, d = 1, 2, 512, 64
+    w = inputs.make_dense(B, H, N, N, d, "f16", "normal", False, seed=3, cfg=142)
+    do = inputs.make_grad_out(w, seed=3, cfg=142)
+    bm = np.ones((1, 4, 4), np.uint8)
+    bm[0, 1, :] = 0
+    bm[0, :, 2] = 0
+    got = _run(w, do, bm)
+    assert np.all(got[0][:, :, 128:256] == 0)
+    assert np.all(got[1][:, :, 256:384] == 0) and np.all(got[2][:, :, 256:384] == 0)
+    _check(w, got, do, bm)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_block_mask_matches_dense_backward(causal):
+    # every block kept: the same tiles in the same order as the dense
+    # backward, so the same bits
+    B, H, N, d = 1, 2, 384, 64
+    w = inputs.make_dense(B, H, N, N, d, "f16", "normal", causal, seed=4, cfg=143)
+    do = inputs.make_grad_out(w, seed=4, cfg=143)
+    got = _run(w, do, np.ones((1, 3, 3), np.uint8))
+    q, k, v = (to_device(x, "f16") for x in (w.q, w.k, w.v))
+    g = to_device(do, "f16")
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, is_causal=causal, return_lse=True)
+    dense = sdpa.scaled_dot_product_attention_backward(q, k, v, out, lse, g, is_causal=causal,
+                                                       grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(got, dense):
+        assert np.array_equal(a, b.double().cpu().numpy())
