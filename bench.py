@@ -593,10 +593,6 @@ def main(argv=None) -> int:
                 raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
-        if w.block_mask is not None:
-            print("bench.py: the backward pass takes no block-sparse mask",
-                  file=sys.stderr)
-            return 2
         step()   # the forward's out and lse feed the backward
         g = up(inputs.make_grad_out(w, cfg=WORKLOADS[a.workload]))
         gdt = torch.float32 if out_f32 else q.dtype
@@ -614,6 +610,15 @@ def main(argv=None) -> int:
             st = (L.sdpa_bwd_dropout if a.dropout > 0 else L.sdpa_bwd)(*bargs)
             if st != 0:
                 raise sdpa.SdpaError(st)
+
+        if w.block_mask is not None:   # the block-sparse backward, same mask
+            bsargs = bargs[:17] + [bm.data_ptr(), int(bm.shape[0]), dt, odt,
+                                   sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME, handle]
+
+            def step():  # noqa: F811 -- the block-sparse backward
+                st = L.sdpa_bwd_block_sparse(*bsargs)
+                if st != 0:
+                    raise sdpa.SdpaError(st)
 
         if w.attn_mask is not None:   # the elementwise-mask backward, same mask layout
             margs_b = bargs[:17] + [mt.data_ptr(), mkind, ctypes.cast(mstr_c, ctypes.c_void_p),
