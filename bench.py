@@ -179,9 +179,13 @@ def cpu_baseline(w, budget_s: float, dropout: float = 0.0):
     sample = f"{n} of {len(units)} (batch, head) units"
     if w.Nq > 8192:
         sample += ", last 256 query rows each"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 2),
-            "host_cpus": len(os.sched_getaffinity(0))}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle", "sample": sample, "seconds": round(dt, 2),
+           "host_cpus": len(os.sched_getaffinity(0))}
+    # the whole workload at the sampled rate (scaled by FLOPs: the oracle's
+    # time grows with the pairs it computes)
+    rec["full_workload_seconds_extrapolated"] = round(dt * w.flops() / flops, 1)
+    return rec
 
 
 def _cpu_baseline_block_sparse(w, budget_s, threads):
@@ -735,8 +739,22 @@ def main(argv=None) -> int:
         rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget, a.dropout) if a.which == "fwd"
                                else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload],
                                                      a.dropout))
+    if rec.get("cpu_baseline"):
+        rec["cpu_baseline"]["cpu_model"] = _cpu_model()
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
