@@ -133,6 +133,10 @@ enum FwdVariant : int {
 #ifndef SDPA_SETPRIO
 #define SDPA_SETPRIO 1
 #endif
+// Build option: waves skip tiles their boolean mask drops entirely.
+#ifndef SDPA_MASK_SKIP
+#define SDPA_MASK_SKIP 1
+#endif
 // Build option: causal dense grids in longest-processing-time order.
 #ifndef SDPA_CAUSAL_LPT
 #define SDPA_CAUSAL_LPT 1
@@ -699,7 +703,21 @@ struct MfmaFwd {
       load_k(kr, x.st, x.hd, jn, x.tid);
       load_v(vr, x.st, x.hd, jn, x.tid);
     }
-    if (live) {
+    // boolean masks: a tile whose mask drops every pair of the wave's rows
+    // adds nothing (its P would be exactly 0), so the wave skips it, e.g.
+    // the keys past a sequence's end under a key-padding mask
+    bool run_tile = live;
+    if (VAR == kMaskBool && SDPA_MASK_SKIP && live) {
+      uint32_t any = 0;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) any |= mr.w[kk][qb][g][0];
+      run_tile = __builtin_amdgcn_ballot_w64(any != 0u) != 0;
+    }
+    if (run_tile) {
       const int kb = j * BN;
       const bool masked = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
       tile(sm, B, kb, !BSP && j == 0, masked, x, qf, S, mr);
