@@ -344,6 +344,32 @@ def copy_calibration(torch) -> int:
     return 0
 
 
+def gemm_calibration(torch) -> int:
+    """Attainable matrix-core rate for reference: the vendor BLAS (torch.mm on
+    ROCm: hipBLASLt) on square 8192 GEMMs, fp16 and bf16, fp32 accumulate."""
+    n = 8192
+    for dt in (torch.float16, torch.bfloat16):
+        a = torch.randn(n, n, device="cuda").to(dt)
+        b = torch.randn(n, n, device="cuda").to(dt)
+        for _ in range(3):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"calibration": "gemm", "dtype": str(dt).replace("torch.", ""),
+                          "m": n, "n": n, "k": n, "ms": round(ms, 4),
+                          "TFLOPs": round(tf, 1),
+                          "pct_of_peak": round(100.0 * tf / PEAK_TFLOPS, 1)}))
+    return 0
+
+
 def _csv_rows(d, name):
     import csv
     import glob
@@ -499,6 +525,9 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (5 times), the "
                          "reference for scaling HBM byte counters")
+    ap.add_argument("--calibrate-gemm", action="store_true",
+                    help="run only square 8192 fp16/bf16 GEMMs through the vendor BLAS, "
+                         "an attainable matrix-core rate for reference")
     ap.add_argument("--summarize", action="store_true",
                     help="summarize rocprofv3 CSV outputs into profiles/ (no GPU needed)")
     ap.add_argument("--trace-dir")
@@ -528,6 +557,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     if a.calibrate_copy:
         return copy_calibration(torch)
+    if a.calibrate_gemm:
+        return gemm_calibration(torch)
     w = inputs.make_config(WORKLOADS[a.workload])
 
     def up(x):
