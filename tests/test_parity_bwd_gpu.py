@@ -7,22 +7,27 @@ stored q, k, v and dO.
 
 Tolerance, from the arithmetic (elementwise).  q, k, v and dO are exact
 matrix-core operands and every product accumulates in fp32.  The roundings
-are: P and dS, each rounded to f16 (relative u = 2^-11) before its product;
-the forward's O inside D_i = <dO_i, O_i>, whose error per element is at most
+are: P and dS, each rounded to f16 (relative u = 2^-11) before its product
+(below 2^-14, f16's subnormal range, the error is absolute instead, at most
+U_SUB = 2^-25 per visible pair); the forward's O inside D_i = <dO_i, O_i>,
+whose error per element is at most
 u * sum_j P_ij |v_jc| (its own f16 P) plus u_o |O_ic| (rounding to the
 output dtype), so D_i is off by at most
     e_D,i = sum_c |dO_ic| (u (P|V|)_ic + u_o |O_ic|);
 the forward's lse, whose error e_lse (at most 1e-4, the forward's bound)
 scales P by up to e_lse; and, for gradients stored in f16/bf16, one final
-rounding.  So, per element,
-    |err dV_j| <= sum_i (u + e_lse) P_ij |dO_i|
-    |err dQ_i| <= scale * sum_j (u |dS_ij| + P_ij (e_D,i + e_lse |dP_ij - D_i|)) |k_j|
+rounding (plus U_SUB for an f16 result in the subnormal range).  So, per
+element,
+    |err dV_j| <= sum_i ((u + e_lse) P_ij + U_SUB) |dO_i|
+    |err dQ_i| <= scale * sum_j (u |dS_ij| + U_SUB + P_ij (e_D,i + e_lse |dP_ij - D_i|)) |k_j|
     |err dK_j| <= the same with q_i in place of k_j,
 plus the output rounding.  The sums are taken from fp64 intermediates, and
 the test allows twice the bound for fp32 accumulation and exp2.  Note the
 bound is relative to the sum of magnitudes, not to the result: dQ and dK are
 sums whose terms cancel (every row of dS sums to zero).
 """
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -36,6 +41,7 @@ from tests.gpu_util import to_device
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -11
+U_SUB = 2.0 ** -25   # half the f16 subnormal spacing
 E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}   # bf16 runs keep O in f32
 U_GRAD = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
@@ -72,15 +78,16 @@ def _ref_and_bound(w, do, grad_f32=True):
             e_d = np.sum(np.abs(g) * (U * (p @ np.abs(v)) + uo * np.abs(o64[b, h])),
                          axis=1, keepdims=True)
             shift = p * (e_d + E_LSE * np.abs(dp - dd))
-            t = U * ds_abs + shift
-            bv[b, h] = ((U + E_LSE) * p).T @ np.abs(g)
+            vis = (p > 0).astype(np.float64)
+            t = U * ds_abs + U_SUB * vis + shift
+            bv[b, h] = ((U + E_LSE) * p + U_SUB * vis).T @ np.abs(g)
             bq[b, h] = sc * (t @ np.abs(k))
             bk[b, h] = sc * (t.T @ np.abs(q))
     bounds = []
     for r, bd in zip(ref, (bq, bk, bv)):
         bd = 2.0 * bd
         if not grad_f32:
-            bd = bd + U_GRAD[w.dtype] * np.abs(r)
+            bd = bd + U_GRAD[w.dtype] * np.abs(r) + (U_SUB if w.dtype == "f16" else 0.0)
         bounds.append(bd + 1e-30)
     return ref, bounds
 
@@ -135,6 +142,25 @@ def test_bwd_1024_invariants_and_parity(causal):
     # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, within the summed bounds
     assert np.all(np.abs(dk.sum(axis=2)) <= rb[1][1].sum(axis=2))
     assert np.all(np.abs(dv.sum(axis=2) - do64.sum(axis=2)) <= rb[1][2].sum(axis=2))
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_bwd_full_workload_sampled_units(cfg):
+    # the noncausal (B32 H32 N1024 d32) and causal (B32 H8 N1024 d64)
+    # workloads at full size, in the launch configuration the benchmark's
+    # backward times (gradients in the input dtype); the oracle checks four
+    # whole (batch, head) units spread over the grid, the first and the last
+    # among them
+    w = inputs.make_config(cfg)
+    do = inputs.make_grad_out(w, seed=cfg, cfg=46)
+    got = _run(w, do, grad_f32=False)
+    units = [(0, 0), (w.B // 3, w.H - 1), (2 * w.B // 3, w.H // 2), (w.B - 1, w.H - 1)]
+    bi, hi = [b for b, _ in units], [h for _, h in units]
+    f64 = lambda a: inputs.storage_to_f64(a[bi, hi][None], w.dtype)
+    sub = types.SimpleNamespace(B=1, H=len(units), dtype=w.dtype, scale=w.scale,
+                                is_causal=w.is_causal, q64=f64(w.q), k64=f64(w.k), v64=f64(w.v))
+    _check([g[bi, hi][None] for g in got], _ref_and_bound(sub, do[bi, hi][None], grad_f32=False),
+           f"{w.name} full size, sampled units")
 
 
 def test_bwd_deterministic():
