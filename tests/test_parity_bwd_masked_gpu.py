@@ -10,6 +10,8 @@ every visible pair (a masked pair's P is an exact 0).  Masks make such
 pairs common enough to matter: a key that only one row sees keeps a tiny P
 unaveraged.
 """
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -32,7 +34,7 @@ def _mask_t(m, kind, mdt):
     return torch.from_numpy(m).cuda().bool() if kind == "bool" else to_device(m, mdt)
 
 
-def _run(w, do, mt):
+def _run(w, do, mt, grad_f32=True):
     q, k, v = (to_device(x, w.dtype) for x in (w.q, w.k, w.v))
     g = to_device(do, w.dtype)
     odt = torch.float32 if w.dtype == "bf16" else None
@@ -41,13 +43,15 @@ def _run(w, do, mt):
                                                  return_lse=True)
     dq, dk, dv = sdpa.scaled_dot_product_attention_backward(
         q, k, v, out, lse, g, is_causal=w.is_causal, scale=float(w.scale),
-        grad_dtype=torch.float32, attn_mask=mt)
+        grad_dtype=torch.float32 if grad_f32 else None, attn_mask=mt)
     torch.cuda.synchronize()
     return [t.double().cpu().numpy() for t in (dq, dk, dv)]
 
 
-def _check(w, got, do, m4, kind, mdt):
-    """m4: the mask broadcast to 4-D (bool bytes or stored additive values)."""
+def _check(w, got, do, m4, kind, mdt, grad_f32=True):
+    """m4: the mask broadcast to 4-D (bool bytes or stored additive values).
+    Gradients stored in f16 add one final rounding (relative 2^-11, or U_SUB
+    in the subnormal range)."""
     do64 = inputs.storage_to_f64(do, w.dtype)
     mv = m4 if kind == "bool" else inputs.storage_to_f64(m4, mdt)
     ref = ograd.sdpa_bwd_masked(w.q64, w.k64, w.v64, do64, mv, kind, float(w.scale), w.is_causal)
@@ -75,6 +79,8 @@ def _check(w, got, do, m4, kind, mdt):
                       ((U + E_LSE) * P + U_SUB * vis).T @ np.abs(g))
             for name, gt, r, bd in zip(("dq", "dk", "dv"), got, ref, bounds):
                 gu, ru, bu = gt[b, h], r[b, h], 2.0 * bd + 1e-30
+                if not grad_f32:
+                    bu = bu + U * np.abs(ru) + U_SUB
                 assert np.all(np.isfinite(gu)), f"({b},{h}) {name}: non-finite"
                 worst = float(np.max(np.abs(gu - ru) / bu))
                 assert worst <= 1.0, f"({b},{h}) {name}: error {worst:.3f} x bound"
@@ -93,6 +99,29 @@ def test_bwd_masked_ragged(dtype, d, causal, kind):
     m = inputs.make_attn_mask((B, H, Nq, Nk), mk, keep=0.8, seed=d + causal, cfg=131, dtype=mdt)
     got = _run(w, do, _mask_t(m, mk, mdt))
     _check(w, got, do, m, mk, mdt)
+
+
+@pytest.mark.parametrize("cfg", [7, 8])
+def test_bwd_masked_full_workload_sampled_units(cfg):
+    # the masked (additive f16 [32, 8, 1024, 1024]) and padded (key-padding
+    # bool [32, 1, 1, 512]) workloads at full size, in the benchmark's launch
+    # configuration (f16 gradients); four whole (batch, head) units, the
+    # first and the last among them, are checked against the oracle
+    w = inputs.make_config(cfg)
+    assert w.dtype == "f16"
+    do = inputs.make_grad_out(w, seed=cfg, cfg=132)
+    kind = w.mask_kind
+    got = _run(w, do, _mask_t(w.attn_mask, kind, w.dtype), grad_f32=False)
+    units = [(0, 0), (w.B // 3, w.H - 1), (2 * w.B // 3, w.H // 2), (w.B - 1, w.H - 1)]
+    bi, hi = [b for b, _ in units], [h for _, h in units]
+    f64 = lambda a: inputs.storage_to_f64(a[bi, hi][None], w.dtype)
+    sub = types.SimpleNamespace(B=1, H=len(units), Nq=w.Nq, Nk=w.Nk, dtype=w.dtype,
+                                scale=w.scale, is_causal=w.is_causal,
+                                q64=f64(w.q), k64=f64(w.k), v64=f64(w.v))
+    m = w.attn_mask
+    msub = m[bi, [h % m.shape[1] for h in hi]][None]
+    _check(sub, [g[bi, hi][None] for g in got], do[bi, hi][None], msub, kind, w.dtype,
+           grad_f32=False)
 
 
 @pytest.mark.parametrize("shape", [(2, 1, 1, 256), (1, 3, 200, 256), (200, 256)])
