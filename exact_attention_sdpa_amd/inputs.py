@@ -268,6 +268,93 @@ def make_block_mask(heads: int, nq: int, nk: int, density: float, diagonal=False
     return m
 
 
+# --- score structures that move the softmax's row maximum late -------------
+#
+# Random N(0,1) inputs keep every score within a few units of the first
+# block's maximum, so a kernel that fixes its softmax reference early is
+# never made to move it.  These families build q and k (v stays N(0,1)) so
+# that the maximum of a row arrives after its first block of keys:
+#
+#   late      keys are scaled to length sqrt(d), and each query row is
+#             aligned with one key of the row's last key tile (its own key
+#             when causal, else one of the last 64 keys):
+#             q_i = 0.25 z_i + beta * k_j / (scale d) puts that key's score
+#             beta = 48 natural-log units above a typical score.
+#   rising    scores climb steadily along the keys: q_i[0] = 8 and
+#             k_j[0] = rate * pos_j with rate chosen so that 2048 keys add
+#             120 log2 units (pos_j counts from the start of the key's own
+#             sequence).
+#   low_first the first 32 keys of every unit sit 25 log2 units below the
+#             rest: q_i[0] = 8, k_j[0] = -drop for pos_j < 32.
+#
+# Offsets are applied in float32 before the rounding to the storage dtype;
+# the oracle sees the stored values, whatever the rounding did to them.
+
+RESCALE_FAMILIES = ("late", "rising", "low_first")
+_RISE_LOG2_PER_KEY = 120.0 / 2048.0
+_LATE_MARGIN = 48.0
+_LOW_FIRST_LOG2 = 25.0
+_LOG2E = 1.4426950408889634
+
+
+def _shape_unit(q: np.ndarray, k: np.ndarray, family: str, causal: bool, scale: float) -> None:
+    """Apply ``family`` in place to one unit's q [nq, d] and k [nk, d]
+    (float32, rows in sequence order)."""
+    nq, nk = q.shape[0], k.shape[0]
+    if nq == 0 or nk == 0:
+        return
+    if family == "late":
+        # keys on the sphere of radius sqrt(d), so that a row's margin does
+        # not depend on its key's length
+        d = k.shape[1]
+        k64 = k.astype(np.float64)
+        k64 *= math.sqrt(d) / np.maximum(np.linalg.norm(k64, axis=1, keepdims=True), 1e-6)
+        k[:] = k64.astype(np.float32)
+        i = np.arange(nq)
+        j = np.minimum(i, nk - 1) if causal else nk - 1 - (i % min(64, nk))
+        q[:] = (0.25 * q + _LATE_MARGIN * k64[j] / (scale * d)).astype(np.float32)
+        return
+    a = np.float32(8.0)
+    q[:, 0] = a
+    if family == "rising":
+        rate = _RISE_LOG2_PER_KEY / (scale * _LOG2E * float(a))
+        k[:, 0] = (rate * np.arange(nk)).astype(np.float32)
+    elif family == "low_first":
+        drop = _LOW_FIRST_LOG2 / (scale * _LOG2E * float(a))
+        k[:, 0] = 0.0
+        k[:min(32, nk), 0] = np.float32(-drop)
+    else:
+        raise ValueError(f"unknown family {family!r}")
+
+
+def make_rescale(family: str, B, H, Nq, Nk, d, dtype="f16", is_causal=False, seed=0, cfg=0,
+                 lens=None, name=None) -> Workload:
+    """A dense (or, with ``lens``, packed) workload whose row maxima arrive
+    late (see the family list above); N(0,1) values otherwise."""
+    if lens is not None:
+        w = make_varlen(lens, H, d, "f32", "normal", is_causal, seed, cfg)
+        q32, k32 = w.q.copy(), w.k.copy()
+        cu = w.cu_seqlens
+        for s in range(len(cu) - 1):
+            for h in range(H):
+                sl = slice(int(cu[s]), int(cu[s + 1]))
+                qs, ks = q32[sl, h].copy(), k32[sl, h].copy()
+                _shape_unit(qs, ks, family, is_causal, float(w.scale))
+                q32[sl, h], k32[sl, h] = qs, ks
+    else:
+        w = make_dense(B, H, Nq, Nk, d, "f32", "normal", is_causal, seed, cfg)
+        q32, k32 = w.q.copy(), w.k.copy()
+        for b in range(B):
+            for h in range(H):
+                _shape_unit(q32[b, h], k32[b, h], family, is_causal, float(w.scale))
+    w.q = to_storage(q32, dtype)
+    w.k = to_storage(k32, dtype)
+    w.v = to_storage(w.v, dtype)
+    w.dtype = dtype
+    w.name = name or f"rescale-{family}"
+    return w
+
+
 CONFIG_NAMES = {1: "tiny", 2: "noncausal", 3: "causal", 4: "varlen", 5: "long", 7: "masked",
                 8: "padded",
                 6: "block_sparse"}

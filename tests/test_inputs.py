@@ -113,3 +113,48 @@ def test_visible_pairs_counts_the_oracle_visibility():
         # a one-head mask counts once per head
         assert inputs.visible_pairs(m[:1], nq, nk, causal, 4) == \
             4 * int(obsp.visibility(nq, nk, m[0], 128, causal).sum())
+
+
+# --- the late-maximum families -------------------------------------------------
+
+def _log2_scores(w, b=0, h=0):
+    """Scaled scores of one unit in log2 units, causal pairs set to -inf."""
+    s = float(w.scale) * 1.4426950408889634 * (w.q64[b, h] @ w.k64[b, h].T)
+    if w.is_causal:
+        s = np.where(np.tri(s.shape[0], s.shape[1], dtype=bool), s, -np.inf)
+    return s
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rescale_families_move_the_row_maximum(dtype, d, causal):
+    """Every family puts a row's maximum well after its first 32 keys: the
+    jump over the first block's maximum is >= 20 log2 units (late,
+    low_first), and rising scores climb >= 100 log2 units over 2048 keys."""
+    for fam, n in (("late", 520), ("low_first", 520), ("rising", 2090)):
+        w = inputs.make_rescale(fam, 1, 1, n, n, d, dtype, causal, seed=3, cfg=9)
+        s = _log2_scores(w)
+        first = np.max(s[:, :32], axis=1)
+        later = np.max(s[:, 32:], axis=1)
+        rows = np.arange(n) >= 64
+        if fam == "rising":
+            rows = np.arange(n) >= 2048 if causal else np.ones(n, bool)
+            jump = np.max(s[:, 2016:2048], axis=1) - first
+            assert np.min(jump[rows]) >= 100, (fam, float(np.min(jump[rows])))
+        else:
+            jump = later - first
+            assert np.min(jump[rows]) >= 20, (fam, float(np.min(jump[rows])))
+        assert np.all(np.isfinite(w.q64)) and np.all(np.abs(w.q64) < 1e4)
+        assert np.all(np.abs(w.k64) < 1e4)
+
+
+def test_rescale_packed_families_restart_per_sequence():
+    w = inputs.make_rescale("low_first", None, 2, None, None, 64, "f16", True, seed=1, cfg=9,
+                            lens=[40, 0, 70])
+    cu = w.cu_seqlens
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        k0 = w.k64[a:b, 0, 0]
+        if b - a:
+            assert np.all(k0[:min(32, b - a)] < -1) and np.all(k0[32:] == 0)
