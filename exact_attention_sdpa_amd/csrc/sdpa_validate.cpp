@@ -297,24 +297,34 @@ sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a
   if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;   // NaN fails too
   if (a->dtype == SDPA_F32) return SDPA_ERR_UNSUPPORTED;
   if (p == 0.f) return SDPA_OK;   // no dropout: the plain kernel
-  const double keep = 1.0 - (double)p;
+  // keep iff a 16-bit number is below T: the keep probability is T / 65536
+  // (1 - p rounded to 16 bits), and kept weights are divided by exactly
+  // that, so the expected output is the undropped one.  p so close to 1
+  // that T rounds to 0 would drop everything: refused.
+  const double t = std::floor((1.0 - (double)p) * 65536.0 + 0.5);
+  if (t < 1.0) return SDPA_ERR_UNSUPPORTED;
   a->dropout = true;
   a->drop_seed = seed;
   a->drop_offset = offset;
-  a->drop_t = (uint32_t)std::floor(keep * 65536.0 + 0.5);
-  a->drop_scale = (float)(1.0 / keep);
+  a->drop_t = (uint32_t)t;
+  a->drop_scale = (float)(65536.0 / t);
   return SDPA_OK;
 }
 
 sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a) {
   if (!(p >= 0.f && p < 1.f)) return SDPA_ERR_INVALID;
   if (p == 0.f) return SDPA_OK;
-  const double keep = 1.0 - (double)p;
+  // keep iff a 16-bit number is below T: the keep probability is T / 65536
+  // (1 - p rounded to 16 bits), and kept weights are divided by exactly
+  // that, so the expected output is the undropped one.  p so close to 1
+  // that T rounds to 0 would drop everything: refused.
+  const double t = std::floor((1.0 - (double)p) * 65536.0 + 0.5);
+  if (t < 1.0) return SDPA_ERR_UNSUPPORTED;
   a->dropout = true;
   a->drop_seed = seed;
   a->drop_offset = offset;
-  a->drop_t = (uint32_t)std::floor(keep * 65536.0 + 0.5);
-  a->drop_scale = (float)(1.0 / keep);
+  a->drop_t = (uint32_t)t;
+  a->drop_scale = (float)(65536.0 / t);
   return SDPA_OK;
 }
 

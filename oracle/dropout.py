@@ -8,9 +8,10 @@ What it computes.  The SDPA tutorial's CausalSelfAttention ("Causal
 self-attention" section) passes its dropout rate to the functional call in
 training.  Dropout on the attention weights: with P the softmax of the
 visible scores (as in oracle/sdpa.py), each weight is kept with probability
-1 - p and kept weights are divided by 1 - p:
+1 - p and kept weights are divided by the keep probability (inverted
+dropout, so that the expected output is the undropped one):
 
-    O_i   = sum_j P_ij z_ij / (1 - p) v_j,   z_ij in {0, 1}
+    O_i   = sum_j P_ij z_ij / kappa v_j,   z_ij in {0, 1}
     lse_i = the logsumexp of the (undropped) visible scores
 
 The pages fix no random-number contract; this is the one taken (the GPU
@@ -27,8 +28,11 @@ kernel implements it independently):
                T = floor((1 - p) * 65536 + 1/2), p taken as a float32
 
 so each call decides 8 keys of one query row, and (n, e) runs over every
-key exactly once.  The keep probability is T / 65536, within 2^-17 of
-1 - p.
+key exactly once.  The keep probability is kappa = T / 65536, within 2^-17
+of 1 - p, and kept weights are divided by that kappa (reading: the scale is
+the inverse of the keep probability actually drawn, which leaves the
+expected output unbiased).  A p that rounds T to 0 would keep nothing; it
+is outside the contract.
 """
 from __future__ import annotations
 
@@ -39,6 +43,11 @@ from .philox import philox4
 
 def keep_threshold(p) -> int:
     return int(np.floor((1.0 - float(np.float32(p))) * 65536.0 + 0.5))
+
+
+def keep_probability(p) -> float:
+    """kappa = T / 65536, the probability that a weight is kept."""
+    return keep_threshold(p) / 65536.0
 
 
 def draw16(nq, nk, unit, seed, offset, row0=0):
@@ -77,8 +86,7 @@ def attend_dropout(q, k, v, scale, is_causal, p, seed, offset, unit):
     l = np.sum(e, axis=1, keepdims=True)
     P = e / l
     z = keep_mask(nq, nk, unit, p, seed, offset)
-    keep = 1.0 - float(np.float32(p))
-    O = ((P * z) / keep) @ v
+    O = ((P * z) / keep_probability(p)) @ v
     return O, m[:, 0] + np.log(l[:, 0])
 
 

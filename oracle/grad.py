@@ -76,20 +76,20 @@ def sdpa_bwd(q, k, v, do, scale, is_causal=False):
 def attention_grads_dropout(q, k, v, do, scale, is_causal, p, seed, offset, unit):
     """Gradients of L = sum(dO * O) for the dropout forward of
     oracle/dropout.py, whose mask z (fixed by seed, offset and the unit
-    index) is a constant: O = (P * z / (1 - p)) V.  By the chain rule, with
-    W = P * z / (1 - p):
+    index) is a constant: O = (P * z / kappa) V, kappa the keep probability
+    T / 65536 of that module.  By the chain rule, with W = P * z / kappa:
         dV    = W^T dO
-        dW    = dO V^T,  dP = dW * z / (1 - p)
+        dW    = dO V^T,  dP = dW * z / kappa
         dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
         dQ    = scale dS K,  dK = scale dS^T Q
     (sum_j' P_ij' dP_ij' = <dO_i, O_i>, as without dropout.)"""
-    from .dropout import keep_mask
+    from .dropout import keep_mask, keep_probability
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     P = _probs(q, k, scale, is_causal)
-    zr = keep_mask(q.shape[0], k.shape[0], unit, p, seed, offset) / (1.0 - float(np.float32(p)))
+    zr = keep_mask(q.shape[0], k.shape[0], unit, p, seed, offset) / keep_probability(p)
     dv = (P * zr).T @ do
     dp = (do @ v.T) * zr
     ds = P * (dp - np.sum(P * dp, axis=1, keepdims=True))

@@ -63,7 +63,8 @@ def test_no_device_is_reported(lib):
     assert call(lib) == DEVICE
 
 
-@pytest.mark.parametrize("pd,status", [(1.0, INVALID), (-0.5, INVALID), (float("nan"), INVALID)])
+@pytest.mark.parametrize("pd,status", [(1.0, INVALID), (-0.5, INVALID), (float("nan"), INVALID),
+                                       (1 - 2 ** -18, UNSUPPORTED)])
 def test_invalid_dropout_rate_rejected_on_host(lib, pd, status):
     a = BASE
     st = lib.sdpa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], a["dq"], a["dk"],

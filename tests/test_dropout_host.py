@@ -28,6 +28,9 @@ def call(lib, B=2, H=4, Nq=128, Nk=128, d=64, scale=0.125, causal=0, p=0.1, seed
     (dict(p=1.0), INVALID), (dict(p=-0.1), INVALID), (dict(p=float("nan")), INVALID),
     (dict(p=1.5), INVALID), (dict(q=None), INVALID), (dict(B=0), INVALID),
     (dict(dt=F32), UNSUPPORTED), (dict(d=48), UNSUPPORTED),
+    # 1 - p below 2^-17: the 16-bit keep threshold rounds to 0, nothing
+    # would be kept
+    (dict(p=float(1 - 2 ** -18)), UNSUPPORTED), (dict(p=float(1 - 2 ** -20)), UNSUPPORTED),
 ])
 def test_invalid_dropout_calls_rejected_on_host(lib, kw, status):
     assert call(lib, **kw) == status

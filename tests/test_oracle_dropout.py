@@ -16,7 +16,8 @@ Dropout:
 * the keep rate and the 16-bit numbers' distribution match the contract
   within binomial / chi-square bounds;
 * p = 0 is the dense oracle exactly; lse never depends on the mask;
-* a single key gives O = z v / (1 - p);
+* a single key gives O = z v / kappa, kappa = floor((1 - p) 65536 + 1/2) / 65536
+  (the keep probability actually drawn), which differs from 1 - p at p = 0.3;
 * averaged over many seeds, O is unbiased (mean = dense O within 5
   standard errors);
 * packed sequences are per-sequence dense units with u = s*H + h;
@@ -166,8 +167,10 @@ def test_single_key():
     p = 0.3
     o, l = D.sdpa_fwd_dropout(q, k, v, 0.5, False, p, 11)
     z = D.keep_mask(20, 1, 0, p, 11, 0)
-    want = z * v[0, 0, 0][None, :] / (1 - np.float32(p))
-    np.testing.assert_allclose(o[0, 0], want, rtol=1e-12)
+    kappa = math.floor((1.0 - float(np.float32(p))) * 65536.0 + 0.5) / 65536.0
+    assert abs(kappa - 0.7) > 1e-6       # the pin tells kappa from 1 - p
+    want = z * v[0, 0, 0][None, :] / kappa
+    np.testing.assert_allclose(o[0, 0], want, rtol=1e-13)
     np.testing.assert_allclose(l[0, 0], 0.5 * (q[0, 0] @ k[0, 0, 0]), rtol=1e-12)
     assert 0 < z.sum() < 20
 
@@ -222,7 +225,7 @@ def _mutant(q, k, v, scale, causal, p, seed, mistake):
         P = e * z / np.maximum((e * z).sum(axis=1, keepdims=True), 1e-300)
         return P @ v
     P = e / e.sum(axis=1, keepdims=True)
-    keep = float(np.float32(p)) if mistake == "scaled_by_p" else 1 - float(np.float32(p))
+    keep = float(np.float32(p)) if mistake == "scaled_by_p" else t / 65536.0
     return (P * z / keep) @ v
 
 

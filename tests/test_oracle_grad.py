@@ -179,7 +179,8 @@ def test_dropout_rowsum_identity():
     from oracle import dropout as odrop
     q, k, v, do = _rand((7, 4), 61), _rand((9, 4), 62), _rand((9, 4), 63), _rand((7, 4), 64)
     P = grad._probs(q, k, 0.5, False)
-    zr = odrop.keep_mask(7, 9, 2, 0.4, 8, 1) / (1.0 - float(np.float32(0.4)))
+    kappa = np.floor((1.0 - float(np.float32(0.4))) * 65536.0 + 0.5) / 65536.0
+    zr = odrop.keep_mask(7, 9, 2, 0.4, 8, 1) / kappa
     o, _ = odrop.attend_dropout(q, k, v, 0.5, False, 0.4, 8, 1, 2)
     np.testing.assert_allclose(np.sum(P * (do @ v.T) * zr, axis=1), np.sum(do * o, axis=1),
                                rtol=1e-12, atol=1e-12)
