@@ -300,7 +300,13 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     odt = q.dtype if out_dtype is None else out_dtype
     if odt not in (q.dtype, torch.float32):
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
-    out = torch.empty(q.shape, dtype=odt, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    elif (tuple(out.shape) != tuple(q.shape) or out.dtype != odt or out.device != q.device
+          or not out.is_contiguous() or out.data_ptr() % 16 != 0):
+        # packed, 3-D, f32, block-sparse and dropout calls write a contiguous
+        # output of the query's shape; any other buffer is refused
+        raise SdpaError(SDPA_ERR_INVALID)
     squeeze = False
     if cu_seqlens is not None:
         if q.dim() != 3 or max_seqlen is None:
