@@ -53,7 +53,7 @@ struct BwdParams {
   float rc;               // 1 / c
   float scale;
   // dropout (the forward's Philox contract): key, last counter word, keep
-  // threshold on the 16-bit numbers, 1 / (1 - p)
+  // threshold on the 16-bit numbers, 65536 / T (the inverse keep probability)
   uint32_t seed_lo, seed_hi, drop_offset, drop_t;
   float drop_scale;
   // elementwise mask (dense layouts): element (b, h, i, j) at
@@ -161,8 +161,9 @@ __device__ __forceinline__ float mask_bias2(uint32_t word, int half) {
   return __uint_as_float(word) * 1.4426950408889634f;
 }
 
-// 1/(1-p) if the 16-bit number u is below the keep threshold, else 0: the
-// sign of u - T (T <= 65536) selects the bits of the scale.
+// 65536/T (the inverse keep probability) if the 16-bit number u is below
+// the keep threshold T, else 0: the sign of u - T (T <= 65536) selects the
+// bits of the scale.
 __device__ __forceinline__ float keep_scale(uint32_t u, uint32_t t, float rp) {
   const uint32_t m = (uint32_t)((int32_t)(u - t) >> 31);
   return __uint_as_float(__float_as_uint(rp) & m);

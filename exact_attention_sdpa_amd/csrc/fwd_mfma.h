@@ -103,7 +103,7 @@ struct MfmaParams {
   int bm_nqb, bm_nkb;  // mask rows and columns
   // dropout launches: keep (query i, key j) of unit u iff a 16-bit number
   // of Philox4x32-10(key = seed, counter = (n(j), i, u, offset)) is below
-  // drop_t; kept weights are scaled by drop_scale = 1 / (1 - p)
+  // drop_t; kept weights are scaled by drop_scale = 65536 / drop_t
   uint32_t seed_lo, seed_hi, drop_offset, drop_t;
   float drop_scale;
   // elementwise-mask launches: mask element (b, h, i, j) at
@@ -544,7 +544,7 @@ struct MfmaFwd {
   // 2(w&1)+1): exactly the 8 keys of Philox call n = kb0/8 + 2 hs + hl of
   // row i, whose output word w carries their two 16-bit numbers (low half
   // = first key of the pair).  The row sums keep the undropped P; the
-  // 1/(1-p) scale is applied to O at the end.
+  // 65536/T scale is applied to O at the end.
   static __device__ __forceinline__ void drop_block(u32x4 (&pf)[NB][2], int kb0, const Ctx& x) {
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {

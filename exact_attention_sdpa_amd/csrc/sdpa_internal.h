@@ -32,7 +32,7 @@ struct FwdArgs {
   uint64_t drop_seed;       // Philox key
   uint32_t drop_offset;     // last Philox counter word
   uint32_t drop_t;          // keep iff the 16-bit number < drop_t
-  float drop_scale;         // 1 / (1 - p)
+  float drop_scale;         // 65536 / drop_t, the inverse keep probability
   const void* amask;        // elementwise mask, or null
   int amask_kind;           // sdpa_mask_kind
   int64_t am_str[3];        // mask (batch, head, row) strides, elements
@@ -112,8 +112,9 @@ sdpa_status validate_bwd_block_mask(const uint8_t* mask, int64_t mask_heads, Bwd
 sdpa_status validate_bwd_dropout(float p, uint64_t seed, uint32_t offset, BwdArgs* a);
 
 // Adds dropout to validated forward arguments: 0 <= p < 1 (p = 0 leaves the
-// plain kernel), f16/bf16 inputs; the keep threshold floor((1-p) 65536 + 1/2)
-// and the scale 1/(1-p) are computed here, in double.
+// plain kernel), f16/bf16 inputs; the keep threshold T = floor((1-p) 65536 +
+// 1/2) and the scale 65536 / T are computed here, in double (T = 0 is
+// refused as unsupported).
 sdpa_status validate_dropout(float p, uint64_t seed, uint32_t offset, FwdArgs* a);
 
 // Host-only checks of a packed-batch backward call (q, k, v, out, dout,
@@ -135,6 +136,10 @@ sdpa_status validate_bwd(const void* q, const void* k, const void* v, const void
 
 // 1 = matrix-core path, 0 = plain f32 path, -1 = unsupported.
 int path_for(sdpa_dtype dtype, int64_t d);
+
+// True if the calling thread's current HIP device is a gfx950 (cached per
+// device after the first query).
+bool current_device_is_gfx950();
 
 // Kernel launchers: queue the kernel on a.stream and return the launch status.
 hipError_t launch_fwd_mfma_f16(const FwdArgs& a);

@@ -213,17 +213,21 @@ SDPA_API sdpa_status sdpa_fwd_block_sparse(const void* q, const void* k, const v
 /* Forward with dropout on the attention weights (the SDPA tutorial's
  * CausalSelfAttention passes its dropout rate to the functional call in
  * training).  Each softmax weight P_ij is kept with probability 1 - p and
- * kept weights are divided by 1 - p:
- *     O_i = sum_j P_ij z_ij / (1 - p) v_j;   lse as sdpa_fwd (undropped).
+ * kept weights are divided by the keep probability kappa:
+ *     O_i = sum_j P_ij z_ij / kappa v_j;   lse as sdpa_fwd (undropped).
  * z comes from Philox4x32-10 (Salmon et al., SC 2011), key = (seed low 32
  * bits, seed high 32 bits), counter = (n(j), i, u, offset) with
  * u = b*H + h (packed: sequence*H + h, i counted from the sequence start),
  * n(j) = 2*(j >> 4) + ((j >> 2) & 1); the 16-bit half e(j) =
  * 4*((j >> 3) & 1) + (j & 3) of the output (word e >> 1, bits 16*(e & 1)..)
- * is compared with T = floor((1 - p) * 65536 + 1/2): kept iff below.  The
- * same (seed, offset) gives the same mask on every call.
+ * is compared with T = floor((1 - p) * 65536 + 1/2): kept iff below, so
+ * kappa = T / 65536 (1 - p to within 2^-17), and the expected output is the
+ * undropped one.  The same (seed, offset) gives the same mask on every
+ * call.
  *
- * dropout_p  0 <= p < 1 (else SDPA_ERR_INVALID); p = 0 is exactly sdpa_fwd.
+ * dropout_p  0 <= p < 1 (else SDPA_ERR_INVALID); p = 0 is exactly sdpa_fwd;
+ *           a p that rounds T to 0 (1 - p below 2^-17) keeps nothing and
+ *           returns SDPA_ERR_UNSUPPORTED.
  * seed, offset  as above.
  * Other arguments as sdpa_fwd; dtype SDPA_F16 or SDPA_BF16 (SDPA_F32:
  * SDPA_ERR_UNSUPPORTED).
@@ -273,9 +277,9 @@ SDPA_API sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const
                               sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
 
 /* Backward pass of sdpa_fwd_dropout: the gradients of sum(dO * O) where
- * O = sum_j P_ij z_ij / (1 - p) v_j and the mask z is the one the forward
+ * O = sum_j P_ij z_ij / kappa v_j and the mask z is the one the forward
  * drew (it is regenerated from the same dropout_p, seed and offset, never
- * stored).  With W = P z / (1 - p): dV = W^T dO, dP = (dO V^T) z / (1 - p),
+ * stored).  With W = P z / kappa: dV = W^T dO, dP = (dO V^T) z / kappa,
  * dS = P (dP - <dO, O>), dQ = scale dS K, dK = scale dS^T Q.  `out` and
  * `lse` are the dropout forward's.  Arguments otherwise as sdpa_bwd;
  * 0 <= dropout_p < 1 (else SDPA_ERR_INVALID), p = 0 is exactly sdpa_bwd.
