@@ -302,3 +302,31 @@ def test_unsupported_raises():
         S.scaled_dot_product_attention(q32h, q32h, q32h,
                                        attn_mask=torch.ones(7, 8, dtype=torch.bool,
                                                             device="cuda"))
+
+
+def test_out_buffer_is_written_or_refused():
+    """out= on the general path (here f32 inputs, a 3-D tensor and a packed
+    batch): a matching contiguous buffer is written and returned; any other
+    buffer is refused rather than silently replaced."""
+    import exact_attention_sdpa_amd as S
+    w = inputs.make_dense(2, 1, 40, 40, 16, "f32", "normal", True, seed=13, cfg=113)
+    q, k, v = (G.to_device(x, "f32")[:, 0] for x in (w.q, w.k, w.v))   # [B, N, d]
+    buf = torch.full(q.shape, 9.0, device="cuda")
+    res = S.scaled_dot_product_attention(q, k, v, is_causal=True, scale=float(w.scale), out=buf)
+    torch.cuda.synchronize()
+    assert res.data_ptr() == buf.data_ptr()
+    ref, _ = _dense_ref(w)
+    G.assert_parity(buf.double().cpu().numpy(), ref[:, 0], "f32", "out= f32 3-D")
+    wv = inputs.make_varlen([5, 0, 33], 2, 32, "f16", "normal", False, seed=14, cfg=113)
+    qv, kv, vv = (G.to_device(x, "f16") for x in (wv.q, wv.k, wv.v))
+    cu = torch.from_numpy(wv.cu_seqlens).cuda()
+    pbuf = torch.zeros(qv.shape, dtype=torch.float16, device="cuda")
+    S.scaled_dot_product_attention(qv, kv, vv, cu_seqlens=cu, max_seqlen=33, out=pbuf)
+    torch.cuda.synchronize()
+    pref, _ = oracle.sdpa_fwd_varlen(wv.q64, wv.k64, wv.v64, wv.cu_seqlens, wv.scale, False)
+    G.assert_parity(pbuf.double().cpu().numpy(), pref, "f16", "out= packed")
+    for bad in (torch.empty(q.shape, dtype=torch.float16, device="cuda"),          # dtype
+                torch.empty((2, 41, 16), device="cuda"),                           # shape
+                torch.empty((2, 16, 40), device="cuda").transpose(1, 2)):          # layout
+        with pytest.raises(S.SdpaError):
+            S.scaled_dot_product_attention(q, k, v, is_causal=True, out=bad)
