@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_MASK_ADD, SDPA_MASK_ADD_F32, SDPA_MASK_BOOL, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -135,6 +135,20 @@ def sdpa_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, sc
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), int(B), int(H),
                              int(Nq), int(Nk), int(d), float(scale), int(is_causal), int(dtype),
                              int(out_dtype), int(grad_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, B, H, Nq, Nk, d, scale, is_causal,
+                     dtype, out_dtype, grad_dtype, stream):
+    """Call the allocation-free backward entry point (sdpa_bwd without a
+    workspace: the row dots live in the library's per-device array)."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = _lib.lib().sdpa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H), int(Nq),
+                                     int(Nk), int(d), float(scale), int(is_causal), int(dtype),
+                                     int(out_dtype), int(grad_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 

@@ -12,10 +12,11 @@ SDPA_F16, SDPA_BF16, SDPA_F32, SDPA_SAME = 0, 1, 2, 255
 SDPA_OK, SDPA_ERR_INVALID, SDPA_ERR_UNSUPPORTED, SDPA_ERR_LAUNCH, SDPA_ERR_DEVICE = range(5)
 SDPA_BLOCK_SPARSE_BLOCK = 128
 SDPA_MASK_BOOL, SDPA_MASK_ADD, SDPA_MASK_ADD_F32 = 0, 1, 2
+SDPA_BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024
 
 # every symbol include/sdpa.h declares
 EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
-           "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
+           "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 _lib = None
 
@@ -70,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.sdpa_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                         i64, i64, ctypes.c_float, ctypes.c_int, vp, i64,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_bwd_noalloc.restype = ctypes.c_int
+    L.sdpa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, vp]
     L.sdpa_bwd_workspace_bytes.restype = i64
     L.sdpa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     L.sdpa_supports.restype = ctypes.c_int

@@ -10,6 +10,10 @@ constexpr int kMaxDevices = 64;
 // per device: 0 = not yet checked, 1 = gfx950, 2 = anything else
 std::atomic<int> g_arch[kMaxDevices];
 
+}  // namespace
+
+namespace sdpa {
+
 bool current_device_is_gfx950() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
@@ -23,7 +27,9 @@ bool current_device_is_gfx950() {
   return st == 1;
 }
 
-}  // namespace
+}  // namespace sdpa
+
+using sdpa::current_device_is_gfx950;
 
 extern "C" {
 

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 10
+#define SDPA_ABI_VERSION 11
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -371,6 +371,32 @@ SDPA_API sdpa_status sdpa_bwd_packed(const void* q, const void* k, const void* v
                                      float dropout_p, uint64_t seed, uint32_t offset,
                                      sdpa_dtype dtype, sdpa_dtype out_dtype,
                                      sdpa_dtype grad_dtype, void* stream);
+
+/* Largest B*H*Nq that sdpa_bwd_noalloc serves (16 MiB of floats). */
+#define SDPA_BWD_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
+
+/* sdpa_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight training loops, harnesses that forbid hipMalloc.
+ * The same gradients, bit for bit, as sdpa_bwd; the B*H*Nq row dots that
+ * sdpa_bwd keeps in the caller's workspace live in a fixed device array
+ * that the library holds, one copy per device, until the process ends.
+ *
+ * Arguments as sdpa_bwd without `workspace`.  The call allocates and frees
+ * nothing and calls no allocating library routine.  Every call on one
+ * device shares that device's array, so calls that overlap in time on one
+ * device (e.g. on two streams) race and give undefined results; calls on
+ * one stream, or on different devices, do not.
+ *
+ * Returns as sdpa_bwd, and SDPA_ERR_UNSUPPORTED when B*H*Nq exceeds
+ * SDPA_BWD_NOALLOC_MAX_ROWS (checked before any device work); the size
+ * limits are checked first, so an oversized call is refused even without a
+ * device. */
+SDPA_API sdpa_status sdpa_bwd_noalloc(const void* q, const void* k, const void* v,
+                                      const void* out, const void* dout, const float* lse,
+                                      void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                                      int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                      int is_causal, sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                      sdpa_dtype grad_dtype, void* stream);
 
 /* Bytes of the workspace sdpa_bwd needs (B*H*Nq floats), or -1 if the sizes
  * overflow.  Pure host function. */

@@ -88,3 +88,22 @@ def test_block_sparse_backward_rejected_on_host():
     assert call(heads=3) == INVALID_
     assert call(dt=2) == UNSUP_
     assert call(mask=DQ) == INVALID_        # overlaps an output
+
+
+def test_noalloc_backward_refuses_sizes_beyond_its_array(lib):
+    """sdpa_bwd_noalloc checks the size against its fixed array before any
+    device call: B*H*Nq above SDPA_BWD_NOALLOC_MAX_ROWS is unsupported,
+    non-positive sizes are invalid."""
+    a = BASE
+    rows = _lib.SDPA_BWD_NOALLOC_MAX_ROWS
+
+    def call(B, H, Nq):
+        return lib.sdpa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], a["dq"],
+                                    a["dk"], a["dv"], B, H, Nq, 128, 64, 0.125, 0, F16, SAME,
+                                    SAME, None)
+
+    assert call(1, 1, rows + 1) == UNSUPPORTED
+    assert call(2, 16, rows // 16) == UNSUPPORTED
+    assert call(2 ** 40, 2 ** 40, 2 ** 40) == INVALID     # the byte count overflows
+    assert call(0, 1, 128) == INVALID
+    assert call(1, 1, 0) == INVALID
