@@ -7,7 +7,9 @@ A step is one call of the whole forward (sdpa_fwd) over one batch of
 synthetic input already resident in device memory.  The default workload is
 the one the headline metric is quoted on: B=32, H=32, N=1024, d=32, f16,
 uniform [0,1) inputs, non-causal (the PyTorch SDPA tutorial's dispatcher
-benchmark).  Prints one JSON line.
+benchmark).  Prints one JSON line.  The default run also times, after the
+headline's timed region, the two d = 64 causal workloads (B32 H8 N1024 f16
+and B1 H16 N65536 bf16) under ``targets``, each with the same event method.
 
 Throughput counts 4*B*H*Nq*Nk*d FLOPs per step (halved when causal; summed
 per sequence for packed batches; 4*d per visible (query, key) pair for the
@@ -528,6 +530,8 @@ def main(argv=None) -> int:
     ap.add_argument("--calibrate-gemm", action="store_true",
                     help="run only square 8192 fp16/bf16 GEMMs through the vendor BLAS, "
                          "an attainable matrix-core rate for reference")
+    ap.add_argument("--no-targets", dest="targets", action="store_false",
+                    help="skip timing the causal and long workloads after the headline")
     ap.add_argument("--summarize", action="store_true",
                     help="summarize rocprofv3 CSV outputs into profiles/ (no GPU needed)")
     ap.add_argument("--trace-dir")
@@ -766,6 +770,13 @@ def main(argv=None) -> int:
     }
     if a.which == "bwd":
         rec["kernels"] = "rowdot + dq + dkdv (kernel_ms spans all three)"
+    if a.targets and a.which == "fwd" and a.workload == "noncausal" and a.dropout == 0:
+        # the two d = 64 causal workloads the 50%-of-peak target names, timed
+        # after the headline's timed region (never inside it)
+        del q, k, v, out, lse
+        rec["targets"] = {
+            "causal": time_target(torch, sdpa, inputs, np, "causal", max(a.steps, 20), 5),
+            "long": time_target(torch, sdpa, inputs, np, "long", max(3, min(a.steps, 10)), 2)}
     if a.cpu_budget > 0:
         rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget, a.dropout) if a.which == "fwd"
                                else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload],
@@ -774,6 +785,50 @@ def main(argv=None) -> int:
         rec["cpu_baseline"]["cpu_model"] = _cpu_model()
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def time_target(torch, sdpa, inputs, np, name, steps, warmup):
+    """Warm kernel time of one more workload, measured like the headline:
+    ``steps`` back-to-back sdpa_fwd launches between two HIP events on the
+    launch stream, after ``warmup`` launches.  bf16 inputs take an f32
+    output, as in the headline run's rule."""
+    w = inputs.make_config(WORKLOADS[name])
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    q, k, v = up(w.q), up(w.k), up(w.v)
+    out_f32 = w.dtype == "bf16"
+    out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device="cuda")
+    lse = torch.empty(tuple(q.shape[:3]), dtype=torch.float32, device="cuda")
+    dt = {"f16": sdpa.SDPA_F16, "bf16": sdpa.SDPA_BF16}[w.dtype]
+    stream = torch.cuda.current_stream()
+    L = sdpa._lib.lib()
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), w.B, w.H,
+            w.Nq, w.Nk, w.d, float(w.scale), int(w.is_causal), None, dt,
+            sdpa.SDPA_F32 if out_f32 else sdpa.SDPA_SAME, stream.cuda_stream]
+
+    def step():
+        st = L.sdpa_fwd(*args)
+        if st != 0:
+            raise sdpa.SdpaError(st)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = w.flops() / (ms * 1e-3) / 1e12
+    return {"workload": describe(w, name)["workload"], "kernel_ms": round(ms, 4),
+            "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS, 4),
+            "steps": steps}
 
 
 def _cpu_model() -> str:

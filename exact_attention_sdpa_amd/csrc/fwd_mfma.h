@@ -15,9 +15,10 @@
 //            XCDs (dispatched round-robin) owns a contiguous range of tiles,
 //            and the tiles of one head run back to back on one XCD, sharing
 //            K/V in that XCD's L2.  Causal dense grids of up to 16 query
-//            tiles per head instead run every head's heaviest query tile
-//            first, then the next heaviest, and so on (longest-processing-
-//            time order), each XCD keeping its own heads.
+//            tiles per head instead give one workgroup the pair of tiles
+//            n-1-i and i (heavy first), so every workgroup sweeps the same
+//            number of key tiles, and the pairs of a head sweep its keys
+//            together on one XCD.
 //   waves    NW waves; wave w owns NB blocks of 32 query rows.
 //   tile     BN keys per step, read with buffer loads whose range check
 //            returns zeros past the last key, staged through double-buffered
@@ -95,6 +96,7 @@ struct MfmaParams {
   int q_rs, kv_rs, o_rs;
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
+  int paired;          // causal dense: tiles n-1-i and i share a workgroup
   float c;             // scale * log2(e), at least 1e-30
   // block-sparse launches: mask [Hm][ceil(Nq/128)][ceil(Nk/128)], nonzero =
   // the 128x128 block of (query, key) pairs is visible
@@ -137,7 +139,12 @@ enum FwdVariant : int {
 #ifndef SDPA_MASK_SKIP
 #define SDPA_MASK_SKIP 1
 #endif
-// Build option: causal dense grids in longest-processing-time order.
+// Build option: causal dense grids of up to 16 query tiles per head run
+// tiles n-1-i and i in one workgroup.
+#ifndef SDPA_CAUSAL_PAIR
+#define SDPA_CAUSAL_PAIR 1
+#endif
+// Build option: otherwise, such grids in longest-processing-time order.
 #ifndef SDPA_CAUSAL_LPT
 #define SDPA_CAUSAL_LPT 1
 #endif
@@ -567,119 +574,150 @@ struct MfmaFwd {
     }
   }
 
-  // One tile, one block of 32 keys at a time: the products S(kk+1) are
-  // issued before the softmax of block kk (they do not depend on it) and
-  // P V of block kk after it.
-  //   t = s*c - m (one fma per score), P = exp2(t).
+  // ---- softmax of one 32-key block, in three parts
+  //   prep   masking and, where the kernel has no reference yet, setting it
+  //          (may branch)
+  //   body   t = s*c - m (one fma per score; folded into the mask's bias for
+  //          elementwise masks), P = exp2(t), the lane's fp32 sums and the
+  //          f16 B operands of P V (straight-line vector code)
+  //   fix    the lane-sum check and its rare redo, dropout (may branch)
   // The first block of the first tile sets m to its row maximum (finite:
   // key 0 is visible to every row).  After that no row maximum is taken:
   // each P is at most its lane's block sum, so one compare per block proves
   // that no f16 P can overflow.  A lane over the limit (rare) raises its
   // row to the block maximum, O and l are rescaled in place, and the
   // block's exponentials are redone.
+
+  static __device__ __forceinline__ void softmax_prep(f32x16 (&sc)[NB], int kk, int kb, bool first,
+                                                      bool masked, const Ctx& x, State& S,
+                                                      const MaskRegs& mr) {
+    if (masked && !MASK) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+    if (MASK) {
+      // the mask's bias is folded into the scaled scores first; pairs the
+      // causal rule or the key tail excludes are then set to -inf whatever
+      // the mask holds there.  A row's reference is set by the first block
+      // in which it has a finite score.
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        const float mref = S.m[qb] == -INFINITY ? 0.f : S.m[qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][r] = mask_score(sc[qb][r], x.c, mref, mr.w[kk][qb], r);
+      }
+      if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+      bool unset = false;
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float mm = row_max(sc[qb]);
+          const bool set_now = S.m[qb] == -INFINITY && mm > -INFINITY;
+          const float sub = set_now ? mm : 0.f;
+          if (set_now) S.m[qb] = mm;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[qb][r] -= sub;
+        }
+      }
+    } else if (BSP) {
+      // block-sparse: a row's reference is set by the first block in
+      // which it sees a key (its first visible block can be anywhere)
+      bool unset = false;
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float mm = row_max(sc[qb]) * x.c;
+          if (S.m[qb] == -INFINITY) S.m[qb] = mm;
+        }
+      }
+    } else if (kk == 0 && first) {
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
+    }
+  }
+
+  static __device__ __forceinline__ void softmax_body(f32x16 (&sc)[NB], const Ctx& x,
+                                                      const State& S, float (&bs)[NB][2],
+                                                      u32x4 (&pf)[NB][2]) {
+    if (!MASK) {
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        // rows that have not seen a key yet have only -inf scores here
+        const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
+      }
+    }
+    exp_block(sc, bs, pf);
+  }
+
+  static __device__ __forceinline__ void softmax_fix(f32x16 (&sc)[NB], int kk, int kb,
+                                                     const Ctx& x, State& S, float (&bs)[NB][2],
+                                                     u32x4 (&pf)[NB][2]) {
+    bool over = false;
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) over = over || !(bs[qb][0] + bs[qb][1] <= kLaneSumLimit);
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        // rows with nothing to raise take y = 0 (a no-op), so no per-lane
+        // branch splits the accumulators' live ranges
+        const float y = fmaxf(row_max(sc[qb]), 0.f);
+        const float alpha = __builtin_amdgcn_exp2f(-y);
+        S.m[qb] += y;
+        S.l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[qb][r] -= y;
+      }
+      exp_block(sc, bs, pf);
+    }
+    if (DROP) drop_block(pf, kb + kk * 32, x);
+#pragma unroll
+    for (int qb = 0; qb < NB; ++qb) S.l[qb] += bs[qb][0] + bs[qb][1];
+  }
+
+  // O^T += V^T P^T for key block kk of the tile in LDS V buffer `buf`.
+  static __device__ __forceinline__ void pv(State& S, const Smem& sm, int buf, int kk,
+                                            const Lanes& ln, const u32x4 (&pf)[NB][2]) {
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 vf =
+            *reinterpret_cast<const u32x4*>(&sm.vt[buf][ln.vl[hs] + db * 32 * VRW + 16 * kk]);
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) S.o[qb][db] = mfma_f16(vf, pf[qb][hs], S.o[qb][db]);
+      }
+  }
+
+  // One tile, one block of 32 keys at a time: the products S(kk+1) are
+  // issued before the softmax of block kk (they do not depend on it) and
+  // P V of block kk right after it.
   static __device__ __forceinline__ void tile(const Smem& sm, int buf, int kb, bool first,
                                               bool masked, const Ctx& x, const u32x4 (&qf)[NB][DS],
                                               State& S, const MaskRegs& mr) {
-    f32x16 sc[NB], sn[NB];
+    f32x16 sc[NB];
     scores(sc, sm, buf, 0, x.ln, qf);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-      const bool pending = kk + 1 < KB;
-      if (masked && !MASK) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
-      if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf);
-      if (MASK) {
-        // the mask's bias is folded into the scaled scores first; pairs the
-        // causal rule or the key tail excludes are then set to -inf whatever
-        // the mask holds there.  A row's reference is set by the first block
-        // in which it has a finite score.
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          const float mref = S.m[qb] == -INFINITY ? 0.f : S.m[qb];
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sc[qb][r] = mask_score(sc[qb][r], x.c, mref, mr.w[kk][qb], r);
-        }
-        if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
-        bool unset = false;
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
-        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) {
-            const float mm = row_max(sc[qb]);
-            const bool set_now = S.m[qb] == -INFINITY && mm > -INFINITY;
-            const float sub = set_now ? mm : 0.f;
-            if (set_now) S.m[qb] = mm;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[qb][r] -= sub;
-          }
-        }
-      } else if (BSP) {
-        // block-sparse: a row's reference is set by the first block in
-        // which it sees a key (its first visible block can be anywhere)
-        bool unset = false;
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
-        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) {
-            const float mm = row_max(sc[qb]) * x.c;
-            if (S.m[qb] == -INFINITY) S.m[qb] = mm;
-          }
-        }
-      } else if (kk == 0 && first) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
-      }
-      if (!MASK) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          // rows that have not seen a key yet have only -inf scores here
-          const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
-        }
-      }
+      f32x16 sn[NB];
       float bs[NB][2];
       u32x4 pf[NB][2];
-      exp_block(sc, bs, pf);
-      bool over = false;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) over = over || !(bs[qb][0] + bs[qb][1] <= kLaneSumLimit);
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          // rows with nothing to raise take y = 0 (a no-op), so no per-lane
-          // branch splits the accumulators' live ranges
-          const float y = fmaxf(row_max(sc[qb]), 0.f);
-          const float alpha = __builtin_amdgcn_exp2f(-y);
-          S.m[qb] += y;
-          S.l[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[qb][r] -= y;
-        }
-        exp_block(sc, bs, pf);
-      }
-      if (DROP) drop_block(pf, kb + kk * 32, x);
+      if (kk + 1 < KB) scores(sn, sm, buf, kk + 1, x.ln, qf);
+      softmax_prep(sc, kk, kb, first, masked, x, S, mr);
+      softmax_body(sc, x, S, bs, pf);
+      softmax_fix(sc, kk, kb, x, S, bs, pf);
       if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(
-              &sm.vt[buf][x.ln.vl[hs] + db * 32 * VRW + 16 * kk]);
-#pragma unroll
-          for (int qb = 0; qb < NB; ++qb) S.o[qb][db] = mfma_f16(vf, pf[qb][hs], S.o[qb][db]);
-        }
+      pv(S, sm, buf, kk, x.ln, pf);
       if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      if (kk + 1 < KB) {
 #pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        S.l[qb] += bs[qb][0] + bs[qb][1];
-        if (pending) sc[qb] = sn[qb];
+        for (int qb = 0; qb < NB; ++qb) sc[qb] = sn[qb];
       }
     }
   }
@@ -730,17 +768,25 @@ struct MfmaFwd {
   }
 
   static __device__ void run(const MfmaParams& p, Smem& sm) {
-    Ctx x;
-    x.tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
-    const int lane = x.tid % 64;
-    x.hl = lane / 32;
-    x.l32 = lane % 32;
-    x.c = p.c;
-
-    // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
-    int qt, bh;
-    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
+    // ---- which tile(s): XCD-contiguous ranges; causal: heaviest tiles first
+    int qt, bh, qt2 = -1;
+    if (CAUSAL && !VARLEN && !BSP && p.paired) {
+      // causal, short sequences: query tile n-1-i and tile i of one head
+      // share a workgroup (heavy one first), so every workgroup sweeps the
+      // same number of key tiles (n+1 tile widths); the pairs of one head
+      // are consecutive and so stay on one XCD, where they sweep the head's
+      // keys together through its L2
+      const int npair = (p.n_qtiles + 1) / 2;
+      int idx = blockIdx.x;
+      if ((p.total & 7) == 0) {
+        const int per = p.total >> 3;
+        idx = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+      }
+      bh = idx / npair;
+      const int pr = idx % npair;
+      qt = p.n_qtiles - 1 - pr;
+      if (pr < qt) qt2 = pr;   // the middle tile of an odd count runs alone
+    } else if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
       // causal, short sequences: every head's heaviest query tiles first,
       // then the next heaviest of every head, ... (longest-processing-time
       // order, which shortens the tail when many heads have few tiles);
@@ -769,6 +815,23 @@ struct MfmaFwd {
       bh = tile / p.n_qtiles;
       if (CAUSAL) qt = p.n_qtiles - 1 - qt;
     }
+    // one or two query tiles, one after the other (qt2 is uniform over the
+    // workgroup, so every wave reaches every barrier of both)
+    run_tile(p, sm, qt, bh);
+    if (qt2 >= 0) run_tile(p, sm, qt2, bh);
+  }
+
+  // One query tile qt of unit bh: stream its key tiles, write O and lse.
+  // Every LDS read of the tile happens before its last barrier, so a second
+  // tile may follow at once.
+  static __device__ __forceinline__ void run_tile(const MfmaParams& p, Smem& sm, int qt, int bh) {
+    Ctx x;
+    x.tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
+    const int lane = x.tid % 64;
+    x.hl = lane / 32;
+    x.l32 = lane % 32;
+    x.c = p.c;
     const int b = bh / p.H, h = bh % p.H;
 
     int nq, nk;

@@ -104,6 +104,11 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.o_rs = (int)a.o_str[2];
   p.n_qtiles = (int)((a.Nq + K::BM - 1) / K::BM);
   p.total = (int)(a.B * a.H * p.n_qtiles);
+  // causal dense grids of 2..16 query tiles per head: one workgroup per
+  // pair of tiles (n-1-i, i), equal work per workgroup
+  p.paired = CAUSAL && !VARLEN && VAR != kBlockSparse && SDPA_CAUSAL_PAIR && p.n_qtiles >= 2 &&
+             p.n_qtiles <= 16;
+  if (p.paired) p.total = (int)(a.B * a.H * ((p.n_qtiles + 1) / 2));
   // scale 0 is carried as a tiny positive multiplier: every visible score
   // becomes 0 to within 1e-30 relative, masked scores stay -inf
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
