@@ -24,8 +24,13 @@
 // column l%32.  Products whose k index comes from an accumulator use the
 // accumulator's register order as the k order, and the other operand is
 // staged permuted to match (vt_key_pos).
-// bf16 inputs: the transposed copies are converted to f16 and P and dS are
-// f16, so the last products run on the f16 matrix cores.
+// Operand types of the products dV = P^T dO, dK = Q^T dS and dQ = dS K:
+// the input type.  bf16 inputs keep the transposed copies of Q, dO and K in
+// bf16 and round P and dS to bf16, so these products run on the bf16
+// matrix cores with dO, Q and K exact and the whole bf16 exponent range
+// (upstream gradients of 1e-8 and below stay exact operands; f16 copies
+// would flush them); P and dS carry bf16's relative rounding, 2^-8.
+// f16 inputs round P and dS to f16 (2^-11).
 #pragma once
 
 #include <type_traits>
@@ -294,19 +299,25 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, int row, int col
 }
 
 // Two rows (2pr, 2pr+1) x 8 columns -> 8 words of the transposed copy: word
-// e holds (row 2pr, row 2pr+1) of column e, f16.
-template <bool BF16>
+// e holds (row 2pr, row 2pr+1) of column e, in the input type.
 __device__ __forceinline__ void store_pair_t(uint32_t* dst, int tw, u32x4 a, u32x4 b) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t x = a[w], y = b[w];
-    if (BF16) {
-      x = bf16x2_to_f16x2(x);
-      y = bf16x2_to_f16x2(y);
-    }
+    const uint32_t x = a[w], y = b[w];
     dst[(2 * w) * tw] = __builtin_amdgcn_perm(y, x, 0x05040100u);
     dst[(2 * w + 1) * tw] = __builtin_amdgcn_perm(y, x, 0x07060302u);
   }
+}
+
+// Two fp32 values packed as operands of the dV / dK / dQ products (the
+// input type, round to nearest even), and those products.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack_grad_operand(float a, float b) {
+  return BF16 ? pack_bf16(a, b) : pack_f16(a, b);
+}
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_in(u32x4 a, u32x4 b, f32x16 c) {
+  return BF16 ? mfma_bf16(a, b, c) : mfma_f16(a, b, c);
 }
 
 // Store a d-major accumulator (lane = row of the output, registers = d) of
@@ -354,7 +365,7 @@ struct BwdDq {
   struct __attribute__((aligned(16))) Buf {
     uint16_t k[BN * KROW];
     uint16_t v[BN * KROW];
-    uint32_t kt[D * TW];   // K^T, f16, keys in vt_key_pos order
+    uint32_t kt[D * TW];   // K^T (input type), keys in vt_key_pos order
   };
   struct __attribute__((aligned(16))) Smem {
     Buf b[2];
@@ -452,7 +463,7 @@ struct BwdDq {
         if (PAIRS % NT == 0 || tid + i * NT < PAIRS) {
           *reinterpret_cast<u32x4*>(&b.k[st.kl[i]]) = r.k0[i];
           *reinterpret_cast<u32x4*>(&b.k[st.kl[i] + KROW]) = r.k1[i];
-          store_pair_t<BF16>(&b.kt[st.kt[i]], TW, r.k0[i], r.k1[i]);
+          store_pair_t(&b.kt[st.kt[i]], TW, r.k0[i], r.k1[i]);
         }
 #pragma unroll
       for (int i = 0; i < VPT; ++i)
@@ -560,7 +571,7 @@ struct BwdDq {
                 d0 = __builtin_fmaf(keep_scale(rr[i] & 0xffffu, p.drop_t, p.drop_scale), dp[r], -dd);
                 d1 = __builtin_fmaf(keep_scale(rr[i] >> 16, p.drop_t, p.drop_scale), dp[r + 1], -dd);
               }
-              w[i] = pack_f16(p0 * d0, p1 * d1);
+              w[i] = pack_grad_operand<BF16>(p0 * d0, p1 * d1);
             }
             dsf[hs] = u32x4{w[0], w[1], w[2], w[3]};
           }
@@ -571,7 +582,7 @@ struct BwdDq {
             for (int db = 0; db < DB; ++db) {
               const u32x4 kta = *reinterpret_cast<const u32x4*>(
                   &b.kt[l32 * TW + hl * 4 + 8 * hs + db * 32 * TW + 16 * kk]);
-              acc[db] = mfma_f16(kta, dsf[hs], acc[db]);
+              acc[db] = mfma_in<BF16>(kta, dsf[hs], acc[db]);
             }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
         }
@@ -657,7 +668,7 @@ struct BwdDkdv {
   struct __attribute__((aligned(16))) Buf {
     uint16_t q[BQ * KROW];
     uint16_t g[BQ * KROW];     // dO rows
-    uint32_t qt[D * TW];       // Q^T, f16, queries in vt_key_pos order
+    uint32_t qt[D * TW];       // Q^T (input type), queries in vt_key_pos order
     uint32_t gt[D * TW];       // dO^T, likewise
     float nl[BQ];              // -lse * log2(e) / c; -inf past the last row
     float nd[BQ];              // -<dO_i, O_i>; 0 past the last row
@@ -763,8 +774,8 @@ struct BwdDkdv {
           *reinterpret_cast<u32x4*>(&b.q[pl[t] + KROW]) = r.q1[t];
           *reinterpret_cast<u32x4*>(&b.g[pl[t]]) = r.g0[t];
           *reinterpret_cast<u32x4*>(&b.g[pl[t] + KROW]) = r.g1[t];
-          store_pair_t<BF16>(&b.qt[ptl[t]], TW, r.q0[t], r.q1[t]);
-          store_pair_t<BF16>(&b.gt[ptl[t]], TW, r.g0[t], r.g1[t]);
+          store_pair_t(&b.qt[ptl[t]], TW, r.q0[t], r.q1[t]);
+          store_pair_t(&b.gt[ptl[t]], TW, r.g0[t], r.g1[t]);
         }
       if (tid < BQ) {
         b.nl[tid] = r.l2;
@@ -890,12 +901,13 @@ struct BwdDkdv {
                 // register r holds query 8 (r >> 2) + 4 hl + (r & 3) of the block
                 const float z0 = (zb >> (8 * (r >> 2) + (r & 3))) & 1u ? p.drop_scale : 0.f;
                 const float z1 = (zb >> (8 * (r >> 2) + (r & 3) + 1)) & 1u ? p.drop_scale : 0.f;
-                wp[e] = pack_f16(p0 * z0, p1 * z1);
-                wd[e] = pack_f16(p0 * __builtin_fmaf(z0, dp[r], ndv[r >> 2][r & 3]),
-                                 p1 * __builtin_fmaf(z1, dp[r + 1], ndv[(r + 1) >> 2][(r + 1) & 3]));
+                wp[e] = pack_grad_operand<BF16>(p0 * z0, p1 * z1);
+                wd[e] = pack_grad_operand<BF16>(
+                    p0 * __builtin_fmaf(z0, dp[r], ndv[r >> 2][r & 3]),
+                    p1 * __builtin_fmaf(z1, dp[r + 1], ndv[(r + 1) >> 2][(r + 1) & 3]));
               } else {
-                wp[e] = pack_f16(p0, p1);
-                wd[e] = pack_f16(p0 * dp[r], p1 * dp[r + 1]);
+                wp[e] = pack_grad_operand<BF16>(p0, p1);
+                wd[e] = pack_grad_operand<BF16>(p0 * dp[r], p1 * dp[r + 1]);
               }
             }
             pf[hs] = u32x4{wp[0], wp[1], wp[2], wp[3]};
@@ -909,8 +921,8 @@ struct BwdDkdv {
               const int wofs = l32 * TW + hl * 4 + 8 * hs + db * 32 * TW + 16 * kk;
               const u32x4 ga = *reinterpret_cast<const u32x4*>(&b.gt[wofs]);
               const u32x4 qa = *reinterpret_cast<const u32x4*>(&b.qt[wofs]);
-              dv[db] = mfma_f16(ga, pf[hs], dv[db]);
-              dk[db] = mfma_f16(qa, dsf[hs], dk[db]);
+              dv[db] = mfma_in<BF16>(ga, pf[hs], dv[db]);
+              dk[db] = mfma_in<BF16>(qa, dsf[hs], dk[db]);
             }
           if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
         }

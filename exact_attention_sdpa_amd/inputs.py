@@ -186,11 +186,15 @@ def make_dense(B, H, Nq, Nk, d, dtype="f16", dist="normal", is_causal=False,
                     v=to_storage(v32, dtype))
 
 
-def make_grad_out(w: Workload, seed=0, cfg=0, dist="normal") -> np.ndarray:
+def make_grad_out(w: Workload, seed=0, cfg=0, dist="normal", scale=1.0) -> np.ndarray:
     """Upstream gradient dO for workload ``w`` (the shape of its output), in
-    its storage dtype."""
+    its storage dtype; ``scale`` multiplies the float32 draws before the
+    rounding (e.g. 1e-6 for the small gradients of bf16 training)."""
     shape = (w.q.shape[0], w.q.shape[1], w.q.shape[2], w.d) if not w.varlen else w.q.shape
-    return to_storage(_draw(_rng(seed, cfg, _TID_DO), shape, dist), w.dtype)
+    g = _draw(_rng(seed, cfg, _TID_DO), shape, dist)
+    if scale != 1.0:
+        g = (g * np.float32(scale)).astype(np.float32)
+    return to_storage(g, w.dtype)
 
 
 def nested_lengths(batch: int, max_len: int, pad_fraction: float, seed=0, cfg=4) -> np.ndarray:

@@ -264,6 +264,12 @@ SDPA_API sdpa_status sdpa_fwd_dropout(const void* q, const void* k, const void* 
  *           aligned (lse and workspace: 4-byte); outputs must not overlap
  *           any input or each other.
  *
+ * Precision: every product accumulates in fp32; q, k, v and dout enter the
+ * matrix cores exactly.  P and dS are rounded to the input type before the
+ * dV, dK and dQ products (f16: relative 2^-11, with f16's subnormal range
+ * below 2^-14; bf16: relative 2^-8 over bf16's whole exponent range, so
+ * upstream gradients as small as bf16 itself holds are not flushed).
+ *
  * Returns SDPA_OK, or SDPA_ERR_INVALID / SDPA_ERR_UNSUPPORTED /
  * SDPA_ERR_DEVICE / SDPA_ERR_LAUNCH with the meanings of sdpa_fwd (f32
  * inputs and packed batches are unsupported).  Queues three kernels on

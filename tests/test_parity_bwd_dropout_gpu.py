@@ -20,6 +20,10 @@ from tests.gpu_util import to_device
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -11
+# rounding of P and dS before the dV, dK, dQ products: f16 for f16 inputs,
+# bf16 (relative 2^-8, no subnormal range in play) for bf16 inputs
+U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+U_SUBP = {"f16": 2.0 ** -25, "bf16": 0.0}
 E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}
 U_GRAD = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
@@ -60,8 +64,10 @@ def _ref_and_bound(w, do, p, seed, offset=0, grad_f32=True):
             ds_abs = np.abs(P * (dp - dd))
             e_d = np.sum(np.abs(g) * (U * (W @ np.abs(v)) + uo * np.abs(o64[b, h])),
                          axis=1, keepdims=True)
-            t = U * ds_abs + P * (e_d + E_LSE * np.abs(dp - dd))
-            bv[b, h] = ((U + E_LSE) * W).T @ np.abs(g)
+            up, us = U_P[w.dtype], U_SUBP[w.dtype]
+            vis = (P > 0).astype(np.float64)
+            t = up * ds_abs + us * vis + P * (e_d + E_LSE * np.abs(dp - dd))
+            bv[b, h] = ((up + E_LSE) * W + us * vis).T @ np.abs(g)
             bq[b, h] = sc * (t @ np.abs(k))
             bk[b, h] = sc * (t.T @ np.abs(q))
     bounds = []

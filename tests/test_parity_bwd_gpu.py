@@ -7,13 +7,14 @@ stored q, k, v and dO.
 
 Tolerance, from the arithmetic (elementwise).  q, k, v and dO are exact
 matrix-core operands and every product accumulates in fp32.  The roundings
-are: P and dS, each rounded to f16 (relative u = 2^-11) before its product
-(below 2^-14, f16's subnormal range, the error is absolute instead, at most
-U_SUB = 2^-25 per visible pair); the forward's O inside D_i = <dO_i, O_i>,
+are: P and dS, each rounded to the input type before its product (f16:
+relative u = 2^-11, and below 2^-14, f16's subnormal range, the error is
+absolute instead, at most U_SUB = 2^-25 per visible pair; bf16: relative
+u = 2^-8); the forward's O inside D_i = <dO_i, O_i>,
 whose error per element is at most
-u * sum_j P_ij |v_jc| (its own f16 P) plus u_o |O_ic| (rounding to the
+u_f * sum_j P_ij |v_jc| (its own f16 P, u_f = 2^-11) plus u_o |O_ic| (rounding to the
 output dtype), so D_i is off by at most
-    e_D,i = sum_c |dO_ic| (u (P|V|)_ic + u_o |O_ic|);
+    e_D,i = sum_c |dO_ic| (u_f (P|V|)_ic + u_o |O_ic|);
 the forward's lse, whose error e_lse (at most 1e-4, the forward's bound)
 scales P by up to e_lse; and, for gradients stored in f16/bf16, one final
 rounding (plus U_SUB for an f16 result in the subnormal range).  So, per
@@ -45,6 +46,10 @@ U_SUB = 2.0 ** -25   # half the f16 subnormal spacing
 E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}   # bf16 runs keep O in f32
 U_GRAD = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# rounding of P and dS before the dV, dK, dQ products: f16 for f16 inputs,
+# bf16 (relative 2^-8, no subnormal range in play) for bf16 inputs
+U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+U_SUBP = {"f16": 2.0 ** -25, "bf16": 0.0}
 
 
 def _run(w, do, grad_f32=True):
@@ -79,8 +84,9 @@ def _ref_and_bound(w, do, grad_f32=True):
                          axis=1, keepdims=True)
             shift = p * (e_d + E_LSE * np.abs(dp - dd))
             vis = (p > 0).astype(np.float64)
-            t = U * ds_abs + U_SUB * vis + shift
-            bv[b, h] = ((U + E_LSE) * p + U_SUB * vis).T @ np.abs(g)
+            up, us = U_P[w.dtype], U_SUBP[w.dtype]
+            t = up * ds_abs + us * vis + shift
+            bv[b, h] = ((up + E_LSE) * p + us * vis).T @ np.abs(g)
             bq[b, h] = sc * (t @ np.abs(k))
             bk[b, h] = sc * (t.T @ np.abs(q))
     bounds = []
@@ -109,6 +115,23 @@ def test_bwd_dense_ragged(dtype, d, causal):
     w = inputs.make_dense(2, 2, 160, 160, d, dtype, "normal", causal, seed=3, cfg=40)
     do = inputs.make_grad_out(w, seed=3, cfg=40)
     _check(_run(w, do), _ref_and_bound(w, do), f"{dtype} d{d} causal={causal}")
+
+
+@pytest.mark.parametrize("mag", [1e-6, 1e-9])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_bf16_small_upstream_gradients(mag, d, causal):
+    """bf16 upstream gradients far below f16's normal range stay exact
+    matrix-core operands: dq, dk and dv meet the same elementwise bound as
+    for O(1) gradients (the bound is linear in dO), and none is flushed."""
+    w = inputs.make_dense(1, 2, 200, 200, d, "bf16", "normal", causal, seed=11, cfg=43)
+    do = inputs.make_grad_out(w, seed=11, cfg=43, scale=mag)
+    got = _run(w, do)
+    ref_bound = _ref_and_bound(w, do)
+    _check(got, ref_bound, f"bf16 dO~{mag:g} d{d} causal={causal}")
+    for g, r in zip(got, ref_bound[0]):
+        rel = np.linalg.norm(g - r) / np.linalg.norm(r)
+        assert rel <= 1e-2, rel
 
 
 @pytest.mark.parametrize("nq,nk", [(100, 260), (300, 70), (33, 1), (1, 50)])

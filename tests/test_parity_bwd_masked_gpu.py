@@ -28,6 +28,10 @@ U = 2.0 ** -11
 U_SUB = 2.0 ** -25   # half the f16 subnormal spacing
 E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}   # bf16 runs keep O in f32
+# rounding of P and dS before the dV, dK, dQ products: f16 for f16 inputs,
+# bf16 (relative 2^-8, no subnormal range in play) for bf16 inputs
+U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+U_SUBP = {"f16": 2.0 ** -25, "bf16": 0.0}
 
 
 def _mask_t(m, kind, mdt):
@@ -74,9 +78,10 @@ def _check(w, got, do, m4, kind, mdt, grad_f32=True):
             e_d = np.sum(np.abs(g) * (U * (P @ np.abs(v)) + U_OUT[w.dtype] * np.abs(o)), axis=1,
                          keepdims=True)
             vis = (s > -np.inf).astype(np.float64)
-            t = U * np.abs(P * (dp - dd)) + U_SUB * vis + P * (e_d + E_LSE * np.abs(dp - dd))
+            up, us = U_P[w.dtype], U_SUBP[w.dtype]
+            t = up * np.abs(P * (dp - dd)) + us * vis + P * (e_d + E_LSE * np.abs(dp - dd))
             bounds = (sc * (t @ np.abs(k)), sc * (t.T @ np.abs(q)),
-                      ((U + E_LSE) * P + U_SUB * vis).T @ np.abs(g))
+                      ((up + E_LSE) * P + us * vis).T @ np.abs(g))
             for name, gt, r, bd in zip(("dq", "dk", "dv"), got, ref, bounds):
                 gu, ru, bu = gt[b, h], r[b, h], 2.0 * bd + 1e-30
                 if not grad_f32:

@@ -23,6 +23,10 @@ from tests.gpu_util import to_device
 pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -11
+# rounding of P and dS before the dV, dK, dQ products: f16 for f16 inputs,
+# bf16 (relative 2^-8, no subnormal range in play) for bf16 inputs
+U_P = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+U_SUBP = {"f16": 2.0 ** -25, "bf16": 0.0}
 E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}   # bf16 runs keep O in f32
 
@@ -61,8 +65,11 @@ def _unit_ref_and_bound(q, k, v, g, scale, causal, dtype, p, seed, offset, unit)
     dd = np.sum(g * o, axis=1, keepdims=True)
     e_d = np.sum(np.abs(g) * (U * (W @ np.abs(v)) + U_OUT[dtype] * np.abs(o)), axis=1,
                  keepdims=True)
-    t = U * np.abs(P * (dp - dd)) + P * (e_d + E_LSE * np.abs(dp - dd))
-    bounds = (scale * (t @ np.abs(k)), scale * (t.T @ np.abs(q)), ((U + E_LSE) * W).T @ np.abs(g))
+    up, us = U_P[dtype], U_SUBP[dtype]
+    vis = (P > 0).astype(np.float64)
+    t = up * np.abs(P * (dp - dd)) + us * vis + P * (e_d + E_LSE * np.abs(dp - dd))
+    bounds = (scale * (t @ np.abs(k)), scale * (t.T @ np.abs(q)),
+              ((up + E_LSE) * W + us * vis).T @ np.abs(g))
     return ref, [2.0 * b + 1e-30 for b in bounds]
 
 
