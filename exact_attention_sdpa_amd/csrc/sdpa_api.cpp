@@ -229,8 +229,8 @@ int64_t sdpa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
 }
 
 int sdpa_supports(sdpa_dtype dtype, int64_t d, int is_causal, int varlen) {
-  (void)is_causal;
-  (void)varlen;
+  // every supported (dtype, d) serves causal masking and packed batches
+  if ((is_causal != 0 && is_causal != 1) || (varlen != 0 && varlen != 1)) return -1;
   return sdpa::path_for(dtype, d);
 }
 

@@ -43,12 +43,17 @@ extern "C" {
 #endif
 
 /* Element types.  SDPA_SAME is only valid as an output type and means
- * "the input type". */
+ * "the input type".  Every enum of this interface spans the whole int32
+ * range (the *_RANGE_* enumerators), so that any 32-bit value a caller
+ * passes is a value of the type, which the library then checks and
+ * refuses if unknown. */
 typedef enum {
+  SDPA_DTYPE_RANGE_MIN = -2147483647 - 1,
   SDPA_F16 = 0,
   SDPA_BF16 = 1,
   SDPA_F32 = 2,
-  SDPA_SAME = 255
+  SDPA_SAME = 255,
+  SDPA_DTYPE_RANGE_MAX = 2147483647
 } sdpa_dtype;
 
 /* Status codes.  Mirrors the tutorial's convention that an unsupported
@@ -56,11 +61,13 @@ typedef enum {
  * control": a backend that cannot serve the input reports "not
  * supported"). */
 typedef enum {
+  SDPA_STATUS_RANGE_MIN = -2147483647 - 1,
   SDPA_OK = 0,
   SDPA_ERR_INVALID = 1,     /* malformed arguments (see sdpa_fwd)          */
   SDPA_ERR_UNSUPPORTED = 2, /* well-formed but outside what is implemented */
   SDPA_ERR_LAUNCH = 3,      /* the HIP runtime refused the launch          */
-  SDPA_ERR_DEVICE = 4       /* no usable gfx950 device is current          */
+  SDPA_ERR_DEVICE = 4,      /* no usable gfx950 device is current          */
+  SDPA_STATUS_RANGE_MAX = 2147483647
 } sdpa_status;
 
 /*
@@ -142,9 +149,11 @@ SDPA_API sdpa_status sdpa_fwd_strided(const void* q, const void* k, const void* 
 
 /* Element types of an elementwise attention mask (sdpa_fwd_masked). */
 typedef enum {
+  SDPA_MASK_KIND_RANGE_MIN = -2147483647 - 1,
   SDPA_MASK_BOOL = 0,    /* one byte per pair (torch.bool storage): nonzero = attend */
   SDPA_MASK_ADD = 1,     /* additive, in the input element type (f16 or bf16)    */
-  SDPA_MASK_ADD_F32 = 2  /* additive, f32                                          */
+  SDPA_MASK_ADD_F32 = 2, /* additive, f32                                          */
+  SDPA_MASK_KIND_RANGE_MAX = 2147483647
 } sdpa_mask_kind;
 
 /* Forward with an elementwise attention mask.  The SDPA tutorial's
@@ -408,15 +417,27 @@ SDPA_API sdpa_status sdpa_bwd_noalloc(const void* q, const void* k, const void* 
  * overflow.  Pure host function. */
 SDPA_API int64_t sdpa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
 
-/* 1 if (dtype, d, is_causal, varlen) is served by the matrix-core path,
- * 0 if it is served by the plain f32 path, -1 if unsupported.  Pure host
+/* Which path would serve a call, asked before making it: the SDPA
+ * tutorial's dispatcher ("Explicit dispatcher control") tries backends in
+ * turn and a backend that cannot serve an input reports "not supported";
+ * here there is one backend per input type, and this query says in
+ * advance whether sdpa_fwd would refuse.  Returns 1 if (dtype, d,
+ * is_causal, varlen) is served by the matrix-core path (f16 / bf16, d in
+ * {32, 64, 128}), 0 if by the plain f32 path (1 <= d <= 128), -1 if
+ * unsupported or if is_causal or varlen is not 0 or 1.  Causal masking and
+ * packed batches are served by every supported (dtype, d).  Pure host
  * function; touches no device. */
 SDPA_API int sdpa_supports(sdpa_dtype dtype, int64_t d, int is_causal, int varlen);
 
-/* Static string naming a status code; never NULL. */
+/* Static string naming a status code, never NULL: "ok", "invalid
+ * argument", "not supported" (the tutorial's wording for an input a backend
+ * cannot serve, "Explicit dispatcher control"), "kernel launch failed",
+ * "current device is not gfx950", or "unknown status". */
 SDPA_API const char* sdpa_status_str(sdpa_status s);
 
-/* SDPA_ABI_VERSION of the built library. */
+/* SDPA_ABI_VERSION of the built library, so that a caller built against
+ * this header can refuse a library whose entry points differ.  Bookkeeping
+ * of this interface; the pages define no versioning. */
 SDPA_API int sdpa_abi_version(void);
 
 #ifdef __cplusplus

@@ -58,6 +58,10 @@ def test_supports_matrix(lib):
             assert lib.sdpa_supports(dt, d, 1, 1) == 1
         for d in (8, 16, 48, 96, 256):
             assert lib.sdpa_supports(dt, d, 0, 0) == -1
+    # the flags are booleans; anything else is refused
+    assert lib.sdpa_supports(F16, 64, 2, 0) == -1
+    assert lib.sdpa_supports(F16, 64, 0, -1) == -1
+    assert lib.sdpa_supports(F32, 8, 1, 1) == 0
     for d in (1, 3, 8, 64, 128):
         assert lib.sdpa_supports(F32, d, 0, 0) == 0
     assert lib.sdpa_supports(F32, 129, 0, 0) == -1
