@@ -18,18 +18,34 @@ SDPA_BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024
 EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
            "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
+# the same library built with the LDS-poisoning debug option
+LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa_debug.so")
+
 _lib = None
+_lib_debug = None
 
 
 def lib() -> ctypes.CDLL:
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def lib_debug() -> ctypes.CDLL:
+    """libsdpa_debug.so: the entry points of lib() with LDS poisoning on."""
+    global _lib_debug
+    if _lib_debug is None:
+        _lib_debug = _load(LIB_DEBUG_PATH)
+    return _lib_debug
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is not built; run `python -m exact_attention_sdpa_amd.build` "
+            f"{path} is not built; run `python -m exact_attention_sdpa_amd.build` "
             "(the HIP library is required, there is no fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     L.sdpa_fwd.restype = ctypes.c_int
     L.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -83,5 +99,4 @@ def lib() -> ctypes.CDLL:
     L.sdpa_status_str.argtypes = [ctypes.c_int]
     L.sdpa_abi_version.restype = ctypes.c_int
     L.sdpa_abi_version.argtypes = []
-    _lib = L
     return L

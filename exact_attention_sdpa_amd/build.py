@@ -4,6 +4,11 @@
 
 Objects go to ``_build/`` next to the package; the library lands in the
 package directory, where ``exact_attention_sdpa_amd._lib`` loads it.
+
+A second library, ``libsdpa_debug.so`` (objects in ``_build/debug/``), is
+the same sources built with -DSDPA_LDS_POISON=1: the forward kernels fill
+their LDS with NaN before writing it, so that a read of LDS ahead of its
+data shows up as NaN in the output (tests/test_lds_poison_gpu.py).
 """
 from __future__ import annotations
 
@@ -37,9 +42,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch=
           "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+LIB_DEBUG = os.path.join(PKG, "libsdpa_debug.so")
+DEBUG_FLAGS = ["-DSDPA_LDS_POISON=1"]
+
+
+def _compile(src: str, verbose: bool, outdir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + COMMON + list(extra) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc(), "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC, "-Wall",
                "-c", src, "-o", obj]
@@ -53,17 +62,32 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8, verbose: bool = False, debug: bool = True) -> str:
+    """Build libsdpa.so and (``debug``) libsdpa_debug.so; returns the first."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    dbg_dir = os.path.join(BUILD, "debug")
+    os.makedirs(dbg_dir, exist_ok=True)
+    jobs_list = [(s, BUILD, ()) for s in srcs]
+    if debug:
+        jobs_list += [(s, dbg_dir, DEBUG_FLAGS) for s in srcs if s.endswith(".hip")]
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1], j[2]), jobs_list))
+    n = len(srcs)
+    _link(objs[:n], LIB)
+    if debug:
+        # the host-only sources are shared; the kernels are the debug ones
+        host = [o for s, o in zip(srcs, objs[:n]) if s.endswith(".cpp")]
+        _link(objs[n:] + host, LIB_DEBUG)
     return LIB
 
 
@@ -71,8 +95,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--no-debug", dest="debug", action="store_false",
+                    help="skip the LDS-poisoning debug library")
     a = ap.parse_args(argv)
-    print(build(a.j, a.verbose))
+    print(build(a.j, a.verbose, a.debug))
     return 0
 
 

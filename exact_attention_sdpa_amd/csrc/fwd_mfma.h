@@ -139,6 +139,14 @@ enum FwdVariant : int {
 #ifndef SDPA_MASK_SKIP
 #define SDPA_MASK_SKIP 1
 #endif
+// Debug build option: fill LDS with NaN before it is written (the whole of
+// it when a tile starts, and each thread's staging slots after the barrier
+// that ends their reads), so that a read of LDS before its data has been
+// written -- a missing or misplaced barrier -- turns the output into NaN.
+// Built into libsdpa_debug.so only.
+#ifndef SDPA_LDS_POISON
+#define SDPA_LDS_POISON 0
+#endif
 // Build option: causal dense grids of up to 16 query tiles per head run
 // tiles n-1-i and i in one workgroup.
 #ifndef SDPA_CAUSAL_PAIR
@@ -341,6 +349,37 @@ struct MfmaFwd {
           dst[(2 * w + 1) * VRW] = __builtin_amdgcn_perm(b, a, 0x07060302u);
         }
       }
+  }
+
+  // Debug (LDS poisoning): NaN (f16 0x7e00, bf16 0x7fc0) written into every
+  // LDS slot this thread stores tiles into, after the barrier that ends the
+  // reads of buffer `buf` and before the step that stores the buffer's next
+  // tile, so that a wave reading a buffer before its tile has been written
+  // -- a missing or misplaced barrier -- computes NaN instead of stale
+  // values.  Single 32-bit writes of one constant keep it light on registers.
+  static __device__ __forceinline__ void poison_slots(Smem& sm, int buf, const Staging& st,
+                                                      int tid) {
+    const uint32_t kn = BF16 ? 0x7fc07fc0u : 0x7e007e00u;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS) {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.k[buf][st.kl[i]]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dst[w] = kn;
+      }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+        uint32_t* dst = &sm.vt[buf][st.vl[i]];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) dst[w * VRW] = 0x7e007e00u;
+      }
+  }
+  // ... and the whole of both buffers, padding included, at the start
+  static __device__ __forceinline__ void poison_all(Smem& sm, int tid) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(&sm);
+    constexpr int NWORDS = (int)(sizeof(Smem) / 4);
+    for (int i = tid; i < NWORDS; i += NT) w[i] = 0x7e007e00u;
   }
 
   // Raw scores S^T = K Q^T for key block kk (32 keys) of the tile in LDS K
@@ -765,6 +804,9 @@ struct MfmaFwd {
       store_v(sm, B ^ 1, vr, x.st, x.tid);
     }
     __syncthreads();
+    // every read of buffer B ended at this barrier; the step after next
+    // stores its next tile there
+    if (SDPA_LDS_POISON) poison_slots(sm, B, x.st, x.tid);
   }
 
   static __device__ void run(const MfmaParams& p, Smem& sm) {
@@ -917,6 +959,12 @@ struct MfmaFwd {
 
     setup_staging(x.st, rs, x.tid);
     x.ln = setup_lanes(x.l32, x.hl);
+
+    if (SDPA_LDS_POISON) {
+      __syncthreads();   // a previous tile of this workgroup has finished reading
+      poison_all(sm, x.tid);
+      __syncthreads();
+    }
 
     // ---- prologue: the first tile staged
     int j = next_tile(x, 0);
