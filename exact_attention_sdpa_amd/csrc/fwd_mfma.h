@@ -147,6 +147,11 @@ enum FwdVariant : int {
 #ifndef SDPA_LDS_POISON
 #define SDPA_LDS_POISON 0
 #endif
+// Build option: block-sparse workgroups start their key sweep at their own
+// diagonal block and wrap around.
+#ifndef SDPA_BSP_ROTATE
+#define SDPA_BSP_ROTATE 1
+#endif
 // Build option: causal dense grids of up to 16 query tiles per head run
 // tiles n-1-i and i in one workgroup.
 #ifndef SDPA_CAUSAL_PAIR
@@ -419,6 +424,7 @@ struct MfmaFwd {
     int nkb;                   // block-sparse: mask columns
     int mchunk;                // block-sparse: which 64 columns mbits holds
     uint64_t mbits;            // block-sparse: those columns, bit set = kept
+    int rot;                   // block-sparse: first physical tile visited
     uint32_t unit;             // dropout: b*H + h (packed: sequence*H + h)
     uint32_t seed_lo, seed_hi, doff, dt;   // dropout: key, offset, threshold
     const char* mbase;         // mask: row wq0 of the unit's mask
@@ -511,14 +517,13 @@ struct MfmaFwd {
     return __builtin_fmaf(s, c, __builtin_fmaf(a, 1.4426950408889634f, -mref));
   }
 
-  // Block-sparse: the first tile >= t whose key block the mask row keeps
-  // (>= ntiles if none).  The row is read 64 columns at a time, one byte
+  // Block-sparse: the first tile in [t, tend) whose key block the mask row
+  // keeps (tend if none).  The row is read 64 columns at a time, one byte
   // per lane, into a wave-uniform bit set, so the scan waits on memory once
   // per 64 columns rather than once per tile.
-  static __device__ __forceinline__ int next_tile(Ctx& x, int t) {
-    if (!BSP) return t;
+  static __device__ __forceinline__ int scan_kept(Ctx& x, int t, int tend) {
     constexpr int TPB = kSparseBlock / BN;   // key tiles per mask column
-    while (t < x.ntiles) {
+    while (t < tend) {
       const int kc = t / TPB;
       const int chunk = kc >> 6;
       if (chunk != x.mchunk) {
@@ -527,10 +532,39 @@ struct MfmaFwd {
         x.mchunk = chunk;
       }
       const uint64_t rest = x.mbits >> (kc & 63);
-      if (rest != 0) return max(t, (kc + (int)__builtin_ctzll(rest)) * TPB);
+      if (rest != 0) return min(max(t, (kc + (int)__builtin_ctzll(rest)) * TPB), tend);
       t = (chunk + 1) * 64 * TPB;
     }
-    return t;
+    return tend;
+  }
+
+  // Block-sparse workgroups visit their key tiles in rotated order, starting
+  // at the tile of their own diagonal block (x.rot) and wrapping around:
+  // virtual tile v is physical tile v + rot, modulo ntiles.  The workgroups
+  // resident on one XCD at a time are consecutive row blocks of one head,
+  // so they start at neighbouring keys and sweep them together through the
+  // XCD's L2; a sweep from key 0 for every workgroup spreads them over the
+  // whole key range as workgroups finish at different times.
+  static __device__ __forceinline__ int phys_tile(const Ctx& x, int v) {
+    const int t = v + x.rot;
+    return t >= x.ntiles ? t - x.ntiles : t;
+  }
+
+  // The first kept virtual tile >= v (>= ntiles if none); every tile when
+  // not block-sparse.
+  static __device__ __forceinline__ int next_tile(Ctx& x, int v) {
+    if (!BSP) return v;
+    const int first = x.ntiles - x.rot;   // virtual index of physical tile 0
+    if (v < first) {
+      const int t = scan_kept(x, v + x.rot, x.ntiles);
+      if (t < x.ntiles) return t - x.rot;
+      v = first;
+    }
+    if (v < x.ntiles) {
+      const int t = scan_kept(x, v - first, x.rot);
+      if (t < x.rot) return t + first;
+    }
+    return x.ntiles;
   }
 
   // ---- softmax update of one tile, one block of 32 keys at a time
@@ -933,6 +967,9 @@ struct MfmaFwd {
       x.nkb = p.bm_nkb;
       x.mchunk = -1;
       x.mbits = 0;
+      // start at the tile of the row block's own diagonal block
+      const int rot = SDPA_BSP_ROTATE ? qt * (kSparseBlock / BN) : 0;
+      x.rot = rot < x.ntiles ? rot : 0;
     }
 
     // ---- Q rows as the B operand of S^T = K Q^T
@@ -966,13 +1003,15 @@ struct MfmaFwd {
       __syncthreads();
     }
 
-    // ---- prologue: the first tile staged
+    // ---- prologue: the first tile staged (j counts virtual tiles, which
+    // are the physical ones unless block-sparse)
     int j = next_tile(x, 0);
     if (j < x.ntiles) {
       KRegs k0;
       VRegs v0;
-      load_k(k0, x.st, x.hd, j, x.tid);
-      load_v(v0, x.st, x.hd, j, x.tid);
+      const int jp = BSP ? phys_tile(x, j) : j;
+      load_k(k0, x.st, x.hd, jp, x.tid);
+      load_v(v0, x.st, x.hd, jp, x.tid);
       store_k(sm, 0, k0, x.st, x.tid);
       store_v(sm, 0, v0, x.st, x.tid);
     }
@@ -984,13 +1023,14 @@ struct MfmaFwd {
         if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1, j + 2);
       }
     } else {
+      // step() takes physical tiles (ntiles: no next tile)
       while (j < x.ntiles) {
         int jn = next_tile(x, j + 1);
-        step<0>(sm, x, S, qf, j, jn);
+        step<0>(sm, x, S, qf, phys_tile(x, j), jn < x.ntiles ? phys_tile(x, jn) : x.ntiles);
         if (jn >= x.ntiles) break;
         j = jn;
         jn = next_tile(x, j + 1);
-        step<1>(sm, x, S, qf, j, jn);
+        step<1>(sm, x, S, qf, phys_tile(x, j), jn < x.ntiles ? phys_tile(x, jn) : x.ntiles);
         j = jn;
       }
     }

@@ -106,20 +106,27 @@ def test_bwd_block_sparse_empty_rows_and_columns():
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_block_mask_matches_dense_backward(causal):
-    # every block kept: the same tiles in the same order as the dense
-    # backward, so the same bits
+    # every block kept: given the same O and lse, the block-sparse backward
+    # visits the same tiles in the same order as the dense one, so the same
+    # bits (the forwards differ in rounding order: the block-sparse forward
+    # starts each row block's sweep at its diagonal block)
     B, H, N, d = 1, 2, 384, 64
     w = inputs.make_dense(B, H, N, N, d, "f16", "normal", causal, seed=4, cfg=143)
     do = inputs.make_grad_out(w, seed=4, cfg=143)
-    got = _run(w, do, np.ones((1, 3, 3), np.uint8))
     q, k, v = (to_device(x, "f16") for x in (w.q, w.k, w.v))
     g = to_device(do, "f16")
+    bmt = torch.ones((1, 3, 3), dtype=torch.uint8, device="cuda")
     out, lse = sdpa.scaled_dot_product_attention(q, k, v, is_causal=causal, return_lse=True)
+    sparse = sdpa.scaled_dot_product_attention_backward(q, k, v, out, lse, g, is_causal=causal,
+                                                        grad_dtype=torch.float32, block_mask=bmt)
     dense = sdpa.scaled_dot_product_attention_backward(q, k, v, out, lse, g, is_causal=causal,
                                                        grad_dtype=torch.float32)
     torch.cuda.synchronize()
-    for a, b in zip(got, dense):
-        assert np.array_equal(a, b.double().cpu().numpy())
+    for a, b in zip(sparse, dense):
+        assert torch.equal(a, b)
+    # and the whole block-sparse path (its own forward) within the bound
+    got = _run(w, do, np.ones((1, 3, 3), np.uint8))
+    _check(w, got, do, np.ones((1, 3, 3), np.uint8))
 
 
 def test_autograd_with_block_mask_matches_explicit():
