@@ -390,6 +390,110 @@ def _counter_kib(d, kernel_match):
     return sum(vals) / len(vals), len(vals)
 
 
+# SQ counters of the forward kernel, from two rocprofv3 --pmc passes (the
+# per-pass limit is 8 SQ counters) on the same workload:
+SQ_PASS_A = ("SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+             "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_LDS")
+SQ_PASS_B = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAIT_INST_LDS "
+             "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_ANY SQ_CYCLES GRBM_GUI_ACTIVE")
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9      # the clock the published peak assumes
+
+
+def _counters_by_name(d, kernel_match):
+    """Average per dispatch of each counter over the matching dispatches."""
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if kernel_match in r["Kernel_Name"]:
+            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatch matching {kernel_match!r} in {d}")
+    return {n: sum(v.values()) / len(v) for n, v in per.items()}
+
+
+def issue_shares(c, avg_ns):
+    """Shares of the SIMD-cycles (1024 SIMDs x duration x 2.4 GHz) in which
+    the matrix cores are busy (SQ_VALU_MFMA_BUSY_CYCLES), the vector unit
+    issues (4 x SQ_ACTIVE_INST_VALU: the counter ticks once per 4-cycle
+    issue of a wave64 instruction), and both at once
+    (SQ_VALU_MFMA_COEXEC_CYCLES); the larger of the first two names the
+    binding unit."""
+    cyc = SIMDS * avg_ns * 1e-9 * CLOCK_HZ
+    mf = c["SQ_VALU_MFMA_BUSY_CYCLES"] / cyc
+    va = 4.0 * c["SQ_ACTIVE_INST_VALU"] / cyc
+    co = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / cyc
+    return {"mfma_busy_share": round(mf, 3), "valu_issue_share": round(va, 3),
+            "coexec_share": round(co, 3), "idle_share": round(max(0.0, 1.0 - mf - va + co), 3),
+            "valu_per_mfma": round(c["SQ_INSTS_VALU"] / max(c["SQ_INSTS_MFMA"], 1.0), 2),
+            "lds_bank_conflicts": c.get("SQ_LDS_BANK_CONFLICT", 0.0),
+            "binding": "vector issue" if va > mf else "matrix core"}
+
+
+def stored_counters(workload: str):
+    """Issue shares from the committed SQ-counter record, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "sq_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sources") != kernel_sources_digest():
+        return None
+    return rec.get("workloads", {}).get(workload)
+
+
+def summarize_counters(a) -> int:
+    """profiles/sq_counters.json (and its text form) from the kernel-trace
+    run and the two SQ-counter passes of one workload."""
+    stats = _csv_rows(a.trace_dir, "kernel_stats.csv")
+    ker = [r for r in stats if "fwd_mfma" in r["Name"]]
+    k = max(ker, key=lambda r: float(r["TotalDurationNs"]))
+    avg_ns = float(k["AverageNs"])
+    c = _counters_by_name(a.ctr_a_dir, "fwd_mfma")
+    c.update(_counters_by_name(a.ctr_b_dir, "fwd_mfma"))
+    sh = issue_shares(c, avg_ns)
+    path = os.path.join(ROOT, "profiles", "sq_counters.json")
+    rec = {"kernel_sources": kernel_sources_digest(), "workloads": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            old = json.load(f)
+        if old.get("kernel_sources") == rec["kernel_sources"]:
+            rec = old
+    rec["workloads"][a.workload] = dict(sh, avg_kernel_us=round(avg_ns / 1e3, 3),
+                                        counters={n: c[n] for n in sorted(c)})
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    lines = [f"# fwd_mfma: issue counters (SQ_*) of the forward kernel",
+             "",
+             "commands (two passes per workload, one counter set each):",
+             f"  rocprofv3 --pmc {SQ_PASS_A} -f csv -d <dir> -o run -- python3 bench.py "
+             "--workload W --steps 3 --warmup 1 --cpu-budget 0 --cold-reps 0 --no-targets",
+             f"  rocprofv3 --pmc {SQ_PASS_B} (same program)",
+             "values: per dispatch of the attention kernel, averaged over the dispatches; whole GPU.",
+             "shares: of 1024 SIMDs x the kernel-trace average duration x 2.4 GHz; vector issue",
+             "counts 4 cycles per SQ_ACTIVE_INST_VALU tick (a wave64 instruction on a 16-lane SIMD);",
+             "one 32x32x16 MFMA keeps the matrix core busy 32 cycles.  'bound by' names the unit",
+             "with the larger share; 'neither' is time lost to waits (memory, LDS, barriers).", ""]
+    for wl, e in sorted(rec["workloads"].items()):
+        lines += [f"## {wl} (kernel average {e['avg_kernel_us']:.1f} us from the kernel-trace profile)"]
+        lines += [f"  {n:28s} {v:.4g}" for n, v in e["counters"].items()]
+        c = e["counters"]
+        lines += [f"  32 x SQ_INSTS_MFMA / SQ_VALU_MFMA_BUSY_CYCLES: "
+                  f"{32 * c['SQ_INSTS_MFMA'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}",
+                  f"  co-executing share of matrix-busy cycles: "
+                  f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.2f}",
+                  f"  VALU instructions per MFMA: {e['valu_per_mfma']}",
+                  f"  share of SIMD-cycles: matrix core busy {e['mfma_busy_share']}, vector issue "
+                  f"{e['valu_issue_share']}, both at once {e['coexec_share']}, neither "
+                  f"{e['idle_share']} -> bound by {e['binding']}", ""]
+    lines.append(f"kernel sources digest: {kernel_sources_digest()}")
+    with open(os.path.join(ROOT, "profiles", "fwd_mfma_sq_counters.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def summarize_bwd(a) -> int:
     """Turn the rocprofv3 kernel trace of a backward run (bench.py --pass bwd)
     into profiles/bwd_<workload>[_dropout].txt: each backward kernel's
@@ -462,7 +566,7 @@ def summarize(a) -> int:
         "Kernel trace (average over the profiled launches):",
         f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- "
         f"python3 bench.py --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
-        f"--cpu-budget 0 --cold-reps 0",
+        f"--cpu-budget 0 --cold-reps 0 --no-targets",
         f"  kernel:  {k['Name']}",
         f"  calls {k['Calls']}  average {avg_ns / 1e3:.2f} us  min {float(k['MinNs']) / 1e3:.2f} us"
         f"  max {float(k['MaxNs']) / 1e3:.2f} us",
@@ -471,7 +575,8 @@ def summarize(a) -> int:
         "",
         "HBM traffic (separate counter passes, one counter block each):",
         f"  commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
-        f"--workload {a.workload}{dflag} --steps 5 --warmup 1 --cpu-budget 0 --cold-reps 0",
+        f"--workload {a.workload}{dflag} --steps 5 --warmup 1 --cpu-budget 0 --cold-reps 0 "
+        "--no-targets",
         "            rocprofv3 --pmc WRITE_SIZE (same program)",
         "            rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 bench.py --calibrate-copy",
         f"  copy of 1 GiB reads FETCH_SIZE {cfetch:.0f} KiB, WRITE_SIZE {cwrite:.0f} KiB"
@@ -532,6 +637,11 @@ def main(argv=None) -> int:
                          "an attainable matrix-core rate for reference")
     ap.add_argument("--no-targets", dest="targets", action="store_false",
                     help="skip timing the causal and long workloads after the headline")
+    ap.add_argument("--summarize-counters", action="store_true",
+                    help="write profiles/sq_counters.json from --trace-dir, --ctr-a-dir, "
+                         "--ctr-b-dir (rocprofv3 outputs of the SQ_PASS_A / SQ_PASS_B sets)")
+    ap.add_argument("--ctr-a-dir")
+    ap.add_argument("--ctr-b-dir")
     ap.add_argument("--summarize", action="store_true",
                     help="summarize rocprofv3 CSV outputs into profiles/ (no GPU needed)")
     ap.add_argument("--trace-dir")
@@ -542,6 +652,8 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.cold_reps is None:
         a.cold_reps = 10 if a.workload in ("long", "block_sparse") else 50
+    if a.summarize_counters:
+        return summarize_counters(a)
     if a.summarize:
         return summarize_bwd(a) if a.which == "bwd" else summarize(a)
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -747,6 +859,13 @@ def main(argv=None) -> int:
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4)}
     roof["traffic"] = (stored_traffic(a.workload + ("_dropout" if a.dropout > 0 else ""))
                        if a.which == "fwd" else None)
+    # the nominal roofline is the matrix cores'; the issue counters (when
+    # taken on these kernel sources) say which unit actually binds
+    sq = stored_counters(a.workload) if a.which == "fwd" and a.dropout == 0 else None
+    if sq:
+        for key in ("mfma_busy_share", "valu_issue_share", "coexec_share", "idle_share",
+                    "binding"):
+            roof[key] = sq[key]
     rec = {
         "metric": METRIC if a.which == "fwd" else METRIC_BWD,
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

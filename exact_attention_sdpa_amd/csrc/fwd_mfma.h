@@ -15,10 +15,9 @@
 //            XCDs (dispatched round-robin) owns a contiguous range of tiles,
 //            and the tiles of one head run back to back on one XCD, sharing
 //            K/V in that XCD's L2.  Causal dense grids of up to 16 query
-//            tiles per head instead give one workgroup the pair of tiles
-//            n-1-i and i (heavy first), so every workgroup sweeps the same
-//            number of key tiles, and the pairs of a head sweep its keys
-//            together on one XCD.
+//            tiles per head instead run every head's heaviest query tile
+//            first, then the next heaviest, and so on (longest-processing-
+//            time order), each XCD keeping its own heads.
 //   waves    NW waves; wave w owns NB blocks of 32 query rows.
 //   tile     BN keys per step, read with buffer loads whose range check
 //            returns zeros past the last key, staged through double-buffered
@@ -96,7 +95,6 @@ struct MfmaParams {
   int q_rs, kv_rs, o_rs;
   int n_qtiles;        // query tiles per (batch, head)
   int total;           // grid size
-  int paired;          // causal dense: tiles n-1-i and i share a workgroup
   float c;             // scale * log2(e), at least 1e-30
   // block-sparse launches: mask [Hm][ceil(Nq/128)][ceil(Nk/128)], nonzero =
   // the 128x128 block of (query, key) pairs is visible
@@ -147,17 +145,7 @@ enum FwdVariant : int {
 #ifndef SDPA_LDS_POISON
 #define SDPA_LDS_POISON 0
 #endif
-// Build option: block-sparse workgroups start their key sweep at their own
-// diagonal block and wrap around.
-#ifndef SDPA_BSP_ROTATE
-#define SDPA_BSP_ROTATE 1
-#endif
-// Build option: causal dense grids of up to 16 query tiles per head run
-// tiles n-1-i and i in one workgroup.
-#ifndef SDPA_CAUSAL_PAIR
-#define SDPA_CAUSAL_PAIR 1
-#endif
-// Build option: otherwise, such grids in longest-processing-time order.
+// Build option: causal dense grids in longest-processing-time order.
 #ifndef SDPA_CAUSAL_LPT
 #define SDPA_CAUSAL_LPT 1
 #endif
@@ -424,7 +412,6 @@ struct MfmaFwd {
     int nkb;                   // block-sparse: mask columns
     int mchunk;                // block-sparse: which 64 columns mbits holds
     uint64_t mbits;            // block-sparse: those columns, bit set = kept
-    int rot;                   // block-sparse: first physical tile visited
     uint32_t unit;             // dropout: b*H + h (packed: sequence*H + h)
     uint32_t seed_lo, seed_hi, doff, dt;   // dropout: key, offset, threshold
     const char* mbase;         // mask: row wq0 of the unit's mask
@@ -517,13 +504,14 @@ struct MfmaFwd {
     return __builtin_fmaf(s, c, __builtin_fmaf(a, 1.4426950408889634f, -mref));
   }
 
-  // Block-sparse: the first tile in [t, tend) whose key block the mask row
-  // keeps (tend if none).  The row is read 64 columns at a time, one byte
+  // Block-sparse: the first tile >= t whose key block the mask row keeps
+  // (>= ntiles if none).  The row is read 64 columns at a time, one byte
   // per lane, into a wave-uniform bit set, so the scan waits on memory once
   // per 64 columns rather than once per tile.
-  static __device__ __forceinline__ int scan_kept(Ctx& x, int t, int tend) {
+  static __device__ __forceinline__ int next_tile(Ctx& x, int t) {
+    if (!BSP) return t;
     constexpr int TPB = kSparseBlock / BN;   // key tiles per mask column
-    while (t < tend) {
+    while (t < x.ntiles) {
       const int kc = t / TPB;
       const int chunk = kc >> 6;
       if (chunk != x.mchunk) {
@@ -532,39 +520,10 @@ struct MfmaFwd {
         x.mchunk = chunk;
       }
       const uint64_t rest = x.mbits >> (kc & 63);
-      if (rest != 0) return min(max(t, (kc + (int)__builtin_ctzll(rest)) * TPB), tend);
+      if (rest != 0) return max(t, (kc + (int)__builtin_ctzll(rest)) * TPB);
       t = (chunk + 1) * 64 * TPB;
     }
-    return tend;
-  }
-
-  // Block-sparse workgroups visit their key tiles in rotated order, starting
-  // at the tile of their own diagonal block (x.rot) and wrapping around:
-  // virtual tile v is physical tile v + rot, modulo ntiles.  The workgroups
-  // resident on one XCD at a time are consecutive row blocks of one head,
-  // so they start at neighbouring keys and sweep them together through the
-  // XCD's L2; a sweep from key 0 for every workgroup spreads them over the
-  // whole key range as workgroups finish at different times.
-  static __device__ __forceinline__ int phys_tile(const Ctx& x, int v) {
-    const int t = v + x.rot;
-    return t >= x.ntiles ? t - x.ntiles : t;
-  }
-
-  // The first kept virtual tile >= v (>= ntiles if none); every tile when
-  // not block-sparse.
-  static __device__ __forceinline__ int next_tile(Ctx& x, int v) {
-    if (!BSP) return v;
-    const int first = x.ntiles - x.rot;   // virtual index of physical tile 0
-    if (v < first) {
-      const int t = scan_kept(x, v + x.rot, x.ntiles);
-      if (t < x.ntiles) return t - x.rot;
-      v = first;
-    }
-    if (v < x.ntiles) {
-      const int t = scan_kept(x, v - first, x.rot);
-      if (t < x.rot) return t + first;
-    }
-    return x.ntiles;
+    return t;
   }
 
   // ---- softmax update of one tile, one block of 32 keys at a time
@@ -624,7 +583,7 @@ struct MfmaFwd {
   // 2(w&1)+1): exactly the 8 keys of Philox call n = kb0/8 + 2 hs + hl of
   // row i, whose output word w carries their two 16-bit numbers (low half
   // = first key of the pair).  The row sums keep the undropped P; the
-  // 65536/T scale is applied to O at the end.
+  // 1/(1-p) scale is applied to O at the end.
   static __device__ __forceinline__ void drop_block(u32x4 (&pf)[NB][2], int kb0, const Ctx& x) {
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
@@ -647,150 +606,119 @@ struct MfmaFwd {
     }
   }
 
-  // ---- softmax of one 32-key block, in three parts
-  //   prep   masking and, where the kernel has no reference yet, setting it
-  //          (may branch)
-  //   body   t = s*c - m (one fma per score; folded into the mask's bias for
-  //          elementwise masks), P = exp2(t), the lane's fp32 sums and the
-  //          f16 B operands of P V (straight-line vector code)
-  //   fix    the lane-sum check and its rare redo, dropout (may branch)
+  // One tile, one block of 32 keys at a time: the products S(kk+1) are
+  // issued before the softmax of block kk (they do not depend on it) and
+  // P V of block kk after it.
+  //   t = s*c - m (one fma per score), P = exp2(t).
   // The first block of the first tile sets m to its row maximum (finite:
   // key 0 is visible to every row).  After that no row maximum is taken:
   // each P is at most its lane's block sum, so one compare per block proves
   // that no f16 P can overflow.  A lane over the limit (rare) raises its
   // row to the block maximum, O and l are rescaled in place, and the
   // block's exponentials are redone.
-
-  static __device__ __forceinline__ void softmax_prep(f32x16 (&sc)[NB], int kk, int kb, bool first,
-                                                      bool masked, const Ctx& x, State& S,
-                                                      const MaskRegs& mr) {
-    if (masked && !MASK) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
-    if (MASK) {
-      // the mask's bias is folded into the scaled scores first; pairs the
-      // causal rule or the key tail excludes are then set to -inf whatever
-      // the mask holds there.  A row's reference is set by the first block
-      // in which it has a finite score.
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        const float mref = S.m[qb] == -INFINITY ? 0.f : S.m[qb];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] = mask_score(sc[qb][r], x.c, mref, mr.w[kk][qb], r);
-      }
-      if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
-      bool unset = false;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
-      if (__builtin_amdgcn_ballot_w64(unset) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          const float mm = row_max(sc[qb]);
-          const bool set_now = S.m[qb] == -INFINITY && mm > -INFINITY;
-          const float sub = set_now ? mm : 0.f;
-          if (set_now) S.m[qb] = mm;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sc[qb][r] -= sub;
-        }
-      }
-    } else if (BSP) {
-      // block-sparse: a row's reference is set by the first block in
-      // which it sees a key (its first visible block can be anywhere)
-      bool unset = false;
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
-      if (__builtin_amdgcn_ballot_w64(unset) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) {
-          const float mm = row_max(sc[qb]) * x.c;
-          if (S.m[qb] == -INFINITY) S.m[qb] = mm;
-        }
-      }
-    } else if (kk == 0 && first) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
-    }
-  }
-
-  static __device__ __forceinline__ void softmax_body(f32x16 (&sc)[NB], const Ctx& x,
-                                                      const State& S, float (&bs)[NB][2],
-                                                      u32x4 (&pf)[NB][2]) {
-    if (!MASK) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        // rows that have not seen a key yet have only -inf scores here
-        const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
-      }
-    }
-    exp_block(sc, bs, pf);
-  }
-
-  static __device__ __forceinline__ void softmax_fix(f32x16 (&sc)[NB], int kk, int kb,
-                                                     const Ctx& x, State& S, float (&bs)[NB][2],
-                                                     u32x4 (&pf)[NB][2]) {
-    bool over = false;
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) over = over || !(bs[qb][0] + bs[qb][1] <= kLaneSumLimit);
-    if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-      for (int qb = 0; qb < NB; ++qb) {
-        // rows with nothing to raise take y = 0 (a no-op), so no per-lane
-        // branch splits the accumulators' live ranges
-        const float y = fmaxf(row_max(sc[qb]), 0.f);
-        const float alpha = __builtin_amdgcn_exp2f(-y);
-        S.m[qb] += y;
-        S.l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[qb][r] -= y;
-      }
-      exp_block(sc, bs, pf);
-    }
-    if (DROP) drop_block(pf, kb + kk * 32, x);
-#pragma unroll
-    for (int qb = 0; qb < NB; ++qb) S.l[qb] += bs[qb][0] + bs[qb][1];
-  }
-
-  // O^T += V^T P^T for key block kk of the tile in LDS V buffer `buf`.
-  static __device__ __forceinline__ void pv(State& S, const Smem& sm, int buf, int kk,
-                                            const Lanes& ln, const u32x4 (&pf)[NB][2]) {
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 vf =
-            *reinterpret_cast<const u32x4*>(&sm.vt[buf][ln.vl[hs] + db * 32 * VRW + 16 * kk]);
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) S.o[qb][db] = mfma_f16(vf, pf[qb][hs], S.o[qb][db]);
-      }
-  }
-
-  // One tile, one block of 32 keys at a time: the products S(kk+1) are
-  // issued before the softmax of block kk (they do not depend on it) and
-  // P V of block kk right after it.
   static __device__ __forceinline__ void tile(const Smem& sm, int buf, int kb, bool first,
                                               bool masked, const Ctx& x, const u32x4 (&qf)[NB][DS],
                                               State& S, const MaskRegs& mr) {
-    f32x16 sc[NB];
+    f32x16 sc[NB], sn[NB];
     scores(sc, sm, buf, 0, x.ln, qf);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-      f32x16 sn[NB];
+      const bool pending = kk + 1 < KB;
+      if (masked && !MASK) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+      if (pending) scores(sn, sm, buf, kk + 1, x.ln, qf);
+      if (MASK) {
+        // the mask's bias is folded into the scaled scores first; pairs the
+        // causal rule or the key tail excludes are then set to -inf whatever
+        // the mask holds there.  A row's reference is set by the first block
+        // in which it has a finite score.
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float mref = S.m[qb] == -INFINITY ? 0.f : S.m[qb];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sc[qb][r] = mask_score(sc[qb][r], x.c, mref, mr.w[kk][qb], r);
+        }
+        if (masked) mask_block(sc, kb + kk * 32, x.nk, x.wq0, x.l32, x.hl);
+        bool unset = false;
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) {
+            const float mm = row_max(sc[qb]);
+            const bool set_now = S.m[qb] == -INFINITY && mm > -INFINITY;
+            const float sub = set_now ? mm : 0.f;
+            if (set_now) S.m[qb] = mm;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[qb][r] -= sub;
+          }
+        }
+      } else if (BSP) {
+        // block-sparse: a row's reference is set by the first block in
+        // which it sees a key (its first visible block can be anywhere)
+        bool unset = false;
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) unset = unset || S.m[qb] == -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) {
+            const float mm = row_max(sc[qb]) * x.c;
+            if (S.m[qb] == -INFINITY) S.m[qb] = mm;
+          }
+        }
+      } else if (kk == 0 && first) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) S.m[qb] = row_max(sc[qb]) * x.c;
+      }
+      if (!MASK) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          // rows that have not seen a key yet have only -inf scores here
+          const float mref = (BSP && S.m[qb] == -INFINITY) ? 0.f : S.m[qb];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[qb][r] = __builtin_fmaf(sc[qb][r], x.c, -mref);
+        }
+      }
       float bs[NB][2];
       u32x4 pf[NB][2];
-      if (kk + 1 < KB) scores(sn, sm, buf, kk + 1, x.ln, qf);
-      softmax_prep(sc, kk, kb, first, masked, x, S, mr);
-      softmax_body(sc, x, S, bs, pf);
-      softmax_fix(sc, kk, kb, x, S, bs, pf);
-      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-      pv(S, sm, buf, kk, x.ln, pf);
-      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
-      if (kk + 1 < KB) {
+      exp_block(sc, bs, pf);
+      bool over = false;
 #pragma unroll
-        for (int qb = 0; qb < NB; ++qb) sc[qb] = sn[qb];
+      for (int qb = 0; qb < NB; ++qb) over = over || !(bs[qb][0] + bs[qb][1] <= kLaneSumLimit);
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          // rows with nothing to raise take y = 0 (a no-op), so no per-lane
+          // branch splits the accumulators' live ranges
+          const float y = fmaxf(row_max(sc[qb]), 0.f);
+          const float alpha = __builtin_amdgcn_exp2f(-y);
+          S.m[qb] += y;
+          S.l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S.o[qb][db][r] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[qb][r] -= y;
+        }
+        exp_block(sc, bs, pf);
+      }
+      if (DROP) drop_block(pf, kb + kk * 32, x);
+      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(
+              &sm.vt[buf][x.ln.vl[hs] + db * 32 * VRW + 16 * kk]);
+#pragma unroll
+          for (int qb = 0; qb < NB; ++qb) S.o[qb][db] = mfma_f16(vf, pf[qb][hs], S.o[qb][db]);
+        }
+      if (SDPA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int qb = 0; qb < NB; ++qb) {
+        S.l[qb] += bs[qb][0] + bs[qb][1];
+        if (pending) sc[qb] = sn[qb];
       }
     }
   }
@@ -844,25 +772,17 @@ struct MfmaFwd {
   }
 
   static __device__ void run(const MfmaParams& p, Smem& sm) {
-    // ---- which tile(s): XCD-contiguous ranges; causal: heaviest tiles first
-    int qt, bh, qt2 = -1;
-    if (CAUSAL && !VARLEN && !BSP && p.paired) {
-      // causal, short sequences: query tile n-1-i and tile i of one head
-      // share a workgroup (heavy one first), so every workgroup sweeps the
-      // same number of key tiles (n+1 tile widths); the pairs of one head
-      // are consecutive and so stay on one XCD, where they sweep the head's
-      // keys together through its L2
-      const int npair = (p.n_qtiles + 1) / 2;
-      int idx = blockIdx.x;
-      if ((p.total & 7) == 0) {
-        const int per = p.total >> 3;
-        idx = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-      }
-      bh = idx / npair;
-      const int pr = idx % npair;
-      qt = p.n_qtiles - 1 - pr;
-      if (pr < qt) qt2 = pr;   // the middle tile of an odd count runs alone
-    } else if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
+    Ctx x;
+    x.tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
+    const int lane = x.tid % 64;
+    x.hl = lane / 32;
+    x.l32 = lane % 32;
+    x.c = p.c;
+
+    // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
+    int qt, bh;
+    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
       // causal, short sequences: every head's heaviest query tiles first,
       // then the next heaviest of every head, ... (longest-processing-time
       // order, which shortens the tail when many heads have few tiles);
@@ -891,23 +811,6 @@ struct MfmaFwd {
       bh = tile / p.n_qtiles;
       if (CAUSAL) qt = p.n_qtiles - 1 - qt;
     }
-    // one or two query tiles, one after the other (qt2 is uniform over the
-    // workgroup, so every wave reaches every barrier of both)
-    run_tile(p, sm, qt, bh);
-    if (qt2 >= 0) run_tile(p, sm, qt2, bh);
-  }
-
-  // One query tile qt of unit bh: stream its key tiles, write O and lse.
-  // Every LDS read of the tile happens before its last barrier, so a second
-  // tile may follow at once.
-  static __device__ __forceinline__ void run_tile(const MfmaParams& p, Smem& sm, int qt, int bh) {
-    Ctx x;
-    x.tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
-    const int lane = x.tid % 64;
-    x.hl = lane / 32;
-    x.l32 = lane % 32;
-    x.c = p.c;
     const int b = bh / p.H, h = bh % p.H;
 
     int nq, nk;
@@ -967,9 +870,6 @@ struct MfmaFwd {
       x.nkb = p.bm_nkb;
       x.mchunk = -1;
       x.mbits = 0;
-      // start at the tile of the row block's own diagonal block
-      const int rot = SDPA_BSP_ROTATE ? qt * (kSparseBlock / BN) : 0;
-      x.rot = rot < x.ntiles ? rot : 0;
     }
 
     // ---- Q rows as the B operand of S^T = K Q^T
@@ -998,20 +898,17 @@ struct MfmaFwd {
     x.ln = setup_lanes(x.l32, x.hl);
 
     if (SDPA_LDS_POISON) {
-      __syncthreads();   // a previous tile of this workgroup has finished reading
       poison_all(sm, x.tid);
       __syncthreads();
     }
 
-    // ---- prologue: the first tile staged (j counts virtual tiles, which
-    // are the physical ones unless block-sparse)
+    // ---- prologue: the first tile staged
     int j = next_tile(x, 0);
     if (j < x.ntiles) {
       KRegs k0;
       VRegs v0;
-      const int jp = BSP ? phys_tile(x, j) : j;
-      load_k(k0, x.st, x.hd, jp, x.tid);
-      load_v(v0, x.st, x.hd, jp, x.tid);
+      load_k(k0, x.st, x.hd, j, x.tid);
+      load_v(v0, x.st, x.hd, j, x.tid);
       store_k(sm, 0, k0, x.st, x.tid);
       store_v(sm, 0, v0, x.st, x.tid);
     }
@@ -1023,14 +920,13 @@ struct MfmaFwd {
         if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1, j + 2);
       }
     } else {
-      // step() takes physical tiles (ntiles: no next tile)
       while (j < x.ntiles) {
         int jn = next_tile(x, j + 1);
-        step<0>(sm, x, S, qf, phys_tile(x, j), jn < x.ntiles ? phys_tile(x, jn) : x.ntiles);
+        step<0>(sm, x, S, qf, j, jn);
         if (jn >= x.ntiles) break;
         j = jn;
         jn = next_tile(x, j + 1);
-        step<1>(sm, x, S, qf, phys_tile(x, j), jn < x.ntiles ? phys_tile(x, jn) : x.ntiles);
+        step<1>(sm, x, S, qf, j, jn);
         j = jn;
       }
     }
@@ -1099,12 +995,15 @@ constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D6
 template <int D>
 constexpr int kBspWavesPerSimd =
     D == 32 ? SDPA_BSP_WAVES_D32 : D == 64 ? SDPA_BSP_WAVES_D64 : SDPA_BSP_WAVES_D128;
-// the dropout kernels (the Philox rounds need about ten more live registers)
+// the dropout kernels (the Philox rounds need about ten more live
+// registers).  At d = 64 the bound of 4 waves keeps them within 128 VGPRs,
+// so two 8-wave workgroups share a CU: a kernel of 129 registers runs one
+// workgroup per CU and measured 20% slower on the causal workload.
 #ifndef SDPA_DROP_WAVES_D32
 #define SDPA_DROP_WAVES_D32 4
 #endif
 #ifndef SDPA_DROP_WAVES_D64
-#define SDPA_DROP_WAVES_D64 3
+#define SDPA_DROP_WAVES_D64 4
 #endif
 #ifndef SDPA_DROP_WAVES_D128
 #define SDPA_DROP_WAVES_D128 2

@@ -13,7 +13,7 @@ namespace sdpa {
 // Tile shape per head dimension: NB blocks of 32 query rows per wave, NW
 // waves, BN keys per step (overridable at build time for tuning sweeps).
 #ifndef SDPA_SHAPE_D32
-#define SDPA_SHAPE_D32 1, 4, 64
+#define SDPA_SHAPE_D32 1, 8, 64
 #endif
 #ifndef SDPA_SHAPE_D64
 #define SDPA_SHAPE_D64 1, 8, 64
@@ -47,7 +47,7 @@ template <> struct BspShape<128> : ShapeOf<SDPA_BSP_SHAPE_D128> {};
 
 // Dropout shapes.
 #ifndef SDPA_DROP_SHAPE_D32
-#define SDPA_DROP_SHAPE_D32 SDPA_SHAPE_D32
+#define SDPA_DROP_SHAPE_D32 1, 4, 64
 #endif
 #ifndef SDPA_DROP_SHAPE_D64
 #define SDPA_DROP_SHAPE_D64 SDPA_SHAPE_D64
@@ -62,7 +62,7 @@ template <> struct DropShape<128> : ShapeOf<SDPA_DROP_SHAPE_D128> {};
 
 // Elementwise-mask shapes.
 #ifndef SDPA_MASK_SHAPE_D32
-#define SDPA_MASK_SHAPE_D32 SDPA_SHAPE_D32
+#define SDPA_MASK_SHAPE_D32 1, 4, 64
 #endif
 #ifndef SDPA_MASK_SHAPE_D64
 #define SDPA_MASK_SHAPE_D64 SDPA_SHAPE_D64
@@ -104,11 +104,6 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.o_rs = (int)a.o_str[2];
   p.n_qtiles = (int)((a.Nq + K::BM - 1) / K::BM);
   p.total = (int)(a.B * a.H * p.n_qtiles);
-  // causal dense grids of 2..16 query tiles per head: one workgroup per
-  // pair of tiles (n-1-i, i), equal work per workgroup
-  p.paired = CAUSAL && !VARLEN && VAR != kBlockSparse && SDPA_CAUSAL_PAIR && p.n_qtiles >= 2 &&
-             p.n_qtiles <= 16;
-  if (p.paired) p.total = (int)(a.B * a.H * ((p.n_qtiles + 1) / 2));
   // scale 0 is carried as a tiny positive multiplier: every visible score
   // becomes 0 to within 1e-30 relative, masked scores stay -inf
   p.c = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);

@@ -79,18 +79,13 @@ def test_all_zero_mask_gives_zeros_and_neg_inf():
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_mask_equals_dense_path(d, causal):
-    """With every block visible the block-sparse kernel visits every key
-    tile, starting at the row block's own diagonal block and wrapping
-    around, where the dense kernel starts at key 0.  Row block 0 starts at
-    key 0 too and takes exactly the dense kernel's arithmetic steps
-    (bit-identical); the others sum the same terms in another order, equal
-    to the dense result within the parity tolerance."""
+    """With every block visible the block-sparse kernel takes the same
+    arithmetic steps as the dense one, key tile by key tile from key 0:
+    bit-identical results."""
     w = inputs.make_dense(2, 2, 333, 333, d, "f16", "normal", causal, seed=d, cfg=84)
     o, lse = _run(w, np.ones((1, 3, 3), np.uint8))
     od, ld = G.run(w)
-    assert np.array_equal(o[:, :, :128], od[:, :, :128])
-    assert np.array_equal(lse[:, :, :128], ld[:, :, :128])
-    G.assert_parity(o, od, "f16", f"all-ones mask d{d} causal={causal}", lse, ld)
+    assert np.array_equal(o, od) and np.array_equal(lse, ld)
 
 
 def test_shared_mask_equals_replicated_per_head_mask():

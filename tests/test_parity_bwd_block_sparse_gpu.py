@@ -106,10 +106,8 @@ def test_bwd_block_sparse_empty_rows_and_columns():
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_block_mask_matches_dense_backward(causal):
-    # every block kept: given the same O and lse, the block-sparse backward
-    # visits the same tiles in the same order as the dense one, so the same
-    # bits (the forwards differ in rounding order: the block-sparse forward
-    # starts each row block's sweep at its diagonal block)
+    # every block kept: the block-sparse forward and backward visit the
+    # same tiles in the same order as the dense ones, so the same bits
     B, H, N, d = 1, 2, 384, 64
     w = inputs.make_dense(B, H, N, N, d, "f16", "normal", causal, seed=4, cfg=143)
     do = inputs.make_grad_out(w, seed=4, cfg=143)
@@ -124,9 +122,10 @@ def test_all_ones_block_mask_matches_dense_backward(causal):
     torch.cuda.synchronize()
     for a, b in zip(sparse, dense):
         assert torch.equal(a, b)
-    # and the whole block-sparse path (its own forward) within the bound
+    # and the whole block-sparse path, its own forward included
     got = _run(w, do, np.ones((1, 3, 3), np.uint8))
-    _check(w, got, do, np.ones((1, 3, 3), np.uint8))
+    for a, b in zip(got, dense):
+        assert np.array_equal(a, b.double().cpu().numpy())
 
 
 def test_autograd_with_block_mask_matches_explicit():
