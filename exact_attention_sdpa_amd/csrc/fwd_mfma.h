@@ -185,10 +185,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// two bf16 (packed) -> two f16 (packed); exact for normal f16 magnitudes.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
 
 // Position of key k (0..BN-1) inside its LDS V^T row: within each group of
 // 16 keys, lane half 0 reads keys {0-3, 8-11} and half 1 keys {4-7, 12-15},
@@ -333,13 +329,18 @@ struct MfmaFwd {
         uint32_t* dst = &sm.vt[buf][st.vl[i]];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          uint32_t a = r.v0[i][w], b = r.v1[i][w];  // (d 2w, d 2w+1) of keys 2pr, 2pr+1
+          const uint32_t a = r.v0[i][w], b = r.v1[i][w];  // (d 2w, d 2w+1) of keys 2pr, 2pr+1
           if (BF16) {
-            a = bf16x2_to_f16x2(a);
-            b = bf16x2_to_f16x2(b);
+            // a bf16 value is the upper half of its f32, so one byte
+            // permute both widens it and picks it out of the pair (the
+            // transpose), and a packing conversion makes the f16 pair
+            const auto f = [&](uint32_t sel) { return __uint_as_float(__builtin_amdgcn_perm(b, a, sel)); };
+            dst[(2 * w) * VRW] = pack_f16(f(0x01000c0cu), f(0x05040c0cu));
+            dst[(2 * w + 1) * VRW] = pack_f16(f(0x03020c0cu), f(0x07060c0cu));
+          } else {
+            dst[(2 * w) * VRW] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+            dst[(2 * w + 1) * VRW] = __builtin_amdgcn_perm(b, a, 0x07060302u);
           }
-          dst[(2 * w) * VRW] = __builtin_amdgcn_perm(b, a, 0x05040100u);
-          dst[(2 * w + 1) * VRW] = __builtin_amdgcn_perm(b, a, 0x07060302u);
         }
       }
   }

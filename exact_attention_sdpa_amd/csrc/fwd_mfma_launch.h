@@ -29,6 +29,21 @@ template <> struct MfmaShape<32> : ShapeOf<SDPA_SHAPE_D32> {};
 template <> struct MfmaShape<64> : ShapeOf<SDPA_SHAPE_D64> {};
 template <> struct MfmaShape<128> : ShapeOf<SDPA_SHAPE_D128> {};
 
+// Packed (variable-length) batches.
+#ifndef SDPA_VARLEN_SHAPE_D32
+#define SDPA_VARLEN_SHAPE_D32 SDPA_SHAPE_D32
+#endif
+#ifndef SDPA_VARLEN_SHAPE_D64
+#define SDPA_VARLEN_SHAPE_D64 SDPA_SHAPE_D64
+#endif
+#ifndef SDPA_VARLEN_SHAPE_D128
+#define SDPA_VARLEN_SHAPE_D128 SDPA_SHAPE_D128
+#endif
+template <int D> struct VarlenShape;
+template <> struct VarlenShape<32> : ShapeOf<SDPA_VARLEN_SHAPE_D32> {};
+template <> struct VarlenShape<64> : ShapeOf<SDPA_VARLEN_SHAPE_D64> {};
+template <> struct VarlenShape<128> : ShapeOf<SDPA_VARLEN_SHAPE_D128> {};
+
 // Block-sparse shapes: 128 query rows per workgroup, one mask row, so every
 // wave of a workgroup needs the same key tiles.
 #ifndef SDPA_BSP_SHAPE_D32
@@ -80,7 +95,9 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   using S = std::conditional_t<
       VAR == kBlockSparse, BspShape<D>,
       std::conditional_t<VAR == kDropout, DropShape<D>,
-                         std::conditional_t<(VAR >= kMaskBool), MaskShape<D>, MfmaShape<D>>>>;
+                         std::conditional_t<(VAR >= kMaskBool), MaskShape<D>,
+                                            std::conditional_t<VARLEN, VarlenShape<D>,
+                                                               MfmaShape<D>>>>>;
   constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   MfmaParams p;
