@@ -29,9 +29,10 @@ def test_validation_under_asan_and_ubsan(tmp_path):
             os.path.join(CSRC, "sdpa_validate.cpp"), "-o", exe])
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+    # verify_asan_link_order=0: the environment's own preloaded libraries
+    # (if any) may come before the ASan runtime; they are left as they are
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    env.pop("LD_PRELOAD", None)
     r = subprocess.run([exe, "100000"], capture_output=True, text=True, env=env, timeout=300)
     out = r.stdout + r.stderr
     assert r.returncode == 0, out[-4000:]
