@@ -1010,18 +1010,28 @@ template <int D>
 constexpr int kDropWavesPerSimd =
     D == 32 ? SDPA_DROP_WAVES_D32 : D == 64 ? SDPA_DROP_WAVES_D64 : SDPA_DROP_WAVES_D128;
 // the elementwise-mask kernels (a tile's mask elements are held in
-// registers while it is processed)
+// registers while it is processed).  Two 8-wave workgroups share a CU only
+// at 4 waves per SIMD (at most 128 VGPRs): boolean and 16-bit additive
+// masks fit at d = 64 without spilling; f32 masks (32 more registers of
+// mask per tile) would spill 28 VGPRs and keep 3.
 #ifndef SDPA_MASK_WAVES_D32
 #define SDPA_MASK_WAVES_D32 4
 #endif
 #ifndef SDPA_MASK_WAVES_D64
-#define SDPA_MASK_WAVES_D64 3
+#define SDPA_MASK_WAVES_D64 4
 #endif
 #ifndef SDPA_MASK_WAVES_D128
 #define SDPA_MASK_WAVES_D128 2
 #endif
-// boolean masks hold a quarter of the registers of f32 ones (4 waves per
-// SIMD at d = 64 spill a few registers and still measure 13% faster than 3)
+#ifndef SDPA_MASKF_WAVES_D32
+#define SDPA_MASKF_WAVES_D32 4
+#endif
+#ifndef SDPA_MASKF_WAVES_D64
+#define SDPA_MASKF_WAVES_D64 3
+#endif
+#ifndef SDPA_MASKF_WAVES_D128
+#define SDPA_MASKF_WAVES_D128 2
+#endif
 #ifndef SDPA_MASKB_WAVES_D32
 #define SDPA_MASKB_WAVES_D32 4
 #endif
@@ -1035,6 +1045,8 @@ template <int D, int VAR>
 constexpr int kMaskWavesPerSimd =
     VAR == kMaskBool
         ? (D == 32 ? SDPA_MASKB_WAVES_D32 : D == 64 ? SDPA_MASKB_WAVES_D64 : SDPA_MASKB_WAVES_D128)
+    : VAR == kMaskAddF32
+        ? (D == 32 ? SDPA_MASKF_WAVES_D32 : D == 64 ? SDPA_MASKF_WAVES_D64 : SDPA_MASKF_WAVES_D128)
         : (D == 32 ? SDPA_MASK_WAVES_D32 : D == 64 ? SDPA_MASK_WAVES_D64 : SDPA_MASK_WAVES_D128);
 template <int D, int VAR>
 constexpr int kVariantWavesPerSimd = VAR == kBlockSparse ? kBspWavesPerSimd<D>
