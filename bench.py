@@ -894,8 +894,8 @@ def main(argv=None) -> int:
         # after the headline's timed region (never inside it)
         del q, k, v, out, lse
         rec["targets"] = {
-            "causal": time_target(torch, sdpa, inputs, np, "causal", max(a.steps, 20), 5),
-            "long": time_target(torch, sdpa, inputs, np, "long", max(3, min(a.steps, 10)), 2)}
+            "causal": time_target(torch, sdpa, inputs, np, "causal", max(a.steps, 20), 5, 50),
+            "long": time_target(torch, sdpa, inputs, np, "long", max(3, min(a.steps, 10)), 2, 10)}
     if a.cpu_budget > 0:
         rec["cpu_baseline"] = (cpu_baseline(w, a.cpu_budget, a.dropout) if a.which == "fwd"
                                else cpu_baseline_bwd(w, a.cpu_budget, WORKLOADS[a.workload],
@@ -906,11 +906,12 @@ def main(argv=None) -> int:
     return 0
 
 
-def time_target(torch, sdpa, inputs, np, name, steps, warmup):
+def time_target(torch, sdpa, inputs, np, name, steps, warmup, reps):
     """Warm kernel time of one more workload, measured like the headline:
     ``steps`` back-to-back sdpa_fwd launches between two HIP events on the
-    launch stream, after ``warmup`` launches.  bf16 inputs take an f32
-    output, as in the headline run's rule."""
+    launch stream, after ``warmup`` launches; then ``reps`` single launches
+    for the median, minimum and spread.  bf16 inputs take an f32 output, as
+    in the headline run's rule."""
     w = inputs.make_config(WORKLOADS[name])
 
     def up(x):
@@ -944,10 +945,22 @@ def time_target(torch, sdpa, inputs, np, name, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # single launches, each between its own pair of events: the spread
+    single = []
+    for _ in range(reps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        step()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        single.append(a0.elapsed_time(a1))
     tf = w.flops() / (ms * 1e-3) / 1e12
     return {"workload": describe(w, name)["workload"], "kernel_ms": round(ms, 4),
             "tflops": round(tf, 2), "frac_of_mfma_peak": round(tf / PEAK_TFLOPS, 4),
-            "steps": steps}
+            "steps": steps,
+            "single_ms": {"median": round(float(np.median(single)), 4),
+                          "min": round(float(np.min(single)), 4),
+                          "stdev": round(float(np.std(single)), 4), "reps": reps}}
 
 
 def _cpu_model() -> str:
