@@ -553,7 +553,7 @@ struct BwdDq {
 #pragma unroll
           for (int hs = 0; hs < 2; ++hs) {
             // dropout: the forward's keep decisions of these 8 keys of row
-            // qi (same lane layout as the forward), dP scaled by z/(1-p)
+            // qi (same lane layout as the forward), dP scaled by z/kappa (kappa = T/65536, the keep probability)
             uint32_t rr[4];
             if (DROP)
               philox4x32_10((uint32_t)((kb + kk * 32) >> 3) + 2 * hs + hl, (uint32_t)qi,
@@ -841,7 +841,7 @@ struct BwdDkdv {
           // query rows (register r holds query 8(r/4) + 4*hl + r%4 of the
           // block), so the matrix cores return S - lse/scale and dP - D.
           // With dropout dP starts at 0 and -D stays in registers, since
-          // dS = P (z dP / (1-p) - D) needs D on its own.
+          // dS = P (z dP / kappa - D) needs D on its own (kappa = T/65536).
           f32x16 s, dp;
           f32x4 ndv[4];
 #pragma unroll

@@ -584,7 +584,7 @@ struct MfmaFwd {
   // 2(w&1)+1): exactly the 8 keys of Philox call n = kb0/8 + 2 hs + hl of
   // row i, whose output word w carries their two 16-bit numbers (low half
   // = first key of the pair).  The row sums keep the undropped P; the
-  // 1/(1-p) scale is applied to O at the end.
+  // 65536/T scale (the inverse keep probability) is applied to O at the end.
   static __device__ __forceinline__ void drop_block(u32x4 (&pf)[NB][2], int kb0, const Ctx& x) {
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
