@@ -145,6 +145,10 @@ enum FwdVariant : int {
 #ifndef SDPA_LDS_POISON
 #define SDPA_LDS_POISON 0
 #endif
+// Build option: 16-bit outputs leave through LDS as whole-row segments.
+#ifndef SDPA_EPI_LDS
+#define SDPA_EPI_LDS 1
+#endif
 // Build option: causal dense grids in longest-processing-time order.
 #ifndef SDPA_CAUSAL_LPT
 #define SDPA_CAUSAL_LPT 1
@@ -202,6 +206,9 @@ struct MfmaFwd {
   // mask element bytes = 32-bit words a lane loads per group of 4 keys
   static constexpr int MW = VAR == kMaskBool ? 1 : VAR == kMaskAdd ? 2 : 4;
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
+  // epilogue: a wave's 16-bit output rows staged in LDS, rows padded by 16
+  // bytes (the LDS area is sized for every wave's rows)
+  static constexpr int OROW = D + 8;
   static constexpr int KB = BN / 32;       // 32-key blocks per step
   static constexpr int DS = D / 16;        // k-steps of S = Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
@@ -221,10 +228,16 @@ struct MfmaFwd {
                 "block-sparse tile shape");
   static_assert(!MASK || !VARLEN, "elementwise masks take dense layouts");
 
+  static constexpr bool EPI_LDS = SDPA_EPI_LDS && !OUTF32;
+  static constexpr int KV_BYTES = 2 * BN * KROW * 2 + 2 * D * VRW * 4;
+  static constexpr int EPI_BYTES = EPI_LDS ? NW * NB * 32 * OROW * 2 : 0;
   struct __attribute__((aligned(16))) Smem {
     uint16_t k[2][BN * KROW];
     uint32_t vt[2][D * VRW];
+    // room for the epilogue's rows where the K/V buffers are smaller
+    uint8_t pad[EPI_BYTES > KV_BYTES ? EPI_BYTES - KV_BYTES : 16];
   };
+  static_assert(!EPI_LDS || EPI_BYTES <= (int)sizeof(Smem), "epilogue rows fit in LDS");
 
   struct KRegs { u32x4 k[KPT]; };
   struct VRegs { u32x4 v0[VPT], v1[VPT]; };
@@ -930,6 +943,9 @@ struct MfmaFwd {
     }
 
     // ---- epilogue: normalise, store O and lse once
+    // (debug poisoning: the last step's poison writes end before any wave
+    // stages its output rows in LDS)
+    if (SDPA_LDS_POISON && EPI_LDS) __syncthreads();
     if (!x.wave_live) return;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
@@ -937,9 +953,39 @@ struct MfmaFwd {
       const float lt = pair_sum(S.l[qb]);
       // block-sparse or masked rows that saw no key: O = 0, lse = -inf
       const float inv = ((BSP || MASK) && !(lt > 0.f)) ? 0.f : (DROP ? p.drop_scale : 1.f) / lt;
-      if (qi < nq) {
+      if (EPI_LDS) {
+        // 16-bit output: the block's 32 rows go through this wave's own LDS
+        // area (every read of the K/V buffers ended at the last step's
+        // barrier) and leave as whole-row segments, 16 bytes per lane, so
+        // that one store covers 1 KB of rows instead of 16 bytes of each of
+        // 32 rows
+        uint16_t* ow = reinterpret_cast<uint16_t*>(&sm) + ((x.tid / 64) * NB + qb) * 32 * OROW;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dcol = db * 32 + 8 * g + 4 * x.hl;
+            const float x0 = S.o[qb][db][4 * g + 0] * inv, x1 = S.o[qb][db][4 * g + 1] * inv;
+            const float x2 = S.o[qb][db][4 * g + 2] * inv, x3 = S.o[qb][db][4 * g + 3] * inv;
+            *reinterpret_cast<u32x2*>(&ow[x.l32 * OROW + dcol]) =
+                BF16 ? u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)}
+                     : u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
+          }
+        const int lane = x.tid % 64;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          const int c = i * 64 + lane;              // 16-byte chunk of the block
+          const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+          const int qr = x.wq0 + qb * 32 + row;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&ow[row * OROW + col]);
+          if (qr < nq)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + ooff +
+                                      (int64_t)qr * ors + col) = v;
+        }
+      }
+      if (qi < nq) {
+#pragma unroll
+        for (int db = 0; db < (EPI_LDS ? 0 : DB); ++db)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int dcol = db * 32 + 8 * g + 4 * x.hl;
