@@ -344,6 +344,39 @@ __device__ __forceinline__ void store_rows(void* base, int64_t off0, int64_t rs,
     }
 }
 
+// The same rows in 16-bit types, through the wave's own LDS area `ow`
+// (32 rows of D + 8 elements; free once the kernel's last barrier has
+// passed): each lane stages its row's values, then stores 16-byte segments
+// along the rows, so that one store covers 1 KB of rows instead of 16 bytes
+// of each of 32 rows.  row0 is the wave's first row.
+template <bool BF16, int D>
+__device__ __forceinline__ void store_rows_lds(void* base, int64_t off0, int64_t rs, int row0,
+                                               int nrows, int l32, int hl,
+                                               const f32x16 (&acc)[D / 32], float mul,
+                                               uint16_t* ow) {
+  constexpr int OROW = D + 8;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = db * 32 + 8 * g + 4 * hl;
+      const float x0 = acc[db][4 * g] * mul, x1 = acc[db][4 * g + 1] * mul;
+      const float x2 = acc[db][4 * g + 2] * mul, x3 = acc[db][4 * g + 3] * mul;
+      *reinterpret_cast<u32x2*>(&ow[l32 * OROW + dcol]) =
+          BF16 ? u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)} : u32x2{pack_f16(x0, x1), pack_f16(x2, x3)};
+    }
+  const int lane = hl * 32 + l32;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int c = i * 64 + lane;   // 16-byte chunk of the wave's 32 rows
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&ow[row * OROW + col]);
+    if (row0 + row < nrows)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + off0 +
+                                (int64_t)(row0 + row) * rs + col) = v;
+  }
+}
+
 // ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false,
           bool VARLEN = false, int MK = kPlain>
@@ -591,7 +624,14 @@ struct BwdDq {
       __syncthreads();
       j = jn;
     }
-    store_rows<BF16, GF32, DB>(p.dq, qoff, un.rs, qi, nq, hl, acc, p.scale);
+    static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dQ rows fit in LDS");
+    // (the masked kernels keep direct stores: through LDS they measured
+    // 5% slower on a key-padding mask)
+    if (GF32 || MK != kPlain)
+      store_rows<BF16, GF32, DB>(p.dq, qoff, un.rs, qi, nq, hl, acc, p.scale);
+    else
+      store_rows_lds<BF16, D>(p.dq, qoff, un.rs, q0w, nq, l32, hl, acc, p.scale,
+                              reinterpret_cast<uint16_t*>(&sm) + wave * 32 * (D + 8));
   }
 };
 
@@ -931,8 +971,15 @@ struct BwdDkdv {
       __syncthreads();
       i = in_;
     }
-    store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);
-    store_rows<BF16, GF32, DB>(p.dv, kvoff, un.rs, ki, nk, hl, dv, 1.f);
+    static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dK, dV rows fit in LDS");
+    if (GF32 || MK != kPlain) {
+      store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);
+      store_rows<BF16, GF32, DB>(p.dv, kvoff, un.rs, ki, nk, hl, dv, 1.f);
+    } else {
+      uint16_t* ow = reinterpret_cast<uint16_t*>(&sm) + wave * 32 * (D + 8);
+      store_rows_lds<BF16, D>(p.dk, kvoff, un.rs, k0w, nk, l32, hl, dk, p.scale, ow);
+      store_rows_lds<BF16, D>(p.dv, kvoff, un.rs, k0w, nk, l32, hl, dv, 1.f, ow);
+    }
   }
 };
 
