@@ -99,3 +99,25 @@ def test_bad_out_view_raises():
         o = torch.empty(1, 2, 64, 64, dtype=torch.float16, device="cuda").as_strided(
             (1, 2, 64, 64), (0, 8, 8, 1))
         sdpa.scaled_dot_product_attention(q, q, q, out=o)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_out_rows_at_eight_byte_alignment(dtype, d):
+    """A 16-bit output whose row stride is a multiple of 4 elements but not
+    of 8 (the ABI's minimum): its rows start 8 bytes off a 16-byte boundary.
+    The kernel's row-segment stores must land exactly in the view, leaving
+    the padding columns between the rows untouched, and give the bits of the
+    contiguous path."""
+    B, H, N = 2, 3, 300
+    g = torch.Generator().manual_seed(d)
+    q, k, v = (torch.randn(B, H, N, d, generator=g).to(TD[dtype]).cuda() for _ in range(3))
+    base = torch.full((B, H, N, d + 4), float("nan"), dtype=TD[dtype], device="cuda")
+    yv = base[..., :d]
+    assert yv.stride()[2] % 8 == 4
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, out=yv, return_lse=True)
+    oc, lc = sdpa.scaled_dot_product_attention(q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == base.data_ptr()
+    assert torch.equal(yv, oc) and torch.equal(lse, lc)
+    assert torch.isnan(base[..., d:]).all()
