@@ -920,11 +920,12 @@ struct BwdDkdv {
             }
           }
           if (masked) {
+            // register r holds query qb + 32 kk + 4 hl + 8(r/4) + r%4, which
+            // sees key ki iff that offset is at least ki - base
+            const int lo = ki - (qb + kk * 32 + 4 * hl);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int query = qb + kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-              if (ki > query) s[r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (8 * (r / 4) + (r % 4) < lo) s[r] = -INFINITY;
           }
           uint32_t zb = 0;
           if (DROP) zb = keep_bits_of_key(qb + kk * 32, k0w, l32, hl, (uint32_t)bh, p) >> (4 * hl);

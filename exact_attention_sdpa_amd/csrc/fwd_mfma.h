@@ -548,12 +548,14 @@ struct MfmaFwd {
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
       const int qi = wq0 + qb * 32 + l32;
+      // register r holds key base + 8(r/4) + r%4; it is visible iff that
+      // offset is at most lim (below nk and, when causal, at most qi), so
+      // each score costs one compare with a constant and one select
+      const int base = kb0 + 4 * hl;
+      const int lim = CAUSAL ? min(nk - 1, qi) - base : nk - 1 - base;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + 8 * (r / 4) + 4 * hl + (r % 4);
-        const bool ok = key < nk && (!CAUSAL || key <= qi);
-        if (!ok) s[qb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) > lim) s[qb][r] = -INFINITY;
     }
   }
 
