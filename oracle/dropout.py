@@ -116,3 +116,53 @@ def sdpa_fwd_dropout_varlen(q, k, v, cu_seqlens, scale, is_causal, p, seed, offs
             O[a:b, h], L[a:b, h] = attend_dropout(q[a:b, h], k[a:b, h], v[a:b, h], scale,
                                                   is_causal, p, seed, offset, s * H + h)
     return O, L
+
+
+def attend_masked_dropout(q, k, v, scale, bias, is_causal, p, seed, offset, unit):
+    """One unit with an elementwise additive bias (the reading of
+    oracle/masked.py: s = scale q k^T + bias, -inf where a boolean mask
+    drops a pair, and the causal rule on top) and dropout on the resulting
+    softmax weights, with the keep mask z of this module for the unit:
+
+        O_i = sum_j P_ij z_ij / kappa v_j,  lse_i = ln sum_j exp(s_ij)
+
+    The mask decides which pairs take part in the softmax; dropout then
+    acts on the weights of the pairs that do, with the same draws as
+    without a mask (they depend on the pair's position only).  A row with
+    no finite score has O = 0 and lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = float(scale) * (q @ k.T) + np.asarray(bias, dtype=np.float64)
+    nq, nk = s.shape
+    if is_causal:
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
+    live = np.any(s > -np.inf, axis=1)
+    P = np.zeros_like(s)
+    lse = np.full(nq, -np.inf)
+    if np.any(live):
+        sl = s[live]
+        m = np.max(sl, axis=1, keepdims=True)   # overflow guard only
+        e = np.exp(sl - m)
+        l = np.sum(e, axis=1, keepdims=True)
+        P[live] = e / l
+        lse[live] = m[:, 0] + np.log(l[:, 0])
+    z = keep_mask(nq, nk, unit, p, seed, offset)
+    return ((P * z) / keep_probability(p)) @ v, lse
+
+
+def sdpa_fwd_masked_dropout(q, k, v, mask, kind, scale, is_causal, p, seed, offset=0):
+    """Dense q [B,H,Nq,d], k/v [B,H,Nk,d]; mask [Bm,Hm,Nq,Nk] (Bm in {1, B},
+    Hm in {1, H}), kind "bool" (nonzero = attend) or "add"; unit u = b*H + h
+    -> O, lse in float64."""
+    B, H, Nq, _ = np.shape(q)
+    m = np.asarray(mask)
+    O = np.empty((B, H, Nq, np.shape(v)[3]))
+    L = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            mu = m[b % m.shape[0], h % m.shape[1]]
+            bias = np.where(mu != 0, 0.0, -np.inf) if kind == "bool" else mu.astype(np.float64)
+            O[b, h], L[b, h] = attend_masked_dropout(q[b, h], k[b, h], v[b, h], scale, bias,
+                                                     is_causal, p, seed, offset, b * H + h)
+    return O, L

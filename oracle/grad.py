@@ -155,3 +155,52 @@ def sdpa_bwd_masked(q, k, v, do, mask, kind, scale, is_causal=False):
             dq[b, h], dk[b, h], dv[b, h] = attention_grads_biased(
                 q[b, h], k[b, h], v[b, h], do[b, h], scale, bias, is_causal)
     return dq, dk, dv
+
+
+def attention_grads_masked_dropout(q, k, v, do, scale, bias, is_causal, p, seed, offset, unit):
+    """Gradients of L = sum(dO * O) for the masked forward with dropout of
+    oracle/dropout.py (attend_masked_dropout): P the softmax of the biased,
+    causally masked scores, z the unit's keep mask, kappa the keep
+    probability.  Both the bias and z are constants, so with W = P z / kappa:
+        dV = W^T dO,  dP = (dO V^T) z / kappa,
+        dS = P (dP - rowsum(P dP)),  dQ = scale dS K,  dK = scale dS^T Q.
+    Rows with no finite score have P = 0 and contribute nothing."""
+    from .dropout import keep_mask, keep_probability
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    s = float(scale) * (q @ k.T) + np.asarray(bias, dtype=np.float64)
+    nq, nk = s.shape
+    if is_causal:
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
+    P = np.zeros_like(s)
+    live = np.any(s > -np.inf, axis=1)
+    if np.any(live):
+        sl = s[live]
+        e = np.exp(sl - np.max(sl, axis=1, keepdims=True))  # overflow guard only
+        P[live] = e / np.sum(e, axis=1, keepdims=True)
+    zr = keep_mask(nq, nk, unit, p, seed, offset) / keep_probability(p)
+    dv = (P * zr).T @ do
+    dp = (do @ v.T) * zr
+    ds = P * (dp - np.sum(P * dp, axis=1, keepdims=True))
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
+
+
+def sdpa_bwd_masked_dropout(q, k, v, do, mask, kind, scale, is_causal, p, seed, offset=0):
+    """Dense layouts; mask as sdpa_bwd_masked; unit u = b*H + h (as the
+    forward)."""
+    q = np.asarray(q)
+    B, H = q.shape[:2]
+    m = np.asarray(mask)
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(np.shape(k), dtype=np.float64)
+    dv = np.empty(np.shape(v), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            mu = m[b % m.shape[0], h % m.shape[1]]
+            bias = np.where(mu != 0, 0.0, -np.inf) if kind == "bool" else mu.astype(np.float64)
+            dq[b, h], dk[b, h], dv[b, h] = attention_grads_masked_dropout(
+                q[b, h], k[b, h], v[b, h], do[b, h], scale, bias, is_causal, p, seed, offset,
+                b * H + h)
+    return dq, dk, dv
