@@ -21,7 +21,7 @@ from ._lib import (SDPA_BF16, SDPA_BLOCK_SPARSE_BLOCK, SDPA_ERR_DEVICE,  # noqa:
                    SDPA_ERR_INVALID, SDPA_ERR_LAUNCH, SDPA_ERR_UNSUPPORTED, SDPA_F16, SDPA_F32,
                    SDPA_MASK_ADD, SDPA_MASK_ADD_F32, SDPA_MASK_BOOL, SDPA_OK, SDPA_SAME)
 
-__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports",
+__all__ = ["sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_masked_dropout", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_masked_dropout", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports",
            "sdpa_status_str", "sdpa_abi_version", "scaled_dot_product_attention",
            "scaled_dot_product_attention_backward", "attention", "SdpaError"]
 
@@ -96,6 +96,32 @@ def sdpa_fwd_masked(q, k, v, out, lse, B, H, Nq, Nk, d, q_strides, kv_strides, o
         int(d), arr(q_strides), arr(kv_strides), arr(out_strides), float(scale),
         int(is_causal), _ptr(mask), int(mask_kind), arr(mask_strides), int(dtype),
         int(out_dtype), stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
+def sdpa_fwd_masked_dropout(q, k, v, out, lse, B, H, Nq, Nk, d, q_strides, kv_strides,
+                            out_strides, scale, is_causal, mask, mask_kind, mask_strides,
+                            dropout_p, seed, offset, dtype, out_dtype, stream):
+    """Call the masked-dropout C entry point (arguments as sdpa_fwd_masked
+    and sdpa_fwd_dropout)."""
+    import ctypes
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    keep = []
+
+    def arr(s):
+        if s is None:
+            return None
+        a = (ctypes.c_int64 * 3)(*[int(x) for x in s])
+        keep.append(a)
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    st = _lib.lib().sdpa_fwd_masked_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+        int(d), arr(q_strides), arr(kv_strides), arr(out_strides), float(scale),
+        int(is_causal), _ptr(mask), int(mask_kind), arr(mask_strides), float(dropout_p),
+        int(seed), int(offset), int(dtype), int(out_dtype), stream)
     if st != SDPA_OK:
         raise SdpaError(st)
 
@@ -201,6 +227,24 @@ def sdpa_bwd_masked(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk
         raise SdpaError(st)
 
 
+def sdpa_bwd_masked_dropout(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d,
+                            scale, is_causal, mask, mask_kind, mask_strides, dropout_p, seed,
+                            offset, dtype, out_dtype, grad_dtype, stream):
+    """Call the masked-dropout backward C entry point."""
+    import ctypes
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    ms = (ctypes.c_int64 * 3)(*[int(x) for x in mask_strides])
+    st = _lib.lib().sdpa_bwd_masked_dropout(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), int(B), int(H), int(Nq), int(Nk), int(d), float(scale),
+        int(is_causal), _ptr(mask), int(mask_kind), ctypes.cast(ms, ctypes.c_void_p),
+        float(dropout_p), int(seed), int(offset), int(dtype), int(out_dtype), int(grad_dtype),
+        stream)
+    if st != SDPA_OK:
+        raise SdpaError(st)
+
+
 def sdpa_bwd_block_sparse(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d,
                           scale, is_causal, block_mask, mask_heads, dtype, out_dtype,
                           grad_dtype, stream):
@@ -273,11 +317,11 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     torch's CPU generator when None) and ``dropout_offset``.  ``attn_mask``
     (dense layouts only) is a device tensor broadcastable to [B,H,Nq,Nk]:
     torch.bool (True = attend), or additive in the input dtype or float32;
-    it runs through sdpa_fwd_masked, and rows with no finite score give
-    zeros and lse = -inf.  A mask together with packed batches, a block
-    mask or dropout, or dropout together with a block mask, is not
-    supported and raises, as the tutorial's backends do for inputs they
-    cannot serve.
+    it runs through sdpa_fwd_masked (sdpa_fwd_masked_dropout with
+    ``dropout_p`` > 0), and rows with no finite score give zeros and
+    lse = -inf.  A mask together with packed batches or a block mask, or
+    dropout together with a block mask, is not supported and raises, as the
+    tutorial's backends do for inputs they cannot serve.
 
     Dense f16/bf16 inputs that are strided views (for instance the q, k, v
     of a packed QKV projection, ``c_attn(x).chunk(3, -1)`` viewed as
@@ -295,10 +339,10 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     if not (query.is_cuda and key.is_cuda and value.is_cuda):
         raise SdpaError(SDPA_ERR_INVALID)
     if attn_mask is not None:
-        if cu_seqlens is not None or block_mask is not None or dropout_p > 0.0:
+        if cu_seqlens is not None or block_mask is not None:
             raise SdpaError(SDPA_ERR_UNSUPPORTED)
         return _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype,
-                               return_lse, stream, out)
+                               return_lse, stream, out, dropout_p, dropout_seed, dropout_offset)
     plain = cu_seqlens is None and block_mask is None and dropout_p == 0.0
     if (plain and query.dim() == 4 and key.dim() == 4 and value.dim() == 4
             and query.dtype in (torch.float16, torch.bfloat16)
@@ -453,7 +497,7 @@ def _mask_operand(attn_mask, q, B, H, Nq, Nk, no_heads=False):
 
 
 def _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype, return_lse,
-                    stream, out):
+                    stream, out, dropout_p=0.0, dropout_seed=None, dropout_offset=0):
     import torch
     squeeze = query.dim() == 3
     q, k, v = (query[:, None], key[:, None], value[:, None]) if squeeze else (query, key, value)
@@ -485,10 +529,19 @@ def _masked_forward(query, key, value, attn_mask, is_causal, scale, out_dtype, r
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if return_lse else None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    odc = _code(odt) if odt != q.dtype else SDPA_SAME
     with torch.cuda.device(q.device):
-        sdpa_fwd_masked(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3], k.stride()[:3],
-                        out.stride()[:3], scale, bool(is_causal), m4, kind, mst, _code(q.dtype),
-                        _code(odt) if odt != q.dtype else SDPA_SAME, stream)
+        if dropout_p > 0.0:
+            if dropout_seed is None:
+                dropout_seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+            sdpa_fwd_masked_dropout(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3],
+                                    k.stride()[:3], out.stride()[:3], scale, bool(is_causal), m4,
+                                    kind, mst, dropout_p, dropout_seed, dropout_offset,
+                                    _code(q.dtype), odc, stream)
+        else:
+            sdpa_fwd_masked(q, k, v, out, lse, B, H, Nq, Nk, d, q.stride()[:3], k.stride()[:3],
+                            out.stride()[:3], scale, bool(is_causal), m4, kind, mst,
+                            _code(q.dtype), odc, stream)
     if squeeze:
         out = out[:, 0]
         if lse is not None:
@@ -508,13 +561,13 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
     ``grad_dtype`` None keeps the input dtype, torch.float32 requests f32
     gradients.  After a dropout forward, pass its ``dropout_p``,
     ``dropout_seed`` and ``dropout_offset``; after a masked or block-sparse
-    forward, the same ``attn_mask`` or ``block_mask`` (dense inputs, no
-    dropout)."""
+    forward, the same ``attn_mask`` or ``block_mask`` (dense inputs; a mask
+    may come with dropout, a block mask may not)."""
     import torch
     if not (query.dtype == key.dtype == value.dtype):
         raise SdpaError(SDPA_ERR_INVALID)
     if (attn_mask is not None or block_mask is not None) and (
-            cu_seqlens is not None or dropout_p > 0.0
+            cu_seqlens is not None or (block_mask is not None and dropout_p > 0.0)
             or (attn_mask is not None and block_mask is not None)):
         raise SdpaError(SDPA_ERR_UNSUPPORTED)
     if cu_seqlens is not None:
@@ -560,8 +613,15 @@ def scaled_dot_product_attention_backward(query, key, value, out, lse, grad_out,
             return dq, dk, dv
         if attn_mask is not None:
             m4, kind, mst = _mask_operand(attn_mask, q, B, H, Nq, Nk)
-            sdpa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
-                            bool(is_causal), m4, kind, mst, dt, odc, gdc, stream)
+            if dropout_p > 0.0:
+                if dropout_seed is None:
+                    raise SdpaError(SDPA_ERR_INVALID)   # the forward's seed is needed
+                sdpa_bwd_masked_dropout(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d,
+                                        scale, bool(is_causal), m4, kind, mst, dropout_p,
+                                        dropout_seed, dropout_offset, dt, odc, gdc, stream)
+            else:
+                sdpa_bwd_masked(q, k, v, o, do, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
+                                bool(is_causal), m4, kind, mst, dt, odc, gdc, stream)
             return dq, dk, dv
         if dropout_p > 0.0:
             if dropout_seed is None:

@@ -15,8 +15,11 @@ SDPA_MASK_BOOL, SDPA_MASK_ADD, SDPA_MASK_ADD_F32 = 0, 1, 2
 SDPA_BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd",
-           "sdpa_bwd_dropout", "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes", "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
+EXPORTS = ("sdpa_fwd", "sdpa_fwd_strided", "sdpa_fwd_masked", "sdpa_fwd_masked_dropout",
+           "sdpa_fwd_block_sparse", "sdpa_fwd_dropout", "sdpa_bwd", "sdpa_bwd_dropout",
+           "sdpa_bwd_packed", "sdpa_bwd_masked", "sdpa_bwd_masked_dropout",
+           "sdpa_bwd_block_sparse", "sdpa_bwd_noalloc", "sdpa_bwd_workspace_bytes",
+           "sdpa_supports", "sdpa_status_str", "sdpa_abi_version")
 
 # the same library built with the LDS-poisoning debug option
 LIB_DEBUG_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsdpa_debug.so")
@@ -57,6 +60,11 @@ def _load(path: str) -> ctypes.CDLL:
     L.sdpa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
                                   ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
                                   ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_fwd_masked_dropout.restype = ctypes.c_int
+    L.sdpa_fwd_masked_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                          ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
+                                          ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32,
+                                          ctypes.c_int, ctypes.c_int, vp]
     L.sdpa_fwd_block_sparse.restype = ctypes.c_int
     L.sdpa_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                         ctypes.c_float, ctypes.c_int, vp, i64, ctypes.c_int,
@@ -83,6 +91,12 @@ def _load(path: str) -> ctypes.CDLL:
     L.sdpa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                   i64, ctypes.c_float, ctypes.c_int, vp, ctypes.c_int, vp,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    L.sdpa_bwd_masked_dropout.restype = ctypes.c_int
+    L.sdpa_bwd_masked_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                                          i64, i64, ctypes.c_float, ctypes.c_int, vp,
+                                          ctypes.c_int, vp, ctypes.c_float, ctypes.c_uint64,
+                                          ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, vp]
     L.sdpa_bwd_block_sparse.restype = ctypes.c_int
     L.sdpa_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64,
                                         i64, i64, ctypes.c_float, ctypes.c_int, vp, i64,

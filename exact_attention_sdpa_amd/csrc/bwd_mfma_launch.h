@@ -40,6 +40,16 @@ template <> hipError_t launch_bwd_masked_tiles<true, 32>(const BwdArgs&, const B
 template <> hipError_t launch_bwd_masked_tiles<true, 64>(const BwdArgs&, const BwdParams&);
 template <> hipError_t launch_bwd_masked_tiles<true, 128>(const BwdArgs&, const BwdParams&);
 
+// Elementwise mask together with dropout.  Defined in bwd_mfma_maskdrop_*.hip.
+template <bool BF16, int D>
+hipError_t launch_bwd_masked_drop_tiles(const BwdArgs& a, const BwdParams& p);
+template <> hipError_t launch_bwd_masked_drop_tiles<false, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_drop_tiles<false, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_drop_tiles<false, 128>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_drop_tiles<true, 32>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_drop_tiles<true, 64>(const BwdArgs&, const BwdParams&);
+template <> hipError_t launch_bwd_masked_drop_tiles<true, 128>(const BwdArgs&, const BwdParams&);
+
 // Block-sparse backward (dense layouts, no dropout).  Defined in
 // bwd_mfma_mask_*.hip.
 template <bool BF16, int D>
@@ -60,15 +70,17 @@ hipError_t launch_bwd_bsp_tiles_impl(const BwdArgs& a, const BwdParams& p) {
                     : launch_bwd_tiles<BF16, D, false, false, false, false, kBlockSparse>(a, p);
 }
 
-template <bool BF16, int D>
+// DROP: the mask together with dropout (compiled in translation units of
+// their own).
+template <bool BF16, int D, bool DROP = false>
 hipError_t launch_bwd_masked_tiles_impl(const BwdArgs& a, const BwdParams& p) {
-#define SDPA_MBCASE(KIND, MK)                                                             \
-  if (a.amask_kind == KIND) {                                                            \
-    if (a.causal)                                                                        \
-      return a.grad_f32 ? launch_bwd_tiles<BF16, D, true, true, false, false, MK>(a, p)   \
-                        : launch_bwd_tiles<BF16, D, true, false, false, false, MK>(a, p); \
-    return a.grad_f32 ? launch_bwd_tiles<BF16, D, false, true, false, false, MK>(a, p)    \
-                      : launch_bwd_tiles<BF16, D, false, false, false, false, MK>(a, p);  \
+#define SDPA_MBCASE(KIND, MK)                                                            \
+  if (a.amask_kind == KIND) {                                                           \
+    if (a.causal)                                                                       \
+      return a.grad_f32 ? launch_bwd_tiles<BF16, D, true, true, DROP, false, MK>(a, p)   \
+                        : launch_bwd_tiles<BF16, D, true, false, DROP, false, MK>(a, p); \
+    return a.grad_f32 ? launch_bwd_tiles<BF16, D, false, true, DROP, false, MK>(a, p)    \
+                      : launch_bwd_tiles<BF16, D, false, false, DROP, false, MK>(a, p);  \
   }
   SDPA_MBCASE(SDPA_MASK_BOOL, kMaskBool)
   SDPA_MBCASE(SDPA_MASK_ADD, kMaskAdd)
@@ -124,6 +136,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
   if (e != hipSuccess) return e;
   if (with_mask)
     return a.bmask != nullptr ? launch_bwd_bsp_tiles<BF16, D>(a, p)
+           : a.dropout        ? launch_bwd_masked_drop_tiles<BF16, D>(a, p)
                               : launch_bwd_masked_tiles<BF16, D>(a, p);
   const bool varlen = a.cu != nullptr;
 #define SDPA_BCASE(C, G, X, V)                                                \

@@ -125,8 +125,14 @@ enum FwdVariant : int {
   kDropout = 2,
   kMaskBool = 3,
   kMaskAdd = 4,
-  kMaskAddF32 = 5
+  kMaskAddF32 = 5,
+  // an elementwise mask together with dropout (kind + 3)
+  kMaskBoolDrop = 6,
+  kMaskAddDrop = 7,
+  kMaskAddF32Drop = 8
 };
+// the mask kind of a variant (kMaskBool / kMaskAdd / kMaskAddF32), else VAR
+constexpr int mask_kind_of(int var) { return var >= kMaskBoolDrop ? var - 3 : var; }
 
 // Build option: raise the wave priority while it issues matrix-core work
 // (measured a few percent faster on MI355X).
@@ -201,10 +207,11 @@ template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bo
           int VAR = kPlain>
 struct MfmaFwd {
   static constexpr bool BSP = VAR == kBlockSparse;
-  static constexpr bool DROP = VAR == kDropout;
+  static constexpr int MK = mask_kind_of(VAR);
+  static constexpr bool DROP = VAR == kDropout || VAR >= kMaskBoolDrop;
   static constexpr bool MASK = VAR >= kMaskBool;
   // mask element bytes = 32-bit words a lane loads per group of 4 keys
-  static constexpr int MW = VAR == kMaskBool ? 1 : VAR == kMaskAdd ? 2 : 4;
+  static constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
   static constexpr int BM = NW * NB * 32;  // query rows per workgroup
   // epilogue: a wave's 16-bit output rows staged in LDS, rows padded by 16
   // bytes (the LDS area is sized for every wave's rows)
@@ -503,12 +510,12 @@ struct MfmaFwd {
   static __device__ __forceinline__ float mask_score(float s, float c, float mref,
                                                      const uint32_t (&w)[4][MW], int r) {
     const int g = r / 4, e = r % 4;
-    if (VAR == kMaskBool) {
+    if (MK == kMaskBool) {
       const uint32_t byte = (w[g][0] >> (8 * e)) & 0xffu;
       return byte != 0u ? __builtin_fmaf(s, c, -mref) : -INFINITY;
     }
     float a;
-    if (VAR == kMaskAdd) {
+    if (MK == kMaskAdd) {
       const uint32_t h = (w[g][e / 2] >> (16 * (e & 1))) & 0xffffu;
       a = BF16 ? __uint_as_float(h << 16)
                : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
@@ -759,7 +766,7 @@ struct MfmaFwd {
     // adds nothing (its P would be exactly 0), so the wave skips it, e.g.
     // the keys past a sequence's end under a key-padding mask
     bool run_tile = live;
-    if (VAR == kMaskBool && SDPA_MASK_SKIP && live) {
+    if (MK == kMaskBool && SDPA_MASK_SKIP && live) {
       uint32_t any = 0;
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk)
@@ -1091,16 +1098,19 @@ constexpr int kDropWavesPerSimd =
 #endif
 template <int D, int VAR>
 constexpr int kMaskWavesPerSimd =
-    VAR == kMaskBool
+    mask_kind_of(VAR) == kMaskBool
         ? (D == 32 ? SDPA_MASKB_WAVES_D32 : D == 64 ? SDPA_MASKB_WAVES_D64 : SDPA_MASKB_WAVES_D128)
-    : VAR == kMaskAddF32
+    : mask_kind_of(VAR) == kMaskAddF32
         ? (D == 32 ? SDPA_MASKF_WAVES_D32 : D == 64 ? SDPA_MASKF_WAVES_D64 : SDPA_MASKF_WAVES_D128)
         : (D == 32 ? SDPA_MASK_WAVES_D32 : D == 64 ? SDPA_MASK_WAVES_D64 : SDPA_MASK_WAVES_D128);
+// a 16-bit additive mask with dropout holds both register sets: it takes
+// the f32 masks' bound (4 waves per SIMD at d = 64 would spill)
 template <int D, int VAR>
-constexpr int kVariantWavesPerSimd = VAR == kBlockSparse ? kBspWavesPerSimd<D>
-                                     : VAR == kDropout   ? kDropWavesPerSimd<D>
-                                     : VAR >= kMaskBool  ? kMaskWavesPerSimd<D, VAR>
-                                                         : kWavesPerSimd<D>;
+constexpr int kVariantWavesPerSimd = VAR == kBlockSparse  ? kBspWavesPerSimd<D>
+                                     : VAR == kDropout    ? kDropWavesPerSimd<D>
+                                     : VAR == kMaskAddDrop ? kMaskWavesPerSimd<D, kMaskAddF32>
+                                     : VAR >= kMaskBool   ? kMaskWavesPerSimd<D, VAR>
+                                                          : kWavesPerSimd<D>;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
           int VAR = kPlain>

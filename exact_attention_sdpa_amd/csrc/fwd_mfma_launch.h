@@ -198,6 +198,18 @@ hipError_t launch_mfma_masked_d(const FwdArgs& a) {
   SDPA_MCASE(SDPA_MASK_BOOL, kMaskBool)
   SDPA_MCASE(SDPA_MASK_ADD, kMaskAdd)
   SDPA_MCASE(SDPA_MASK_ADD_F32, kMaskAddF32)
+  return hipErrorInvalidValue;
+}
+
+// An elementwise mask together with dropout (dense layouts, any strides):
+// the mask shapes, one instantiation per mask kind, causal flag and output
+// type (compiled in translation units of their own).
+template <bool BF16, int D>
+hipError_t launch_mfma_masked_drop_d(const FwdArgs& a) {
+  if (a.cu != nullptr || a.amask == nullptr || !a.dropout) return hipErrorInvalidValue;
+  SDPA_MCASE(SDPA_MASK_BOOL, kMaskBoolDrop)
+  SDPA_MCASE(SDPA_MASK_ADD, kMaskAddDrop)
+  SDPA_MCASE(SDPA_MASK_ADD_F32, kMaskAddF32Drop)
 #undef SDPA_MCASE
   return hipErrorInvalidValue;
 }

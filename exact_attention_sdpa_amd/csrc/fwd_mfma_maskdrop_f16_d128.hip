@@ -1,0 +1,7 @@
+// Instantiations of the matrix-core forward with an elementwise mask and
+// dropout: f16 inputs, head dim 128.
+#include "fwd_mfma_launch.h"
+
+namespace sdpa {
+template hipError_t launch_mfma_masked_drop_d<false, 128>(const FwdArgs&);
+}  // namespace sdpa

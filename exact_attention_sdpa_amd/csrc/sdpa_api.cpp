@@ -92,6 +92,33 @@ sdpa_status sdpa_fwd_masked(const void* q, const void* k, const void* v, void* o
   return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
 }
 
+sdpa_status sdpa_fwd_masked_dropout(const void* q, const void* k, const void* v, void* out,
+                                    float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                    int64_t d, const int64_t* q_strides,
+                                    const int64_t* kv_strides, const int64_t* out_strides,
+                                    float scale, int is_causal, const void* mask,
+                                    sdpa_mask_kind mask_kind, const int64_t* mask_strides,
+                                    float dropout_p, uint64_t seed, uint32_t offset,
+                                    sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream) {
+  const bool strided = q_strides != nullptr || kv_strides != nullptr || out_strides != nullptr;
+  sdpa::FwdArgs a;
+  const sdpa_status st = sdpa::validate(q, k, v, out, lse, B, H, Nq, Nk, d, scale, is_causal,
+                                        nullptr, dtype, out_dtype, stream, &a, !strided);
+  if (st != SDPA_OK) return st;
+  if (strided) {
+    const sdpa_status ss = sdpa::validate_strides(q_strides, kv_strides, out_strides, &a);
+    if (ss != SDPA_OK) return ss;
+  }
+  const sdpa_status sm = sdpa::validate_attn_mask(mask, mask_kind, mask_strides, &a);
+  if (sm != SDPA_OK) return sm;
+  const sdpa_status sd = sdpa::validate_dropout(dropout_p, seed, offset, &a);
+  if (sd != SDPA_OK) return sd;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_fwd_mfma_masked_bf16(a)
+                                          : sdpa::launch_fwd_mfma_masked_f16(a);
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
 sdpa_status sdpa_fwd_block_sparse(const void* q, const void* k, const void* v, void* out,
                                   float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                                   int64_t d, float scale, int is_causal,
@@ -175,6 +202,29 @@ sdpa_status sdpa_bwd_masked(const void* q, const void* k, const void* v, const v
   if (st != SDPA_OK) return st;
   const sdpa_status sm = sdpa::validate_bwd_attn_mask(mask, mask_kind, mask_strides, &a);
   if (sm != SDPA_OK) return sm;
+  if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
+  const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bwd_mfma_masked_bf16(a)
+                                          : sdpa::launch_bwd_mfma_masked_f16(a);
+  return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;
+}
+
+sdpa_status sdpa_bwd_masked_dropout(const void* q, const void* k, const void* v, const void* out,
+                                    const void* dout, const float* lse, void* dq, void* dk,
+                                    void* dv, float* workspace, int64_t B, int64_t H, int64_t Nq,
+                                    int64_t Nk, int64_t d, float scale, int is_causal,
+                                    const void* mask, sdpa_mask_kind mask_kind,
+                                    const int64_t* mask_strides, float dropout_p, uint64_t seed,
+                                    uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
+                                    sdpa_dtype grad_dtype, void* stream) {
+  sdpa::BwdArgs a;
+  const sdpa_status st =
+      sdpa::validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
+                         is_causal, dtype, out_dtype, grad_dtype, stream, &a);
+  if (st != SDPA_OK) return st;
+  const sdpa_status sm = sdpa::validate_bwd_attn_mask(mask, mask_kind, mask_strides, &a);
+  if (sm != SDPA_OK) return sm;
+  const sdpa_status sd = sdpa::validate_bwd_dropout(dropout_p, seed, offset, &a);
+  if (sd != SDPA_OK) return sd;
   if (!current_device_is_gfx950()) return SDPA_ERR_DEVICE;
   const hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_bwd_mfma_masked_bf16(a)
                                           : sdpa::launch_bwd_mfma_masked_f16(a);

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SDPA_ABI_VERSION 11
+#define SDPA_ABI_VERSION 12
 
 #if defined(__GNUC__)
 #define SDPA_API __attribute__((visibility("default")))
@@ -248,6 +248,31 @@ SDPA_API sdpa_status sdpa_fwd_dropout(const void* q, const void* k, const void* 
                                       uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype,
                                       void* stream);
 
+/* Forward with an elementwise attention mask and dropout together: the
+ * tutorial's module in training on padded batches passes both.  The mask
+ * decides which pairs enter the softmax, exactly as in sdpa_fwd_masked;
+ * dropout then acts on the resulting weights with the draws and scaling of
+ * sdpa_fwd_dropout (the draws depend only on the pair's position, so a
+ * mask changes none of them):
+ *     P = softmax(scale q k^T + a),  O_i = sum_j P_ij z_ij / kappa v_j,
+ *     lse = that of the masked scores (undropped).
+ * A row whose every score is -inf gets out = 0 and lse = -inf.
+ *
+ * mask, mask_kind, mask_strides  as sdpa_fwd_masked.
+ * dropout_p, seed, offset  as sdpa_fwd_dropout (unit u = b*H + h).
+ * q_strides, kv_strides, out_strides  all NULL or all given, as
+ *           sdpa_fwd_masked.  Other arguments as sdpa_fwd; dense layouts,
+ *           dtype SDPA_F16 or SDPA_BF16.
+ * Returns the errors of sdpa_fwd_masked and sdpa_fwd_dropout; p = 0 is
+ * exactly sdpa_fwd_masked.
+ */
+SDPA_API sdpa_status sdpa_fwd_masked_dropout(
+    const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+    int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides, const int64_t* kv_strides,
+    const int64_t* out_strides, float scale, int is_causal, const void* mask,
+    sdpa_mask_kind mask_kind, const int64_t* mask_strides, float dropout_p, uint64_t seed,
+    uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype, void* stream);
+
 /* Backward pass of sdpa_fwd: the gradients dq, dk, dv of sum(dout * out)
  * with respect to q, k and v.  The FlashAttention article (method
  * paragraph) names recomputation in the backward pass as its second
@@ -328,6 +353,24 @@ SDPA_API sdpa_status sdpa_bwd_masked(const void* q, const void* k, const void* v
                                      int is_causal, const void* mask, sdpa_mask_kind mask_kind,
                                      const int64_t* mask_strides, sdpa_dtype dtype,
                                      sdpa_dtype out_dtype, sdpa_dtype grad_dtype, void* stream);
+
+/* Backward pass of sdpa_fwd_masked_dropout: the gradients of
+ * sum(dout * out) with the mask's bias and the dropout mask z constants:
+ *     P = softmax(scale q k^T + a),  W = P z / kappa,  dV = W^T dO,
+ *     dP = (dO V^T) z / kappa,  dS = P (dP - rowsum(dO * O)),
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ * `out` and `lse` are the forward's; z is regenerated from the same
+ * dropout_p, seed and offset.  mask arguments as sdpa_bwd_masked, dropout
+ * arguments as sdpa_bwd_dropout, the rest as sdpa_bwd.  p = 0 is exactly
+ * sdpa_bwd_masked.
+ */
+SDPA_API sdpa_status sdpa_bwd_masked_dropout(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv, float* workspace, int64_t B, int64_t H,
+    int64_t Nq, int64_t Nk, int64_t d, float scale, int is_causal, const void* mask,
+    sdpa_mask_kind mask_kind, const int64_t* mask_strides, float dropout_p, uint64_t seed,
+    uint32_t offset, sdpa_dtype dtype, sdpa_dtype out_dtype, sdpa_dtype grad_dtype,
+    void* stream);
 
 /* Backward pass of sdpa_fwd_block_sparse: the gradients of sum(dout * out)
  * for exact attention restricted to the pairs the block mask keeps (the

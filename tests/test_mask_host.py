@@ -1,4 +1,5 @@
-"""Host-side checks of the elementwise-mask entry point (sdpa_fwd_masked):
+"""Host-side checks of the elementwise-mask entry points (sdpa_fwd_masked,
+sdpa_bwd_masked and their dropout forms):
 every malformed call is rejected before any device work."""
 import ctypes
 
@@ -89,3 +90,40 @@ def test_masked_backward_rejected_on_host(lib):
     assert bcall(lib, mask=0x7000000) == INVALID      # overlaps dq
     # a unit's mask beyond 32-bit offsets
     assert bcall(lib, kind=MF32, ms=(0, 0, 1 << 19), N=1024) == UNSUPPORTED
+
+
+def dcall(lib, p=0.1, ms=(4 * 128 * 128, 128 * 128, 128), kind=MBOOL, mask=M, dt=F16, d=64,
+          causal=0, o=O, lse=L):
+    return lib.sdpa_fwd_masked_dropout(Q, K, V, o, lse, 2, 4, 128, 128, d, None, None, None,
+                                       0.125, causal, mask, kind, arr(ms), p, 7, 3, dt, SAME,
+                                       None)
+
+
+def dbcall(lib, p=0.1, ms=(4 * 128 * 128, 128 * 128, 128), kind=MBOOL, mask=M, dt=F16):
+    return lib.sdpa_bwd_masked_dropout(Q, K, V, O, 0x5000000, L, 0x7000000, 0x7800000,
+                                       0x8000000, 0x9000000, 2, 4, 128, 128, 64, 0.125, 0, mask,
+                                       kind, arr(ms), p, 7, 3, dt, SAME, SAME, None)
+
+
+def test_masked_dropout_calls_on_host(lib):
+    """sdpa_fwd_masked_dropout / sdpa_bwd_masked_dropout: the mask checks
+    and the dropout checks both apply."""
+    for kind in (MBOOL, MADD, MF32):
+        for p in (0.0, 0.1, 0.999):
+            assert dcall(lib, p=p, kind=kind) in (OK, DEVICE)
+            assert dbcall(lib, p=p, kind=kind) in (OK, DEVICE)
+        assert dcall(lib, kind=kind, causal=1) in (OK, DEVICE)
+    for f in (dcall, dbcall):
+        assert f(lib, mask=None) == INVALID
+        assert f(lib, ms=None) == INVALID
+        assert f(lib, kind=5) == INVALID
+        assert f(lib, ms=(0, 0, 130)) == INVALID
+        assert f(lib, kind=MF32, mask=M + 4) == INVALID
+        assert f(lib, dt=F32) == UNSUPPORTED
+        for p in (1.0, -0.1, 1.5, float("nan")):
+            assert f(lib, p=p) == INVALID
+        assert f(lib, p=float(1 - 2 ** -18)) == UNSUPPORTED   # nothing would be kept
+    assert dcall(lib, mask=O) == INVALID
+    assert dcall(lib, mask=L) == INVALID
+    assert dcall(lib, d=48) == UNSUPPORTED
+    assert dbcall(lib, mask=0x9000000) == INVALID      # overlaps the workspace

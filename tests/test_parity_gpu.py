@@ -294,8 +294,9 @@ def test_unsupported_raises():
         S.scaled_dot_product_attention(q32h, q32h, q32h,
                                        attn_mask=torch.ones(8, 8, dtype=torch.float64,
                                                             device="cuda"))
-    with pytest.raises(S.SdpaError):     # a mask together with dropout
-        S.scaled_dot_product_attention(q32h, q32h, q32h, dropout_p=0.1,
+    with pytest.raises(S.SdpaError):     # a mask with dropout needs f16/bf16 inputs too
+        q32 = q[..., :32].float()
+        S.scaled_dot_product_attention(q32, q32, q32, dropout_p=0.1,
                                        attn_mask=torch.ones(8, 8, dtype=torch.bool,
                                                             device="cuda"))
     with pytest.raises(S.SdpaError):     # a mask that does not broadcast to [B,H,Nq,Nk]

@@ -16,7 +16,8 @@ families of ``inputs.make_rescale`` do:
 
 Each runs on f16 and bf16, d in {32, 64, 128}, causal on and off, through
 the plain, packed, block-sparse, elementwise-mask (boolean, additive in the
-input type, additive f32) and dropout (dense and packed) entry points,
+input type, additive f32), dropout (dense and packed) and mask-with-dropout
+entry points,
 compared element by element at the tolerances of tests/gpu_util.py.
 
 Outputs are f32 for both input types: these rows concentrate their weight
@@ -38,7 +39,8 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 VARIANTS = ["plain", "varlen", "block_sparse", "mask_bool", "mask_add", "mask_add_f32",
-            "dropout", "dropout_varlen"]
+            "dropout", "dropout_varlen", "mask_bool_dropout", "mask_add_dropout",
+            "mask_add_f32_dropout"]
 
 # per family: (query rows = keys per unit, heads); ``rising`` spans > 2048 keys
 DENSE_N = {"late": (520, 2), "rising": (2090, 1), "low_first": (520, 2)}
@@ -72,15 +74,16 @@ def _run_case(family, variant, dtype, d, causal):
               out_dtype=torch.float32 if out_f32 else None)
     if w.varlen:
         kw.update(cu_seqlens=torch.from_numpy(w.cu_seqlens).cuda(), max_seqlen=w.Nq)
-    if variant.startswith("dropout"):
+    drop = "dropout" in variant
+    if drop:
         kw.update(dropout_p=DROP_P, dropout_seed=DROP_SEED, dropout_offset=DROP_OFF)
     mask = kind = None
     if variant == "block_sparse":
         mask = inputs.make_block_mask(w.H, w.Nq, w.Nk, 0.5, diagonal=True, seed=seed, cfg=122)
         kw["block_mask"] = torch.from_numpy(mask).cuda()
     elif variant.startswith("mask"):
-        kind = "bool" if variant == "mask_bool" else "add"
-        mdt = "f32" if variant == "mask_add_f32" else dtype
+        kind = "bool" if variant.startswith("mask_bool") else "add"
+        mdt = "f32" if variant.startswith("mask_add_f32") else dtype
         mask = inputs.make_attn_mask((w.B, w.H, w.Nq, w.Nk), kind, keep=0.8, bias_std=2.0,
                                      seed=seed, cfg=123, dtype=mdt)
         kw["attn_mask"] = (torch.from_numpy(mask).cuda().bool() if kind == "bool"
@@ -104,13 +107,18 @@ def _run_case(family, variant, dtype, d, causal):
         ref, lref = obsp.sdpa_fwd_block_sparse(w.q64, w.k64, w.v64, mask, w.scale, causal)
     else:
         m64 = mask if kind == "bool" else inputs.storage_to_f64(
-            mask, "f32" if variant == "mask_add_f32" else dtype)
-        ref, lref = oracle.sdpa_fwd_masked(w.q64, w.k64, w.v64, m64, kind, w.scale, causal)
+            mask, "f32" if variant.startswith("mask_add_f32") else dtype)
+        if drop:
+            ref, lref = odrop.sdpa_fwd_masked_dropout(w.q64, w.k64, w.v64, m64, kind, w.scale,
+                                                      causal, DROP_P, DROP_SEED, DROP_OFF)
+        else:
+            ref, lref = oracle.sdpa_fwd_masked(w.q64, w.k64, w.v64, m64, kind, w.scale, causal)
 
     live = _check_empty_rows(o, l, lref, what)
-    if variant.startswith("dropout"):
+    if drop:
         # kept weights are scaled by 1/(1-p), and so is the f16 rounding of P
-        m = G.assert_parity(o * (1 - DROP_P), ref * (1 - DROP_P), dtype, what, l, lref)
+        m = G.assert_parity(o[live] * (1 - DROP_P), ref[live] * (1 - DROP_P), dtype, what,
+                            l[live], lref[live])
     elif np.all(live):
         m = G.assert_parity(o, ref, dtype, what, l, lref)
     else:
