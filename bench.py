@@ -16,7 +16,8 @@ per sequence for packed batches; 4*d per visible (query, key) pair for the
 block-sparse workload, which calls sdpa_fwd_block_sparse; every pair for the
 elementwise-mask workloads, which call sdpa_fwd_masked and compute every
 pair).  `--dropout P`
-times sdpa_fwd_dropout instead (same FLOPs).  `roofline.achieved` divides the
+times sdpa_fwd_dropout instead (sdpa_fwd_masked_dropout on the
+elementwise-mask workloads; same FLOPs).  `roofline.achieved` divides the
 same FLOPs by the kernel's own average duration from HIP events recorded around
 each launch on the launch stream; the peak is MI355X's published dense
 fp16/bf16 matrix rate, 2.5 PFLOP/s.  `cpu_baseline` times the fp64 CPU
@@ -146,10 +147,10 @@ def cpu_baseline(w, budget_s: float, dropout: float = 0.0):
         threads = 1
     if w.block_mask is not None:
         return _cpu_baseline_block_sparse(w, budget_s, threads)
+    if w.attn_mask is not None:
+        return _cpu_baseline_masked(w, budget_s, threads, dropout)
     if dropout > 0:
         return _cpu_baseline_dropout(w, budget_s, threads, dropout)
-    if w.attn_mask is not None:
-        return _cpu_baseline_masked(w, budget_s, threads)
     flops = 0.0
     n = 0
     t0 = time.perf_counter()
@@ -219,12 +220,14 @@ def _cpu_baseline_block_sparse(w, budget_s, threads):
             "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def _cpu_baseline_masked(w, budget_s, threads):
-    """The fp64 masked oracle on whole (batch, head) units in turn, FLOPs
-    counted as the metric does (every pair)."""
+def _cpu_baseline_masked(w, budget_s, threads, dropout=0.0):
+    """The fp64 masked oracle (the mask-with-dropout one when ``dropout`` >
+    0) on whole (batch, head) units in turn, FLOPs counted as the metric
+    does (every pair)."""
     import numpy as np
 
     from exact_attention_sdpa_amd import inputs
+    from oracle import dropout as odrop
     from oracle import masked as om
     m = w.attn_mask
     m = m.reshape((1,) * (4 - m.ndim) + m.shape)
@@ -236,8 +239,12 @@ def _cpu_baseline_masked(w, budget_s, threads):
         mu = m[b % m.shape[0], h % m.shape[1]]
         mu = mu if w.mask_kind == "bool" else inputs.storage_to_f64(mu, w.dtype)
         mu = np.broadcast_to(mu, (w.Nq, w.Nk))
-        om.sdpa_fwd_masked(dec(w.q), dec(w.k), dec(w.v), mu[None, None], w.mask_kind,
-                           w.scale, w.is_causal)
+        if dropout > 0:
+            odrop.sdpa_fwd_masked_dropout(dec(w.q), dec(w.k), dec(w.v), mu[None, None],
+                                          w.mask_kind, w.scale, w.is_causal, dropout, 2023)
+        else:
+            om.sdpa_fwd_masked(dec(w.q), dec(w.k), dec(w.v), mu[None, None], w.mask_kind,
+                               w.scale, w.is_causal)
         flops += 4.0 * w.Nq * w.Nk * w.d / (2 if w.is_causal else 1)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -311,9 +318,13 @@ def cpu_baseline_bwd(w, budget_s, cfg, dropout=0.0):
             m4 = w.attn_mask.reshape((1,) * (4 - w.attn_mask.ndim) + w.attn_mask.shape)
             mu = m4[b % m4.shape[0], h % m4.shape[1]]
             mu = mu if w.mask_kind == "bool" else inputs.storage_to_f64(mu, w.dtype)
-            oracle.sdpa_bwd_masked(dec(w.q), dec(w.k), dec(w.v), dec(do),
-                                   np.broadcast_to(mu, (w.Nq, w.Nk))[None, None], w.mask_kind,
-                                   w.scale, w.is_causal)
+            mu = np.broadcast_to(mu, (w.Nq, w.Nk))[None, None]
+            if dropout > 0:
+                oracle.sdpa_bwd_masked_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), mu,
+                                               w.mask_kind, w.scale, w.is_causal, dropout, 2023)
+            else:
+                oracle.sdpa_bwd_masked(dec(w.q), dec(w.k), dec(w.v), dec(do), mu, w.mask_kind,
+                                       w.scale, w.is_causal)
         elif dropout > 0:
             oracle.sdpa_bwd_dropout(dec(w.q), dec(w.k), dec(w.v), dec(do), w.scale, w.is_causal,
                                     dropout, 2023, 0)
@@ -622,8 +633,8 @@ def main(argv=None) -> int:
                     help="time the forward (default, the headline metric) or the backward "
                          "pass (sdpa_bwd: dQ, dK, dV; dense workloads)")
     ap.add_argument("--dropout", type=float, default=0.0,
-                    help="dropout rate on the attention weights (sdpa_fwd_dropout; dense and "
-                         "packed workloads)")
+                    help="dropout rate on the attention weights (sdpa_fwd_dropout on dense and "
+                         "packed workloads, sdpa_fwd_masked_dropout on masked ones)")
     ap.add_argument("--cold-reps", type=int, default=None,
                     help="launches timed with cold caches (a 512 MiB write before each); "
                          "default 50, 10 for the 64k-token workloads, 0 = skip")
@@ -725,9 +736,6 @@ def main(argv=None) -> int:
 
     if w.attn_mask is not None:
         import ctypes
-        if a.dropout > 0:
-            print("bench.py: dropout with an elementwise mask is not supported", file=sys.stderr)
-            return 2
         m = w.attn_mask
         m = m.reshape((1,) * (4 - m.ndim) + m.shape)
         mt = (torch.from_numpy(np.ascontiguousarray(m)).cuda() if w.mask_kind == "bool"
@@ -742,6 +750,14 @@ def main(argv=None) -> int:
             st = L.sdpa_fwd_masked(*margs)
             if st != 0:
                 raise sdpa.SdpaError(st)
+
+        if a.dropout > 0:
+            mdargs = margs[:18] + [float(a.dropout), 2023, 0] + margs[18:]
+
+            def step():  # noqa: F811 -- the mask-with-dropout entry point
+                st = L.sdpa_fwd_masked_dropout(*mdargs)
+                if st != 0:
+                    raise sdpa.SdpaError(st)
 
     if a.which == "bwd":
         step()   # the forward's out and lse feed the backward
@@ -780,6 +796,14 @@ def main(argv=None) -> int:
                 st = L.sdpa_bwd_masked(*margs_b)
                 if st != 0:
                     raise sdpa.SdpaError(st)
+
+            if a.dropout > 0:
+                mdargs_b = margs_b[:20] + [float(a.dropout), 2023, 0] + margs_b[20:]
+
+                def step():  # noqa: F811 -- the mask-with-dropout backward
+                    st = L.sdpa_bwd_masked_dropout(*mdargs_b)
+                    if st != 0:
+                        raise sdpa.SdpaError(st)
 
         if w.varlen:
             T = int(w.cu_seqlens[-1])
