@@ -525,7 +525,7 @@ def summarize_bwd(a) -> int:
            f"{describe(w, a.workload, a.dropout)['workload']}", "",
            f"  command: rocprofv3 --kernel-trace --stats -f csv -d <dir> -o run -- python3 bench.py "
            f"--pass bwd --workload {a.workload}{dflag} --steps {a.steps} --warmup {a.warmup} "
-           f"--cpu-budget 0 --cold-reps 0",
+           f"--cpu-budget 0 --cold-reps 0 --no-targets",
            "  (the forward runs once first to produce out and lse; it is listed for completeness)",
            "", f"{'kernel':62s}{'calls':>7s}{'average us':>13s}   share of backward"]
     for r in sorted(ker, key=lambda r: -float(r["TotalDurationNs"])):
