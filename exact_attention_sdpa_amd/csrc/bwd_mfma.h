@@ -984,9 +984,11 @@ struct BwdDkdv {
   }
 };
 
-// waves per SIMD the dQ kernel's registers are fitted to
+// waves per SIMD the dQ kernel's registers are fitted to (d = 64: at 4 the
+// kernel spilled 3-4 VGPRs; 3 holds it in 134-146 without spilling and
+// measured 2-4% faster)
 #ifndef SDPA_BWD_DQ_WAVES_D64
-#define SDPA_BWD_DQ_WAVES_D64 4
+#define SDPA_BWD_DQ_WAVES_D64 3
 #endif
 template <int D>
 constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64 : 2;
@@ -1003,9 +1005,14 @@ void bwd_dq_kernel(BwdParams p) {
   K::run(p, sm);
 }
 
-// waves per SIMD the dK/dV kernel's registers are fitted to
+// waves per SIMD the dK/dV kernel's registers are fitted to (d = 128: one
+// wave per SIMD would hold it without spilling, but halves the resident
+// workgroups and measured 20% slower than two with a few spilled VGPRs)
+#ifndef SDPA_BWD_KV_WAVES_D128
+#define SDPA_BWD_KV_WAVES_D128 2
+#endif
 template <int D>
-constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
+constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : SDPA_BWD_KV_WAVES_D128;
 // with dropout: -D of 16 queries and the Philox state stay live
 template <int D>
 constexpr int kBwdKvDropWavesPerSimd = D == 32 ? 3 : D == 64 ? 2 : 1;

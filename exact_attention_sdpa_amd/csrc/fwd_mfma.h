@@ -1023,6 +1023,10 @@ struct MfmaFwd {
 };
 
 // Waves per SIMD the register allocation is fitted to, per head dimension.
+// An 8-wave workgroup takes 2 waves of every SIMD, so only 4 (two
+// workgroups per CU) or 2 (one) are worth fitting to: d = 128 holds 168-170
+// VGPRs at 2 without spilling, where a bound of 3 spilled 8-12 and ran 24-29%
+// slower.
 #ifndef SDPA_WAVES_D32
 #define SDPA_WAVES_D32 4
 #endif
@@ -1030,7 +1034,7 @@ struct MfmaFwd {
 #define SDPA_WAVES_D64 4
 #endif
 #ifndef SDPA_WAVES_D128
-#define SDPA_WAVES_D128 3
+#define SDPA_WAVES_D128 2
 #endif
 template <int D>
 constexpr int kWavesPerSimd = D == 32 ? SDPA_WAVES_D32 : D == 64 ? SDPA_WAVES_D64 : SDPA_WAVES_D128;
