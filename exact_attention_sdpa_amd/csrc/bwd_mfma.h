@@ -1017,9 +1017,31 @@ constexpr int kBwdKvWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : SDPA_BWD_KV_WAVES
 template <int D>
 constexpr int kBwdKvDropWavesPerSimd = D == 32 ? 3 : D == 64 ? 2 : 1;
 
+// with an elementwise mask (its elements of a step are held in registers):
+// bounds that do not spill, except for boolean masks at d = 32 (2-4 VGPRs
+// spilled at 4 waves measured 3-4% faster than 3 waves without).  Against
+// the dense bounds, measured on B32 H8 N1024 d = 64 and B32 H32 N1024
+// d = 32 (f16): d = 64 +4-8% for boolean and additive masks, +17% on the
+// key-padding workload (B32 H8 N512); additive masks at d = 32 +7-13%.
+#ifndef SDPA_BWD_KVM_WAVES_D32
+#define SDPA_BWD_KVM_WAVES_D32 3
+#endif
+#ifndef SDPA_BWD_KVMB_WAVES_D32
+#define SDPA_BWD_KVMB_WAVES_D32 4
+#endif
+#ifndef SDPA_BWD_KVM_WAVES_D64
+#define SDPA_BWD_KVM_WAVES_D64 2
+#endif
+template <int D, int MK>
+constexpr int kBwdKvMaskWavesPerSimd =
+    MK < kMaskBool ? kBwdKvWavesPerSimd<D>
+    : D == 32      ? (MK == kMaskBool ? SDPA_BWD_KVMB_WAVES_D32 : SDPA_BWD_KVM_WAVES_D32)
+    : D == 64      ? SDPA_BWD_KVM_WAVES_D64
+                   : kBwdKvWavesPerSimd<D>;
+
 template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
           int MK>
-__global__ __launch_bounds__(NW * 64, DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvWavesPerSimd<D>)
+__global__ __launch_bounds__(NW * 64, (DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvMaskWavesPerSimd<D, MK>))
 void bwd_dkdv_kernel(BwdParams p) {
   using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN, MK>;
   __shared__ typename K::Smem sm;
