@@ -984,21 +984,30 @@ struct BwdDkdv {
   }
 };
 
-// waves per SIMD the dQ kernel's registers are fitted to (d = 64: at 4 the
-// kernel spilled 3-4 VGPRs; 3 holds it in 134-146 without spilling and
-// measured 2-4% faster)
+// waves per SIMD the dQ kernel's registers are fitted to.  At d = 64 the
+// kernels with 16-bit gradients (staged through LDS for their stores)
+// spilled 3-4 VGPRs at 4, and the masked and block-sparse ones 4-21; at 3
+// none spills (134-160 VGPRs) and the plain ones measured 2-4% faster.  The
+// plain kernels with f32 gradients fit 4 without spilling, and 3 measured
+// 6% slower for them.
 #ifndef SDPA_BWD_DQ_WAVES_D64
 #define SDPA_BWD_DQ_WAVES_D64 3
 #endif
-template <int D>
-constexpr int kBwdDqWavesPerSimd = D == 32 ? 4 : D == 64 ? SDPA_BWD_DQ_WAVES_D64 : 2;
+#ifndef SDPA_BWD_DQ_WAVES_D64_GF32
+#define SDPA_BWD_DQ_WAVES_D64_GF32 4
+#endif
+template <int D, bool GF32, int MK>
+constexpr int kBwdDqWavesPerSimd =
+    D == 32   ? 4
+    : D == 64 ? (GF32 && MK == kPlain ? SDPA_BWD_DQ_WAVES_D64_GF32 : SDPA_BWD_DQ_WAVES_D64)
+              : 2;
 // with dropout the Philox state needs more registers
 template <int D>
 constexpr int kBwdDqDropWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
           int MK>
-__global__ __launch_bounds__(NW * 64, DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D>)
+__global__ __launch_bounds__(NW * 64, (DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D, GF32, MK>))
 void bwd_dq_kernel(BwdParams p) {
   using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN, MK>;
   __shared__ typename K::Smem sm;
