@@ -1116,9 +1116,17 @@ constexpr int kVariantWavesPerSimd = VAR == kBlockSparse  ? kBspWavesPerSimd<D>
                                      : VAR >= kMaskBool   ? kMaskWavesPerSimd<D, VAR>
                                                           : kWavesPerSimd<D>;
 
+// two query blocks per wave (the wide d = 32 shape: 4-wave workgroups, three
+// per CU): 149 VGPRs at 3 waves per SIMD, 24-33 spilled at 4
+#ifndef SDPA_WIDE_WAVES
+#define SDPA_WIDE_WAVES 3
+#endif
+template <int NB, int D, int VAR>
+constexpr int kKernelWavesPerSimd = NB > 1 ? SDPA_WIDE_WAVES : kVariantWavesPerSimd<D, VAR>;
+
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
           int VAR = kPlain>
-__global__ __launch_bounds__(NW * 64, (kVariantWavesPerSimd<D, VAR>)) void
+__global__ __launch_bounds__(NW * 64, (kKernelWavesPerSimd<NB, D, VAR>)) void
 fwd_mfma_kernel(MfmaParams p) {
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   __shared__ typename K::Smem sm;

@@ -51,6 +51,23 @@ def test_dense_sweep(dtype, d, causal):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [250, 600])
+def test_d32_wide_grid(dtype, causal, n):
+    """d = 32 grids of at least 2048 query tiles of 256 rows run the kernels
+    with two query blocks per wave: distinct random units, full sequences
+    and ragged tails, every unit compared with the oracle."""
+    B = 64 if n <= 256 else 22      # 64 x 32 x 1 or 22 x 32 x 3 >= 2048 tiles
+    w = inputs.make_dense(B, 32, n, n, 32, dtype, "normal", causal, seed=n + causal, cfg=45)
+    assert w.B * w.H * -(-n // 256) >= 2048
+    ref, lref = _dense_ref(w)
+    for out_f32 in ((True,) if dtype == "bf16" else (False, True)):
+        o, lse = G.run(w, out_f32=out_f32)
+        G.assert_parity(o, ref, dtype, f"wide {dtype} N{n} causal{causal} f32out{out_f32}",
+                        lse, lref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("nq,nk", [(1, 300), (130, 70), (70, 130), (256, 1000), (1000, 256)])
 def test_dense_nq_ne_nk(dtype, causal, nq, nk):
     w = inputs.make_dense(2, 3, nq, nk, 64, dtype, "normal", causal, seed=nq * 7 + nk, cfg=50)

@@ -17,7 +17,8 @@ families of ``inputs.make_rescale`` do:
 Each runs on f16 and bf16, d in {32, 64, 128}, causal on and off, through
 the plain, packed, block-sparse, elementwise-mask (boolean, additive in the
 input type, additive f32), dropout (dense and packed) and mask-with-dropout
-entry points,
+entry points, and at d = 32 on a grid large enough to select the kernels
+with two query blocks per wave,
 compared element by element at the tolerances of tests/gpu_util.py.
 
 Outputs are f32 for both input types: these rows concentrate their weight
@@ -41,6 +42,10 @@ pytestmark = pytest.mark.gpu
 VARIANTS = ["plain", "varlen", "block_sparse", "mask_bool", "mask_add", "mask_add_f32",
             "dropout", "dropout_varlen", "mask_bool_dropout", "mask_add_dropout",
             "mask_add_f32_dropout"]
+# "wide" (d = 32, its own test): the plain units replicated over the batch
+# until the grid has at least 2048 query tiles of 256 rows, which selects
+# the d = 32 kernels with two query blocks per wave
+WIDE_TILES = 2048
 
 # per family: (query rows = keys per unit, heads); ``rising`` spans > 2048 keys
 DENSE_N = {"late": (520, 2), "rising": (2090, 1), "low_first": (520, 2)}
@@ -64,9 +69,24 @@ def _check_empty_rows(o, lse, lref, what):
     return ~dead
 
 
+def _widen(w):
+    """The workload's units repeated over the batch until the grid holds at
+    least WIDE_TILES query tiles; returns it and the repeat count."""
+    tiles = w.B * w.H * -(-w.Nq // 256)
+    rep = -(-WIDE_TILES // tiles)
+    for name in ("q", "k", "v"):
+        setattr(w, name, np.ascontiguousarray(np.tile(getattr(w, name), (rep, 1, 1, 1))))
+    w.B *= rep
+    return w, rep
+
+
 def _run_case(family, variant, dtype, d, causal):
-    seed = d + 3 * causal + 11 * VARIANTS.index(variant)
-    w = _workload(family, variant, dtype, d, causal, seed)
+    seed = d + 3 * causal + 11 * (VARIANTS + ["wide"]).index(variant)
+    w = _workload(family, "plain" if variant == "wide" else variant, dtype, d, causal, seed)
+    rep = 1
+    if variant == "wide":
+        q64, k64, v64 = w.q64, w.k64, w.v64    # the unit set the oracle sees
+        w, rep = _widen(w)
     out_f32 = True
     what = f"{family} {variant} {dtype} d{d} causal={causal}"
     q, k, v = (G.to_device(x, dtype) for x in (w.q, w.k, w.v))
@@ -95,6 +115,9 @@ def _run_case(family, variant, dtype, d, causal):
 
     if variant == "plain":
         ref, lref = oracle.sdpa_fwd(w.q64, w.k64, w.v64, w.scale, causal)
+    elif variant == "wide":
+        ref, lref = oracle.sdpa_fwd(q64, k64, v64, w.scale, causal)
+        ref, lref = np.tile(ref, (rep, 1, 1, 1)), np.tile(lref, (rep, 1, 1))
     elif variant == "varlen":
         ref, lref = oracle.sdpa_fwd_varlen(w.q64, w.k64, w.v64, w.cu_seqlens, w.scale, causal)
     elif variant == "dropout":
@@ -134,3 +157,11 @@ def test_late_maximum(dtype, d, causal, variant):
     print(f"rescale case {dtype} d{d} causal={causal} {variant}", flush=True)
     for family in inputs.RESCALE_FAMILIES:
         _run_case(family, variant, dtype, d, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_late_maximum_wide_grid(dtype, causal):
+    print(f"rescale case {dtype} d32 causal={causal} wide", flush=True)
+    for family in inputs.RESCALE_FAMILIES:
+        _run_case(family, "wide", dtype, 32, causal)
