@@ -30,12 +30,13 @@ template <> struct MfmaShape<64> : ShapeOf<SDPA_SHAPE_D64> {};
 template <> struct MfmaShape<128> : ShapeOf<SDPA_SHAPE_D128> {};
 
 // The wide d = 32 shape for large dense grids: two blocks of 32 query rows
-// per wave and 4 waves (the same 256 rows per workgroup), three workgroups
-// per CU.  A wave's K and V fragment reads and the workgroup's staging then
-// serve twice the rows, which measured +1...6% on d = 32 grids of at least
-// 2048 query tiles (B32 H32 N1024, B16 H16 N4096, B128 H16 N512, ...), but
+// per wave and 4 waves (256 rows per workgroup), three workgroups per CU.
+// A wave's K and V fragment reads and the workgroup's staging then serve
+// twice the rows, which measured +1...6% on d = 32 grids of at least 2048
+// query tiles of 256 rows (B32 H32 N1024, B16 H16 N4096, B128 H16 N512,
+// ...) and +5% with dropout (B32 H32 N1024, against its 128-row shape), but
 // 12 resident waves per CU instead of 16 lose 3-15% on smaller grids
-// (B2 H16 N4096, B1 H16 N16384), which keep the 8-wave shape.
+// (B2 H16 N4096, B1 H16 N16384), which keep the other shapes.
 #ifndef SDPA_WIDE_SHAPE_D32
 #define SDPA_WIDE_SHAPE_D32 2, 4, 64
 #endif
@@ -111,11 +112,12 @@ template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, int VAR = kPl
 hipError_t launch_mfma_inst(const FwdArgs& a) {
   using S = std::conditional_t<
       VAR == kBlockSparse, BspShape<D>,
-      std::conditional_t<VAR == kDropout, DropShape<D>,
-                         std::conditional_t<(VAR >= kMaskBool), MaskShape<D>,
-                                            std::conditional_t<VARLEN, VarlenShape<D>,
-                                                               std::conditional_t<WIDE, WideShape<D>,
-                                                                                  MfmaShape<D>>>>>>;
+      std::conditional_t<
+          WIDE, WideShape<D>,
+          std::conditional_t<VAR == kDropout, DropShape<D>,
+                             std::conditional_t<(VAR >= kMaskBool), MaskShape<D>,
+                                                std::conditional_t<VARLEN, VarlenShape<D>,
+                                                                   MfmaShape<D>>>>>>;
   constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
   using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
   MfmaParams p;
@@ -171,6 +173,24 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
     return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, kBlockSparse>(a)
                      : launch_mfma_inst<BF16, D, false, false, false, kBlockSparse>(a);
   }
+  // the wide d = 32 shape for large dense grids (plain and dropout)
+  if constexpr (D == 32) {
+    static_assert(WideShape<32>::NW * WideShape<32>::NB * 32 == 256, "wide tile rows");
+    const int64_t tiles = a.B * a.H * ((a.Nq + 255) / 256);
+    if (!varlen && tiles >= SDPA_WIDE_MIN_TILES) {
+#define SDPA_WCASE(VAR)                                                                     \
+      if (a.causal)                                                                         \
+        return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, VAR, true>(a)       \
+                         : launch_mfma_inst<BF16, D, true, false, false, VAR, true>(a);     \
+      return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, VAR, true>(a)        \
+                       : launch_mfma_inst<BF16, D, false, false, false, VAR, true>(a);
+      if (a.dropout) {
+        SDPA_WCASE(kDropout)
+      }
+      SDPA_WCASE(kPlain)
+#undef SDPA_WCASE
+    }
+  }
   if (a.dropout) {
 #define SDPA_DCASE(C, V, O)                                                  \
     if (a.causal == C && varlen == V && a.out_f32 == O)                      \
@@ -184,19 +204,6 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
     SDPA_DCASE(true, true, false)
     SDPA_DCASE(true, true, true)
 #undef SDPA_DCASE
-  }
-  if constexpr (D == 32) {
-    static_assert(MfmaShape<32>::NW * MfmaShape<32>::NB == WideShape<32>::NW * WideShape<32>::NB,
-                  "the wide shape keeps the rows per workgroup");
-    constexpr int BM = MfmaShape<D>::NW * MfmaShape<D>::NB * 32;
-    const int64_t tiles = a.B * a.H * ((a.Nq + BM - 1) / BM);
-    if (!varlen && tiles >= SDPA_WIDE_MIN_TILES) {
-      if (a.causal)
-        return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, kPlain, true>(a)
-                         : launch_mfma_inst<BF16, D, true, false, false, kPlain, true>(a);
-      return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, kPlain, true>(a)
-                       : launch_mfma_inst<BF16, D, false, false, false, kPlain, true>(a);
-    }
   }
 #define SDPA_CASE(C, V, O)                                                   \
   if (a.causal == C && varlen == V && a.out_f32 == O)                        \

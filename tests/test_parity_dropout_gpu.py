@@ -145,3 +145,26 @@ def test_module_training_workload_full_size():
         ref, lref = odrop.attend_dropout(q64[b, h], k64[b, h], v64[b, h], w.scale, True, 0.1,
                                          2023, 0, b * w.H + h)
         G.assert_parity(o[b, h], ref, "f16", f"unit {b},{h}", lse[b, h], lref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d32_wide_grid_dropout(dtype, causal):
+    """d = 32 grids of at least 2048 query tiles of 256 rows run the dropout
+    kernels with two query blocks per wave: B32 H32 N1024 (the headline
+    shape in training) and a ragged N = 600 grid, on sampled units plus the
+    first and last."""
+    for B, H, n in ((32, 32, 1024), (22, 32, 600)):
+        assert B * H * -(-n // 256) >= 2048
+        w = inputs.make_dense(B, H, n, n, 32, dtype, "normal", causal, seed=n + 5 * causal,
+                              cfg=103)
+        o, lse = _run(w, 0.15, seed=77, offset=4, out_f32=dtype == "bf16")
+        q64, k64, v64 = w.q64, w.k64, w.v64
+        rng = np.random.default_rng(n)
+        units = [0, B * H - 1] + [int(u) for u in rng.choice(B * H, size=6, replace=False)]
+        for u in units:
+            b, h = divmod(u, H)
+            ref, lref = odrop.attend_dropout(q64[b, h], k64[b, h], v64[b, h], w.scale, causal,
+                                             0.15, 77, 4, u)
+            G.assert_parity(o[b, h] * 0.85, ref * 0.85, dtype,
+                            f"wide dropout N{n} unit {b},{h}", lse[b, h], lref)
