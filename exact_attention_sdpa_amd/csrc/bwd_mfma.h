@@ -9,15 +9,19 @@
 //   dV = P^T dO,   dP = dO V^T,   D_i = <dO_i, O_i> = sum_j P_ij dP_ij
 //   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q
 //
-// Three kernels, no atomics (deterministic):
-//   rowdot   D_i = <dO_i, O_i> in fp32, one thread per row.
+// Two kernels, no atomics (deterministic):
 //   dq       one wave per 32 query rows (lanes own queries, as in the
-//            forward): S^T = K Q^T and dP^T = V dO^T on the matrix cores,
-//            P and dS in registers, dQ^T += K^T dS^T with K^T staged in LDS
-//            in the key order of dS's registers.
+//            forward): D_i = <dO_i, O_i> in fp32 from the wave's dO operand
+//            registers and its rows of O (written out for dkdv); S^T = K Q^T
+//            and dP^T = V dO^T on the matrix cores, P and dS in registers,
+//            dQ^T += K^T dS^T with K^T staged in LDS in the key order of
+//            dS's registers.
 //   dkdv     one wave per 32 key rows (lanes own keys): S = Q K^T and
 //            dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS, with Q^T
-//            and dO^T staged in LDS in the query order of P's registers.
+//            and dO^T staged in LDS in the query order of P's registers;
+//            launched after dq, whose D it reads.
+// (Built with SDPA_BWD_FUSED_ROWDOT=0, a third kernel, rowdot, computes D
+// first, one thread per row.)
 // Matrix-core layout of v_mfma_f32_32x32x16 (measured, see the forward):
 // A lane l holds row l%32, k-slots 8(l/32)..+7; B lane l holds column l%32,
 // the same k-slots; C lane l, register r holds row 8(r/4)+4(l/32)+r%4,
@@ -71,7 +75,15 @@ struct BwdParams {
   // blocks, nonzero = the block's pairs are visible
   const uint8_t* bmask;
   int bm_hstride, bm_nqb, bm_nkb;
+  int out_f32;            // O is f32 (else the input type)
 };
+
+// Build option: the dQ kernel computes D_i = <dO_i, O_i> for its own rows
+// (it holds dO already) and writes it for the dK/dV kernel, which runs
+// after it, instead of a separate pass over dO and O.
+#ifndef SDPA_BWD_FUSED_ROWDOT
+#define SDPA_BWD_FUSED_ROWDOT 1
+#endif
 
 // Block-sparse scan: the first tile index >= t whose 128x128 mask block is
 // kept, tiles of 128/tpb rows or keys, mask entries base[b * stride] for
@@ -190,7 +202,8 @@ __device__ __forceinline__ void unpack8(u32x4 w, float (&x)[8]) {
   }
 }
 
-// ---- D_i = <dO_i, O_i>, one thread per row
+// ---- D_i = <dO_i, O_i>, one thread per row (builds without the fused row
+// dot of the dQ kernel)
 template <bool BF16, int D, bool OF32>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p, int64_t rows) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -447,7 +460,46 @@ struct BwdDq {
     float lse2 = qok ? p.lse[li] * 1.4426950408889634f : 0.f;
     // masks, block-sparse: a row that saw no key (lse = -inf) has P = 0
     if (MK != kPlain && lse2 == -INFINITY) lse2 = INFINITY;
-    const float dd = qok ? p.dsum[li] : 0.f;
+    float dd;
+    if (SDPA_BWD_FUSED_ROWDOT) {
+      // D of the lane's row: the lane holds 8 columns of dO per k-step (the
+      // other half of the row is in lane l^32); rows past the end read as
+      // zeros, so their D is 0
+      float part = 0.f;
+      if (p.out_f32) {
+        const int rs4 = rs_bytes * 2;
+        const __amdgpu_buffer_rsrc_t orr = rows_rsrc(
+            reinterpret_cast<const uint16_t*>(reinterpret_cast<const float*>(p.out) + qoff), 0,
+            nq, rs4, 2 * D);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          float g[8];
+          unpack8<BF16>(gf[ds], g);
+          const int c = 2 * (ds * 16 + hl * 8);   // 16-bit units
+          const u32x4 oa = ld16(orr, qi, c, rs4), ob = ld16(orr, qi, c + 8, rs4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            part = __builtin_fmaf(g[i], __uint_as_float(oa[i]), part);
+            part = __builtin_fmaf(g[4 + i], __uint_as_float(ob[i]), part);
+          }
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t orr =
+            rows_rsrc(reinterpret_cast<const uint16_t*>(p.out) + qoff, 0, nq, rs_bytes, D);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          float g[8], o[8];
+          unpack8<BF16>(gf[ds], g);
+          unpack8<BF16>(ld16(orr, qi, ds * 16 + hl * 8, rs_bytes), o);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part = __builtin_fmaf(g[i], o[i], part);
+        }
+      }
+      dd = pair_sum(part);
+      if (hl == 0 && qok) p.dsum[li] = dd;
+    } else {
+      dd = qok ? p.dsum[li] : 0.f;
+    }
     // masks: the lane's row of the unit's mask, read per 32-key block as
     // the forward reads it (load_mask_groups)
     constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;

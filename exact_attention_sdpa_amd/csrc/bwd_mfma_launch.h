@@ -148,14 +148,18 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
   // D_i = <dO_i, O_i> (with dropout O is the dropped output, and D is still
   // sum_j P_ij dP_ij with dP the gradient of the undropped weights)
   // rows of O / dO: [B,H,Nq] dense, [T,H] packed (both flat, row stride d)
-  const int64_t rows = a.cu != nullptr ? a.T * a.H : a.B * a.H * a.Nq;
-  const dim3 grid((unsigned)((rows + 255) / 256));
-  if (a.out_f32)
-    hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, true>), grid, dim3(256), 0, a.stream, p, rows);
-  else
-    hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // (computed by the dQ kernel, which runs first, unless built without)
+  p.out_f32 = a.out_f32 ? 1 : 0;
+  if (!SDPA_BWD_FUSED_ROWDOT) {
+    const int64_t rows = a.cu != nullptr ? a.T * a.H : a.B * a.H * a.Nq;
+    const dim3 grid((unsigned)((rows + 255) / 256));
+    if (a.out_f32)
+      hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, true>), grid, dim3(256), 0, a.stream, p, rows);
+    else
+      hipLaunchKernelGGL((bwd_rowdot_kernel<BF16, D, false>), grid, dim3(256), 0, a.stream, p, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (with_mask)
     return a.bmask != nullptr ? launch_bwd_bsp_tiles<BF16, D>(a, p)
            : a.dropout        ? launch_bwd_masked_drop_tiles<BF16, D>(a, p)

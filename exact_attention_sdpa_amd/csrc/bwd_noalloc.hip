@@ -58,8 +58,8 @@ sdpa_status sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const 
       sdpa::validate_bwd(q, k, v, out, dout, lse, dq, dk, dv, work, B, H, Nq, Nk, d, scale,
                          is_causal, dtype, out_dtype, grad_dtype, stream, &a);
   if (st != SDPA_OK) return st;
-  // the row-dot kernel writes every D_i before the gradient kernels read
-  // it, so nothing needs clearing
+  // the dQ kernel writes every D_i before the dK/dV kernel, launched after
+  // it, reads it, so nothing needs clearing
   const hipError_t e =
       dtype == SDPA_BF16 ? sdpa::launch_bwd_mfma_bf16(a) : sdpa::launch_bwd_mfma_f16(a);
   return e == hipSuccess ? SDPA_OK : SDPA_ERR_LAUNCH;

@@ -306,8 +306,9 @@ SDPA_API sdpa_status sdpa_fwd_masked_dropout(
  *
  * Returns SDPA_OK, or SDPA_ERR_INVALID / SDPA_ERR_UNSUPPORTED /
  * SDPA_ERR_DEVICE / SDPA_ERR_LAUNCH with the meanings of sdpa_fwd (f32
- * inputs and packed batches are unsupported).  Queues three kernels on
- * `stream`; allocates nothing.  Nothing is launched unless SDPA_OK is
+ * inputs and packed batches are unsupported).  Queues two kernels on
+ * `stream` (dQ, which also writes the row dots into `workspace`, then dK
+ * and dV); allocates nothing.  Nothing is launched unless SDPA_OK is
  * returned.
  */
 SDPA_API sdpa_status sdpa_bwd(const void* q, const void* k, const void* v, const void* out,
