@@ -322,6 +322,24 @@ __device__ __forceinline__ void store_pair_t(uint32_t* dst, int tw, u32x4 a, u32
   }
 }
 
+// Debug (LDS poisoning, SDPA_LDS_POISON): all-ones words are NaN in f16,
+// bf16 and f32.  The whole LDS is filled when a kernel starts, and after
+// the barrier that ends the reads of a staging buffer each thread refills
+// the slots it stores that buffer's next tile into (same thread, so the
+// refill and the later store are ordered), so that a read of a buffer
+// before its tile has been written turns the gradients into NaN.
+template <class Smem>
+__device__ __forceinline__ void poison_whole_lds(Smem& sm, int tid, int nt) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(&sm);
+  for (int i = tid; i < (int)(sizeof(Smem) / 4); i += nt) w[i] = 0xffffffffu;
+}
+template <class Regs>
+__device__ __forceinline__ Regs poison_regs() {
+  Regs r;
+  __builtin_memset(&r, 0xff, sizeof(r));
+  return r;
+}
+
 // Two fp32 values packed as operands of the dV / dK / dQ products (the
 // input type, round to nearest even), and those products.
 template <bool BF16>
@@ -577,6 +595,10 @@ struct BwdDq {
     auto next_tile = [&](int t) {
       return BSP ? block_scan_next(bsc, t, kSparseBlock / BN, ntiles, lane) : t;
     };
+    if (SDPA_LDS_POISON) {
+      poison_whole_lds(sm, tid, NT);
+      __syncthreads();
+    }
     int j = next_tile(0);
     if (j < ntiles) {
       Regs r0;
@@ -674,8 +696,14 @@ struct BwdDq {
       }
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
+      // every read of buffer buf ended at this barrier; the next step
+      // stores the tile after next there
+      if (SDPA_LDS_POISON) store(buf, poison_regs<Regs>());
       j = jn;
     }
+    // (debug poisoning: the last refills end before any wave stages its
+    // gradient rows in LDS)
+    if (SDPA_LDS_POISON) __syncthreads();
     static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dQ rows fit in LDS");
     // (the masked kernels keep direct stores: through LDS they measured
     // 5% slower on a key-padding mask)
@@ -907,6 +935,10 @@ struct BwdDkdv {
     auto next_tile = [&](int t) {
       return BSP ? block_scan_next(bsc, t, kSparseBlock / BQ, nqt, lane) : t;
     };
+    if (SDPA_LDS_POISON) {
+      poison_whole_lds(sm, tid, NT);
+      __syncthreads();
+    }
     int i = next_tile(i0);
     if (i < nqt) {
       Regs r0;
@@ -1022,8 +1054,11 @@ struct BwdDkdv {
       }
       if (nxt) store(buf ^ 1, rn);
       __syncthreads();
+      // every read of buffer buf ended at this barrier
+      if (SDPA_LDS_POISON) store(buf, poison_regs<Regs>());
       i = in_;
     }
+    if (SDPA_LDS_POISON) __syncthreads();
     static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dK, dV rows fit in LDS");
     if (GF32 || MK != kPlain) {
       store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);

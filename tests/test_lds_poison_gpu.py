@@ -78,3 +78,61 @@ def test_poisoned_variants(debug_lib, causal):
                                        "add", w.scale, causal)
     G.assert_parity(o, ref, "f16", "poisoned additive mask", lse, lref)
     assert np.all(np.isfinite(o))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_poisoned_wide_d32_grid(debug_lib, dtype, causal):
+    """A d = 32 grid of at least 2048 query tiles (the kernels with two
+    query blocks per wave, whose 16-bit epilogue stages both blocks' rows in
+    LDS), plain and with dropout, on sampled units."""
+    w = inputs.make_dense(64, 32, 333, 333, 32, dtype, "normal", causal, seed=3, cfg=143)
+    assert w.B * w.H * -(-w.Nq // 256) >= 2048
+    q64, k64, v64 = w.q64, w.k64, w.v64
+    units = [0, w.B * w.H - 1] + [int(u) for u in
+                                  np.random.default_rng(9).choice(w.B * w.H, 4, replace=False)]
+    o, lse = _fwd(w, dtype == "bf16")
+    od, lsed = _fwd(w, dtype == "bf16", dropout_p=0.25, dropout_seed=5, dropout_offset=1)
+    for u in units:
+        b, h = divmod(u, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref, lref = oracle.sdpa_fwd(q64[sl], k64[sl], v64[sl], w.scale, causal)
+        G.assert_parity(o[sl], ref, dtype, f"poisoned wide {dtype} unit {b},{h}", lse[sl], lref)
+        ref, lref = odrop.attend_dropout(q64[b, h], k64[b, h], v64[b, h], w.scale, causal, 0.25,
+                                         5, 1, u)
+        G.assert_parity(od[b, h] * 0.75, ref * 0.75, dtype,
+                        f"poisoned wide dropout {dtype} unit {b},{h}", lsed[b, h], lref)
+
+
+# --- the backward kernels under poisoning: their K/V (dQ kernel) and
+# Q/dO/row-statistic/mask (dK/dV kernel) staging buffers are poisoned the
+# same way; the bounds are those of the backward parity tests
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_poisoned_backward(debug_lib, dtype, d, causal):
+    from tests import test_parity_bwd_gpu as TB
+    # several query and key tiles with ragged tails, so every staging buffer
+    # of both kernels is poisoned and refilled more than once; f32 and
+    # 16-bit gradients (the latter leave through LDS)
+    w = inputs.make_dense(2, 2, 200, 200, d, dtype, "normal", causal, seed=5, cfg=144)
+    do = inputs.make_grad_out(w, seed=5, cfg=144)
+    for grad_f32 in (True, False):
+        TB._check(TB._run(w, do, grad_f32=grad_f32), TB._ref_and_bound(w, do, grad_f32=grad_f32),
+                  f"poisoned bwd {dtype} d{d} causal={causal} f32grad={grad_f32}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_poisoned_backward_variants(debug_lib, causal):
+    from tests import test_parity_bwd_dropout_gpu as TD
+    from tests import test_parity_bwd_masked_gpu as TM
+    w = inputs.make_dense(2, 2, 150, 161, 64, "f16", "normal", causal, seed=6, cfg=145)
+    do = inputs.make_grad_out(w, seed=6, cfg=145)
+    for kind, mdt in (("bool", "f16"), ("add", "f16")):
+        m = inputs.make_attn_mask((2, 2, 150, 161), kind, keep=0.8, seed=6, cfg=146, dtype=mdt)
+        TM._check(w, TM._run(w, do, TM._mask_t(m, kind, mdt)), do, m, kind, mdt)
+    wd = inputs.make_dense(2, 2, 160, 160, 64, "f16", "normal", causal, seed=7, cfg=147)
+    dod = inputs.make_grad_out(wd, seed=7, cfg=147)
+    TD._check(TD._run(wd, dod, 0.2, seed=21, offset=2), TD._ref_and_bound(wd, dod, 0.2, 21, 2),
+              f"poisoned bwd dropout causal={causal}")
