@@ -20,7 +20,18 @@ namespace sdpa {
 #ifndef SDPA_BWD_KV_ROWS_D64
 #define SDPA_BWD_KV_ROWS_D64 32
 #endif
-constexpr int kBwdDqWaves = 4, kBwdKvWaves = 4;
+// Waves per workgroup (32 rows or keys each).  8 for the unmasked d = 32
+// kernels without dropout: a step's staged tile is shared by twice the
+// waves at the same occupancy, +5% on B32 H32 N1024.  Block-sparse kernels
+// need exactly one 128-row mask block per workgroup; masked ones stage a
+// mask tile that grows with the workgroup's keys; the dropout dK/dV kernel
+// runs at 3 waves per SIMD, where an 8-wave workgroup leaves room for only
+// one per CU (-12% measured).
+#ifndef SDPA_BWD_WAVES_D32
+#define SDPA_BWD_WAVES_D32 8
+#endif
+template <int D, int MK, bool DROP>
+constexpr int kBwdWaves = MK == kPlain && !DROP && D == 32 ? SDPA_BWD_WAVES_D32 : 4;
 // Keys (dQ) and query rows (dK/dV) per step.  64 at d = 32 for the unmasked
 // kernels: half the steps and barriers, +5.5% on B32 H32 N1024; the masked
 // ones stage a mask tile per step in LDS, which at 64 rows would halve
@@ -35,18 +46,18 @@ constexpr int kBwdKvRows =
 
 template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN, int MK = kPlain>
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
-  using Q = BwdDq<BF16, D, kBwdDqWaves, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
-  using KV = BwdDkdv<BF16, D, kBwdKvWaves, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
+  using Q = BwdDq<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
+  using KV = BwdDkdv<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdDqWaves, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
-                     dim3(p.total), dim3(kBwdDqWaves * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
+                     dim3(p.total), dim3(kBwdWaves<D, MK, DROP> * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdKvWaves, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
-                     dim3(p.total), dim3(kBwdKvWaves * 64), 0, a.stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
+                     dim3(p.total), dim3(kBwdWaves<D, MK, DROP> * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -150,7 +161,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, bool with_mask = false) {
   // rows of O / dO: [B,H,Nq] dense, [T,H] packed (both flat, row stride d)
   // (computed by the dQ kernel, which runs first, unless built without)
   p.out_f32 = a.out_f32 ? 1 : 0;
-  if (!SDPA_BWD_FUSED_ROWDOT) {
+  if constexpr (!SDPA_BWD_FUSED_ROWDOT) {
     const int64_t rows = a.cu != nullptr ? a.T * a.H : a.B * a.H * a.Nq;
     const dim3 grid((unsigned)((rows + 255) / 256));
     if (a.out_f32)
