@@ -121,3 +121,43 @@ def test_out_rows_at_eight_byte_alignment(dtype, d):
     assert out.data_ptr() == base.data_ptr()
     assert torch.equal(yv, oc) and torch.equal(lse, lc)
     assert torch.isnan(base[..., d:]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_d32_grid_in_place_and_cross(causal):
+    """d = 32 grids of at least 2048 query tiles (the kernels with two query
+    blocks per wave) read the packed-QKV views in place and write the
+    module's layout, with the same bits as the contiguous path; and a
+    cross-attention grid (Nq != Nk) of that size matches the oracle on
+    sampled units."""
+    B, N, H, d = 64, 250, 32, 32
+    x, q, k, v = _packed_qkv(B, N, H, d, "f16", seed=11 + causal)
+    assert B * H * -(-N // 256) >= 2048
+    y = torch.full((B, N, H * d), float("nan"), dtype=torch.float16, device="cuda")
+    yv = y.view(B, N, H, d).transpose(1, 2)
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, is_causal=causal, out=yv,
+                                                 return_lse=True)
+    oc, lc = sdpa.scaled_dot_product_attention(q.contiguous(), k.contiguous(), v.contiguous(),
+                                               is_causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, oc) and torch.equal(lse, lc)
+    units = [(0, 0), (B - 1, H - 1), (17, 5), (40, 30)]
+    for b, h in units:
+        ref, lref = _ref(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                         1.0 / np.sqrt(d), causal)
+        G.assert_parity(out[b:b + 1, h:h + 1].double().cpu().numpy(), ref, "f16",
+                        f"wide in place unit {b},{h}", lse[b:b + 1, h:h + 1].double().cpu().numpy(),
+                        lref)
+    # cross attention: 250 queries, 600 keys
+    g = torch.Generator().manual_seed(21 + causal)
+    qx = torch.randn(B, H, 250, d, generator=g).half().cuda()
+    kx = torch.randn(B, H, 600, d, generator=g).half().cuda()
+    vx = torch.randn(B, H, 600, d, generator=g).half().cuda()
+    ox, lx = sdpa.scaled_dot_product_attention(qx, kx, vx, is_causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    for b, h in units:
+        ref, lref = _ref(qx[b:b + 1, h:h + 1], kx[b:b + 1, h:h + 1], vx[b:b + 1, h:h + 1],
+                         1.0 / np.sqrt(d), causal)
+        G.assert_parity(ox[b:b + 1, h:h + 1].double().cpu().numpy(), ref, "f16",
+                        f"wide cross unit {b},{h}", lx[b:b + 1, h:h + 1].double().cpu().numpy(),
+                        lref)
