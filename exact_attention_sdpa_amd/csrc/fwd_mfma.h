@@ -204,7 +204,7 @@ __host__ __device__ constexpr int vt_key_pos(int k) {
 }
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
-          int VAR = kPlain>
+          int VAR = kPlain, int KS = 1>
 struct MfmaFwd {
   static constexpr bool BSP = VAR == kBlockSparse;
   static constexpr int MK = mask_kind_of(VAR);
@@ -212,7 +212,11 @@ struct MfmaFwd {
   static constexpr bool MASK = VAR >= kMaskBool;
   // mask element bytes = 32-bit words a lane loads per group of 4 keys
   static constexpr int MW = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
-  static constexpr int BM = NW * NB * 32;  // query rows per workgroup
+  // KS key groups: the workgroup's waves form KS groups of NWG waves over
+  // the same query rows; group g takes key tiles g, g + KS, ... and the
+  // groups' partial states are merged at the end
+  static constexpr int NWG = NW / KS;
+  static constexpr int BM = NWG * NB * 32;  // query rows per workgroup
   // epilogue: a wave's 16-bit output rows staged in LDS, rows padded by 16
   // bytes (the LDS area is sized for every wave's rows)
   static constexpr int OROW = D + 8;
@@ -220,13 +224,15 @@ struct MfmaFwd {
   static constexpr int DS = D / 16;        // k-steps of S = Q K^T
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
   static constexpr int NT = NW * 64;
+  static constexpr int NTG = NWG * 64;     // threads of a key group (staging)
   static constexpr int NC = D / 8;         // 16-byte chunks per row
   static constexpr int KROW = D + 8;       // LDS K row, elements
   static constexpr int VRW = BN / 2 + 4;   // LDS V^T row, 32-bit words
   static constexpr int KCHUNKS = BN * NC;        // 16-byte K chunks per tile
   static constexpr int VPAIRS = (BN / 2) * NC;   // (2 rows x 16 bytes) V chunks
-  static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-  static constexpr int VPT = (VPAIRS + NT - 1) / NT;
+  static constexpr int KPT = (KCHUNKS + NTG - 1) / NTG;
+  static constexpr int VPT = (VPAIRS + NTG - 1) / NTG;
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && VAR == kPlain), "key groups");
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(BN % 32 == 0 && BN <= 128, "key block");
   // block-sparse: a workgroup's rows are exactly one mask row, and a key
@@ -236,11 +242,15 @@ struct MfmaFwd {
   static_assert(!MASK || !VARLEN, "elementwise masks take dense layouts");
 
   static constexpr bool EPI_LDS = SDPA_EPI_LDS && !OUTF32;
-  static constexpr int KV_BYTES = 2 * BN * KROW * 2 + 2 * D * VRW * 4;
-  static constexpr int EPI_BYTES = EPI_LDS ? NW * NB * 32 * OROW * 2 : 0;
+  static constexpr int KV_BYTES = 2 * KS * (BN * KROW * 2 + D * VRW * 4);
+  // key groups: the other group's state (per lane: O, m, l) for the merge,
+  // after the epilogue's rows
+  static constexpr int MITEMS = 16 * DB + 2;
+  static constexpr int MERGE_OFF = EPI_LDS ? NWG * NB * 32 * OROW * 2 : 0;
+  static constexpr int EPI_BYTES = MERGE_OFF + (KS > 1 ? NWG * NB * MITEMS * 64 * 4 : 0);
   struct __attribute__((aligned(16))) Smem {
-    uint16_t k[2][BN * KROW];
-    uint32_t vt[2][D * VRW];
+    uint16_t k[2 * KS][BN * KROW];
+    uint32_t vt[2 * KS][D * VRW];
     // room for the epilogue's rows where the K/V buffers are smaller
     uint8_t pad[EPI_BYTES > KV_BYTES ? EPI_BYTES - KV_BYTES : 16];
   };
@@ -277,14 +287,14 @@ struct MfmaFwd {
   static __device__ __forceinline__ void setup_staging(Staging& st, int64_t rs, int tid) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
+      const int c = tid + i * NTG;
       const int row = c / NC, col = (c % NC) * 8;
       st.kg[i] = (int)(((int64_t)row * rs + col) * 2);
       st.kl[i] = row * KROW + col;
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * NT;
+      const int c = tid + i * NTG;
       // consecutive lanes take consecutive key pairs of one column chunk
       const int pr = c % (BN / 2);
       const int col = (c / (BN / 2)) * 8;
@@ -316,7 +326,7 @@ struct MfmaFwd {
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(hd.k, t, hd);
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS)
+      if (KCHUNKS % NTG == 0 || tid + i * NTG < KCHUNKS)
         r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, st.kg[i], 0, 0));
   }
 
@@ -325,7 +335,7 @@ struct MfmaFwd {
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(hd.v, t, hd);
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+      if (VPAIRS % NTG == 0 || tid + i * NTG < VPAIRS) {
         r.v0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, st.vg[i], 0, 0));
         r.v1[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, st.vg[i] + hd.rs_bytes, 0, 0));
@@ -336,7 +346,7 @@ struct MfmaFwd {
                                                  const Staging& st, int tid) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS)
+      if (KCHUNKS % NTG == 0 || tid + i * NTG < KCHUNKS)
         *reinterpret_cast<u32x4*>(&sm.k[buf][st.kl[i]]) = r.k[i];
   }
 
@@ -345,7 +355,7 @@ struct MfmaFwd {
                                                  const Staging& st, int tid) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+      if (VPAIRS % NTG == 0 || tid + i * NTG < VPAIRS) {
         uint32_t* dst = &sm.vt[buf][st.vl[i]];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -376,14 +386,14 @@ struct MfmaFwd {
     const uint32_t kn = BF16 ? 0x7fc07fc0u : 0x7e007e00u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS) {
+      if (KCHUNKS % NTG == 0 || tid + i * NTG < KCHUNKS) {
         uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.k[buf][st.kl[i]]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) dst[w] = kn;
       }
 #pragma unroll
     for (int i = 0; i < VPT; ++i)
-      if (VPAIRS % NT == 0 || tid + i * NT < VPAIRS) {
+      if (VPAIRS % NTG == 0 || tid + i * NTG < VPAIRS) {
         uint32_t* dst = &sm.vt[buf][st.vl[i]];
 #pragma unroll
         for (int w = 0; w < 8; ++w) dst[w * VRW] = 0x7e007e00u;
@@ -427,6 +437,7 @@ struct MfmaFwd {
     Lanes ln;
     Head hd;
     int ntiles, nk, wq0, l32, hl, tid;
+    int gtid, bb;   // thread index within its key group; the group's first LDS buffer
     bool wave_live;
     float c;
     const uint8_t* mrow;       // block-sparse: the workgroup's mask row
@@ -441,7 +452,7 @@ struct MfmaFwd {
   };
 
   static __device__ __forceinline__ bool skip_tile(const Ctx& x, int t) {
-    return !x.wave_live || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
+    return !x.wave_live || (KS > 1 && t >= x.ntiles) || (CAUSAL && t * BN > x.wq0 + NB * 32 - 1);
   }
 
   // Elementwise mask: the lane's elements of tile t, by 32-key block.  The
@@ -759,8 +770,8 @@ struct MfmaFwd {
     // second register set, measured slower)
     if (MASK && live) load_mask(mr, x, j);
     if (nxt) {
-      load_k(kr, x.st, x.hd, jn, x.tid);
-      load_v(vr, x.st, x.hd, jn, x.tid);
+      load_k(kr, x.st, x.hd, jn, x.gtid);
+      load_v(vr, x.st, x.hd, jn, x.gtid);
     }
     // boolean masks: a tile whose mask drops every pair of the wave's rows
     // adds nothing (its P would be exactly 0), so the wave skips it, e.g.
@@ -779,22 +790,25 @@ struct MfmaFwd {
     if (run_tile) {
       const int kb = j * BN;
       const bool masked = (kb + BN > x.nk) || (CAUSAL && kb + BN - 1 > x.wq0);
-      tile(sm, B, kb, !BSP && j == 0, masked, x, qf, S, mr);
+      tile(sm, x.bb + B, kb, !BSP && (KS == 1 ? j == 0 : j < KS), masked, x, qf, S, mr);
     }
     if (nxt) {
-      store_k(sm, B ^ 1, kr, x.st, x.tid);
-      store_v(sm, B ^ 1, vr, x.st, x.tid);
+      store_k(sm, x.bb + (B ^ 1), kr, x.st, x.gtid);
+      store_v(sm, x.bb + (B ^ 1), vr, x.st, x.gtid);
     }
     __syncthreads();
     // every read of buffer B ended at this barrier; the step after next
     // stores its next tile there
-    if (SDPA_LDS_POISON) poison_slots(sm, B, x.st, x.tid);
+    if (SDPA_LDS_POISON) poison_slots(sm, x.bb + B, x.st, x.gtid);
   }
 
   static __device__ void run(const MfmaParams& p, Smem& sm) {
     Ctx x;
     x.tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(x.tid / 64);   // wave-uniform
+    const int grp = KS > 1 ? wave / NWG : 0;   // key group
+    x.gtid = KS > 1 ? x.tid % NTG : x.tid;
+    x.bb = KS > 1 ? 2 * grp : 0;
     const int lane = x.tid % 64;
     x.hl = lane / 32;
     x.l32 = lane % 32;
@@ -865,7 +879,7 @@ struct MfmaFwd {
 
     const int kend = CAUSAL ? min(nk, q0 + BM) : nk;
     x.ntiles = (kend + BN - 1) / BN;
-    x.wq0 = q0 + wave * NB * 32;   // first query row of this wave
+    x.wq0 = q0 + (KS > 1 ? wave % NWG : wave) * NB * 32;   // first query row of this wave
     x.wave_live = x.wq0 < nq;
     if (DROP) {
       x.unit = (uint32_t)bh;
@@ -914,7 +928,7 @@ struct MfmaFwd {
         for (int r = 0; r < 16; ++r) S.o[qb][db][r] = 0.f;
     }
 
-    setup_staging(x.st, rs, x.tid);
+    setup_staging(x.st, rs, x.gtid);
     x.ln = setup_lanes(x.l32, x.hl);
 
     if (SDPA_LDS_POISON) {
@@ -923,21 +937,29 @@ struct MfmaFwd {
     }
 
     // ---- prologue: the first tile staged
-    int j = next_tile(x, 0);
+    int j = KS > 1 ? grp : next_tile(x, 0);
     if (j < x.ntiles) {
       KRegs k0;
       VRegs v0;
-      load_k(k0, x.st, x.hd, j, x.tid);
-      load_v(v0, x.st, x.hd, j, x.tid);
-      store_k(sm, 0, k0, x.st, x.tid);
-      store_v(sm, 0, v0, x.st, x.tid);
+      load_k(k0, x.st, x.hd, j, x.gtid);
+      load_v(v0, x.st, x.hd, j, x.gtid);
+      store_k(sm, x.bb, k0, x.st, x.gtid);
+      store_v(sm, x.bb, v0, x.st, x.gtid);
     }
     __syncthreads();
 
-    if (!BSP) {
+    if (!BSP && KS == 1) {
       for (; j < x.ntiles; j += 2) {
         step<0>(sm, x, S, qf, j, j + 1);
         if (j + 1 < x.ntiles) step<1>(sm, x, S, qf, j + 1, j + 2);
+      }
+    } else if (!BSP) {
+      // every group makes the same number of steps (one barrier each); a
+      // group past its last tile only waits at them
+      const int nsteps = (x.ntiles + KS - 1) / KS;
+      for (int s = 0; s < nsteps; s += 2, j += 2 * KS) {
+        step<0>(sm, x, S, qf, j, j + KS);
+        if (s + 1 < nsteps) step<1>(sm, x, S, qf, j + KS, j + 2 * KS);
       }
     } else {
       while (j < x.ntiles) {
@@ -955,6 +977,46 @@ struct MfmaFwd {
     // (debug poisoning: the last step's poison writes end before any wave
     // stages its output rows in LDS)
     if (SDPA_LDS_POISON && EPI_LDS) __syncthreads();
+    if constexpr (KS > 1) {
+      // key groups: group 1 hands its state to group 0 through LDS (every
+      // read of the K/V buffers ended at the last step's barrier); group 0
+      // brings both states to the larger reference m and adds them
+      float* mg = reinterpret_cast<float*>(reinterpret_cast<char*>(&sm) + MERGE_OFF) +
+                  (wave % NWG) * NB * MITEMS * 64 + x.tid % 64;
+      if (grp == 1 && x.wave_live) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          float* e = mg + qb * MITEMS * 64;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) e[(db * 16 + r) * 64] = S.o[qb][db][r];
+          e[(16 * DB) * 64] = S.m[qb];
+          e[(16 * DB + 1) * 64] = S.l[qb];
+        }
+      }
+      __syncthreads();
+      if (grp != 0) return;
+      // group 1 starts at tile 1; a wave that skips it skips every tile of
+      // that group (causal: its rows end before key BN)
+      if (!skip_tile(x, 1)) {
+#pragma unroll
+        for (int qb = 0; qb < NB; ++qb) {
+          const float* e = mg + qb * MITEMS * 64;
+          const float m1 = e[(16 * DB) * 64], l1 = e[(16 * DB + 1) * 64];
+          const float m = fmaxf(S.m[qb], m1);
+          const float a0 = __builtin_amdgcn_exp2f(S.m[qb] - m);
+          const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+          S.m[qb] = m;
+          S.l[qb] = S.l[qb] * a0 + l1 * a1;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              S.o[qb][db][r] = S.o[qb][db][r] * a0 + e[(db * 16 + r) * 64] * a1;
+        }
+      }
+    }
     if (!x.wave_live) return;
 #pragma unroll
     for (int qb = 0; qb < NB; ++qb) {
@@ -1125,10 +1187,10 @@ template <int NB, int D, int VAR>
 constexpr int kKernelWavesPerSimd = NB > 1 ? SDPA_WIDE_WAVES : kVariantWavesPerSimd<D, VAR>;
 
 template <bool BF16, int D, int NB, int NW, int BN, bool CAUSAL, bool VARLEN, bool OUTF32,
-          int VAR = kPlain>
+          int VAR = kPlain, int KS = 1>
 __global__ __launch_bounds__(NW * 64, (kKernelWavesPerSimd<NB, D, VAR>)) void
 fwd_mfma_kernel(MfmaParams p) {
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR, KS>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -61,6 +61,36 @@ template <> struct VarlenShape<32> : ShapeOf<SDPA_VARLEN_SHAPE_D32> {};
 template <> struct VarlenShape<64> : ShapeOf<SDPA_VARLEN_SHAPE_D64> {};
 template <> struct VarlenShape<128> : ShapeOf<SDPA_VARLEN_SHAPE_D128> {};
 
+// Key groups for grids of few query tiles: 8 waves over 128 query rows, in
+// two groups of 4 that take alternate key tiles and merge their states at
+// the end.  Against the 256-row shape a workgroup's chain of key steps is
+// half as long and the grid has twice the waves, which pays where that grid
+// would leave most CUs with one workgroup or none (f16, one box: B1 H16
+// N2048 +66/69% at d = 32, +15/21% at d = 64, +33/36% at d = 128,
+// non-causal/causal; 256 tiles of 256 rows: d = 32 +16%, causal d = 64 and
+// 128 +13...19%, but non-causal d = 64 and 128 -9...25%, as do larger
+// grids).  Thresholds in query tiles of 256 rows (plain launches, dense or
+// packed):
+#ifndef SDPA_SPLIT_TILES_D32
+#define SDPA_SPLIT_TILES_D32 256
+#endif
+#ifndef SDPA_SPLIT_TILES_D64
+#define SDPA_SPLIT_TILES_D64 128
+#endif
+#ifndef SDPA_SPLIT_TILES_D128
+#define SDPA_SPLIT_TILES_D128 128
+#endif
+#ifndef SDPA_SPLIT_TILES_CAUSAL
+#define SDPA_SPLIT_TILES_CAUSAL 256
+#endif
+template <int D> struct SplitShape : ShapeOf<1, 8, MfmaShape<D>::BN> {};
+template <int D>
+constexpr int64_t kSplitTiles(bool causal) {
+  return D == 32 ? SDPA_SPLIT_TILES_D32
+                 : causal ? SDPA_SPLIT_TILES_CAUSAL
+                          : (D == 64 ? SDPA_SPLIT_TILES_D64 : SDPA_SPLIT_TILES_D128);
+}
+
 // Block-sparse shapes: 128 query rows per workgroup, one mask row, so every
 // wave of a workgroup needs the same key tiles.
 #ifndef SDPA_BSP_SHAPE_D32
@@ -108,18 +138,20 @@ template <> struct MaskShape<64> : ShapeOf<SDPA_MASK_SHAPE_D64> {};
 template <> struct MaskShape<128> : ShapeOf<SDPA_MASK_SHAPE_D128> {};
 
 template <bool BF16, int D, bool CAUSAL, bool VARLEN, bool OUTF32, int VAR = kPlain,
-          bool WIDE = false>
+          bool WIDE = false, int KS = 1>
 hipError_t launch_mfma_inst(const FwdArgs& a) {
   using S = std::conditional_t<
       VAR == kBlockSparse, BspShape<D>,
+      std::conditional_t<
+          (KS > 1), SplitShape<D>,
       std::conditional_t<
           WIDE, WideShape<D>,
           std::conditional_t<VAR == kDropout, DropShape<D>,
                              std::conditional_t<(VAR >= kMaskBool), MaskShape<D>,
                                                 std::conditional_t<VARLEN, VarlenShape<D>,
-                                                                   MfmaShape<D>>>>>>;
+                                                                   MfmaShape<D>>>>>>>;
   constexpr int NB = S::NB, NW = S::NW, BN = S::BN;
-  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>;
+  using K = MfmaFwd<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR, KS>;
   MfmaParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
@@ -157,7 +189,7 @@ hipError_t launch_mfma_inst(const FwdArgs& a) {
   p.am_bs = a.am_str[0];
   p.am_hs = a.am_str[1];
   p.am_rs = (int)a.am_str[2];
-  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR>), dim3(p.total),
+  hipLaunchKernelGGL((fwd_mfma_kernel<BF16, D, NB, NW, BN, CAUSAL, VARLEN, OUTF32, VAR, KS>), dim3(p.total),
                      dim3(NW * 64), 0, a.stream, p);
   return hipGetLastError();
 }
@@ -204,6 +236,22 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
     SDPA_DCASE(true, true, false)
     SDPA_DCASE(true, true, true)
 #undef SDPA_DCASE
+  }
+  // key groups for grids of few query tiles (B counts sequences and Nq is
+  // the longest one for packed batches)
+  if (a.B * a.H * ((a.Nq + 255) / 256) <= kSplitTiles<D>(a.causal)) {
+#define SDPA_SCASE(C, V, O)                                                  \
+    if (a.causal == C && varlen == V && a.out_f32 == O)                      \
+      return launch_mfma_inst<BF16, D, C, V, O, kPlain, false, 2>(a);
+    SDPA_SCASE(false, false, false)
+    SDPA_SCASE(false, false, true)
+    SDPA_SCASE(false, true, false)
+    SDPA_SCASE(false, true, true)
+    SDPA_SCASE(true, false, false)
+    SDPA_SCASE(true, false, true)
+    SDPA_SCASE(true, true, false)
+    SDPA_SCASE(true, true, true)
+#undef SDPA_SCASE
   }
 #define SDPA_CASE(C, V, O)                                                   \
   if (a.causal == C && varlen == V && a.out_f32 == O)                        \

@@ -81,8 +81,10 @@ def test_all_zero_mask_gives_zeros_and_neg_inf():
 def test_all_ones_mask_equals_dense_path(d, causal):
     """With every block visible the block-sparse kernel takes the same
     arithmetic steps as the dense one, key tile by key tile from key 0:
-    bit-identical results."""
-    w = inputs.make_dense(2, 2, 333, 333, d, "f16", "normal", causal, seed=d, cfg=84)
+    bit-identical results.  2 x 65 units of two query tiles: above the tile
+    count under which plain launches split each workgroup's keys over two
+    wave groups (another order of additions)."""
+    w = inputs.make_dense(2, 65, 333, 333, d, "f16", "normal", causal, seed=d, cfg=84)
     o, lse = _run(w, np.ones((1, 3, 3), np.uint8))
     od, ld = G.run(w)
     assert np.array_equal(o, od) and np.array_equal(lse, ld)

@@ -107,8 +107,11 @@ def test_bwd_block_sparse_empty_rows_and_columns():
 @pytest.mark.parametrize("causal", [False, True])
 def test_all_ones_block_mask_matches_dense_backward(causal):
     # every block kept: the block-sparse forward and backward visit the
-    # same tiles in the same order as the dense ones, so the same bits
-    B, H, N, d = 1, 2, 384, 64
+    # same tiles in the same order as the dense ones, so the same bits.
+    # 130 heads x 2 query tiles: above the tile count under which the dense
+    # forward splits each workgroup's keys over two wave groups (another
+    # order of additions)
+    B, H, N, d = 1, 130, 384, 64
     w = inputs.make_dense(B, H, N, N, d, "f16", "normal", causal, seed=4, cfg=143)
     do = inputs.make_grad_out(w, seed=4, cfg=143)
     q, k, v = (to_device(x, "f16") for x in (w.q, w.k, w.v))

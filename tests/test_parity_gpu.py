@@ -4,6 +4,7 @@ Tolerances are in tests/gpu_util.py.  Small shapes are compared in full;
 the large workloads are compared on whole sampled (batch, head) units or on
 sampled query rows that the oracle computes one by one.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -64,6 +65,31 @@ def test_d32_wide_grid(dtype, causal, n):
         o, lse = G.run(w, out_f32=out_f32)
         G.assert_parity(o, ref, dtype, f"wide {dtype} N{n} causal{causal} f32out{out_f32}",
                         lse, lref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_threshold_both_sides(dtype, d, causal):
+    """Plain grids of at most 128 query tiles of 256 rows (256 at d = 32 and
+    when causal) split each workgroup's keys over two wave groups that merge
+    their states; one tile more runs the one-group kernels.  The same ragged
+    units (N = 300, two tiles each) on both sides of the threshold, every
+    unit against the oracle, and the two results against each other."""
+    limit = 256 if (d == 32 or causal) else 128
+    H = limit // 2 + 1       # H x 2 tiles: one group; (H - 1) x 2 = limit: two
+    w = inputs.make_dense(1, H, 300, 300, d, dtype, "normal", causal, seed=d + causal, cfg=46)
+    ws = dataclasses.replace(w, H=H - 1, q=w.q[:, : H - 1].copy(), k=w.k[:, : H - 1].copy(),
+                             v=w.v[:, : H - 1].copy())
+    ref, lref = _dense_ref(w)
+    out_f32 = dtype == "bf16"
+    o1, l1 = G.run(w, out_f32=out_f32)
+    G.assert_parity(o1, ref, dtype, f"one group {dtype} d{d} causal{causal}", l1, lref)
+    o2, l2 = G.run(ws, out_f32=out_f32)
+    G.assert_parity(o2, ref[:, : H - 1], dtype, f"two groups {dtype} d{d} causal{causal}", l2,
+                    lref[:, : H - 1])
+    # the two orders of additions agree to fp32 rounding of O and lse
+    G.assert_parity(o2, o1[:, : H - 1], dtype, "two groups vs one", l2, l1[:, : H - 1])
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

@@ -46,6 +46,10 @@ VARIANTS = ["plain", "varlen", "block_sparse", "mask_bool", "mask_add", "mask_ad
 # until the grid has at least 2048 query tiles of 256 rows, which selects
 # the d = 32 kernels with two query blocks per wave
 WIDE_TILES = 2048
+# plain grids of at most 256 query tiles (of 256 rows) split each
+# workgroup's keys over two wave groups; a grid above that runs the
+# one-group kernels, which the small workloads here do not reach
+ONE_GROUP_TILES = 260
 
 # per family: (query rows = keys per unit, heads); ``rising`` spans > 2048 keys
 DENSE_N = {"late": (520, 2), "rising": (2090, 1), "low_first": (520, 2)}
@@ -69,11 +73,11 @@ def _check_empty_rows(o, lse, lref, what):
     return ~dead
 
 
-def _widen(w):
+def _widen(w, target=WIDE_TILES):
     """The workload's units repeated over the batch until the grid holds at
-    least WIDE_TILES query tiles; returns it and the repeat count."""
+    least `target` query tiles; returns it and the repeat count."""
     tiles = w.B * w.H * -(-w.Nq // 256)
-    rep = -(-WIDE_TILES // tiles)
+    rep = -(-target // tiles)
     for name in ("q", "k", "v"):
         setattr(w, name, np.ascontiguousarray(np.tile(getattr(w, name), (rep, 1, 1, 1))))
     w.B *= rep
@@ -81,12 +85,14 @@ def _widen(w):
 
 
 def _run_case(family, variant, dtype, d, causal):
-    seed = d + 3 * causal + 11 * (VARIANTS + ["wide"]).index(variant)
-    w = _workload(family, "plain" if variant == "wide" else variant, dtype, d, causal, seed)
+    seed = d + 3 * causal + 11 * (VARIANTS + ["wide", "one_group"]).index(variant)
+    widened = variant in ("wide", "one_group")
+    w = _workload(family, "plain" if widened else variant, dtype, d, causal, seed)
     rep = 1
-    if variant == "wide":
+    if widened:
         q64, k64, v64 = w.q64, w.k64, w.v64    # the unit set the oracle sees
-        w, rep = _widen(w)
+        w, rep = _widen(w, WIDE_TILES if variant == "wide" else ONE_GROUP_TILES)
+        assert variant == "wide" or w.B * w.H * -(-w.Nq // 256) < WIDE_TILES
     out_f32 = True
     what = f"{family} {variant} {dtype} d{d} causal={causal}"
     q, k, v = (G.to_device(x, dtype) for x in (w.q, w.k, w.v))
@@ -115,7 +121,7 @@ def _run_case(family, variant, dtype, d, causal):
 
     if variant == "plain":
         ref, lref = oracle.sdpa_fwd(w.q64, w.k64, w.v64, w.scale, causal)
-    elif variant == "wide":
+    elif widened:
         ref, lref = oracle.sdpa_fwd(q64, k64, v64, w.scale, causal)
         ref, lref = np.tile(ref, (rep, 1, 1, 1)), np.tile(lref, (rep, 1, 1))
     elif variant == "varlen":
@@ -165,3 +171,14 @@ def test_late_maximum_wide_grid(dtype, causal):
     print(f"rescale case {dtype} d32 causal={causal} wide", flush=True)
     for family in inputs.RESCALE_FAMILIES:
         _run_case(family, "wide", dtype, 32, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_late_maximum_one_group(dtype, d, causal):
+    """The plain workloads above run the two-group kernels (small grids);
+    the same units repeated past 256 query tiles run the one-group ones."""
+    print(f"rescale case {dtype} d{d} causal={causal} one_group", flush=True)
+    for family in inputs.RESCALE_FAMILIES:
+        _run_case(family, "one_group", dtype, d, causal)
