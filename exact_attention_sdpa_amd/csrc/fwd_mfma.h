@@ -809,9 +809,8 @@ struct MfmaFwd {
     const int grp = KS > 1 ? wave / NWG : 0;   // key group
     x.gtid = KS > 1 ? x.tid % NTG : x.tid;
     x.bb = KS > 1 ? 2 * grp : 0;
-    const int lane = x.tid % 64;
-    x.hl = lane / 32;
-    x.l32 = lane % 32;
+    x.hl = (x.tid >> 5) & 1;
+    x.l32 = x.tid & 31;
     x.c = p.c;
 
     // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
