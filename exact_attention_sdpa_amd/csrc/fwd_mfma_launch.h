@@ -69,8 +69,9 @@ template <> struct VarlenShape<128> : ShapeOf<SDPA_VARLEN_SHAPE_D128> {};
 // N2048 +66/69% at d = 32, +15/21% at d = 64, +33/36% at d = 128,
 // non-causal/causal; 256 tiles of 256 rows: d = 32 +16%, causal d = 64 and
 // 128 +13...19%, but non-causal d = 64 and 128 -9...25%, as do larger
-// grids).  Thresholds in query tiles of 256 rows (plain launches, dense or
-// packed):
+// grids).  With dropout (same kernels, keep decisions by position) B1 H16
+// N2048 gains +26/30%, +54/59% and +46/48%.  Thresholds in query tiles of
+// 256 rows (plain and dropout launches, dense or packed):
 #ifndef SDPA_SPLIT_TILES_D32
 #define SDPA_SPLIT_TILES_D32 256
 #endif
@@ -223,7 +224,24 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
 #undef SDPA_WCASE
     }
   }
+  // key groups for grids of few query tiles (B counts sequences and Nq is
+  // the longest one for packed batches)
+  const bool split = a.B * a.H * ((a.Nq + 255) / 256) <= kSplitTiles<D>(a.causal);
   if (a.dropout) {
+    if (split) {
+#define SDPA_SDCASE(C, V, O)                                                 \
+      if (a.causal == C && varlen == V && a.out_f32 == O)                    \
+        return launch_mfma_inst<BF16, D, C, V, O, kDropout, false, 2>(a);
+      SDPA_SDCASE(false, false, false)
+      SDPA_SDCASE(false, false, true)
+      SDPA_SDCASE(false, true, false)
+      SDPA_SDCASE(false, true, true)
+      SDPA_SDCASE(true, false, false)
+      SDPA_SDCASE(true, false, true)
+      SDPA_SDCASE(true, true, false)
+      SDPA_SDCASE(true, true, true)
+#undef SDPA_SDCASE
+    }
 #define SDPA_DCASE(C, V, O)                                                  \
     if (a.causal == C && varlen == V && a.out_f32 == O)                      \
       return launch_mfma_inst<BF16, D, C, V, O, kDropout>(a);
@@ -237,9 +255,7 @@ hipError_t launch_mfma_d(const FwdArgs& a) {
     SDPA_DCASE(true, true, true)
 #undef SDPA_DCASE
   }
-  // key groups for grids of few query tiles (B counts sequences and Nq is
-  // the longest one for packed batches)
-  if (a.B * a.H * ((a.Nq + 255) / 256) <= kSplitTiles<D>(a.causal)) {
+  if (split) {
 #define SDPA_SCASE(C, V, O)                                                  \
     if (a.causal == C && varlen == V && a.out_f32 == O)                      \
       return launch_mfma_inst<BF16, D, C, V, O, kPlain, false, 2>(a);

@@ -136,6 +136,25 @@ def test_same_seed_same_output_and_lse_matches_plain():
     assert np.array_equal(z[0], plain[0])
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_one_group_grid(dtype, d, causal):
+    """The small grids above run the dropout kernels that split each
+    workgroup's keys over two wave groups; 130 units of two query tiles
+    (N = 300) run the one-group ones, checked on sampled units plus the
+    first and last."""
+    B, H, n, p, seed, off = 1, 130, 300, 0.2, 77 + d, 4
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, d, dtype, "normal", causal, seed=d + causal, cfg=104)
+    o, lse = _run(w, p, seed=seed, offset=off, out_f32=dtype == "bf16")
+    for h in (0, 17, 64, H - 1):
+        ref, lref = odrop.attend_dropout(w.q64[0, h], w.k64[0, h], w.v64[0, h], w.scale, causal,
+                                         p, seed, off, h)
+        G.assert_parity(o[0, h] * (1 - p), ref * (1 - p), dtype, f"one group {dtype} d{d} head {h}",
+                        lse[0, h], lref)
+
+
 def test_module_training_workload_full_size():
     """The tutorial's CausalSelfAttention core in training (dropout 0.1,
     causal; B32 H8 N1024 d64 f16), checked on sampled (batch, head) units."""
