@@ -764,26 +764,32 @@ __device__ __forceinline__ uint32_t keep_bits_of_key(int q0, int key0, int l32, 
 }
 
 template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP = false,
-          bool VARLEN = false, int MK = kPlain>
+          bool VARLEN = false, int MK = kPlain, int KS = 1>
 struct BwdDkdv {
-  static constexpr int BK = NW * 32;
+  // KS query groups: the workgroup's waves form KS groups of NWG waves over
+  // the same keys; group g takes query tiles i0 + g, i0 + g + KS, ... and
+  // the groups' dK and dV partial sums are added at the end
+  static constexpr int NWG = NW / KS;
+  static constexpr int BK = NWG * 32;
   static constexpr int KB = BQ / 32;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int NT = NW * 64;
+  static constexpr int NTG = NWG * 64;   // threads of a query group (staging)
   static constexpr int NC = D / 8;
   static constexpr int KROW = D + 8;
   static constexpr int TW = BQ / 2 + 4;
   static constexpr int PAIRS = (BQ / 2) * NC;   // Q and dO: (2 rows x 16 bytes) tasks
-  static constexpr int PPT = (PAIRS + NT - 1) / NT;
-  static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NT, "shape");
+  static constexpr int PPT = (PAIRS + NTG - 1) / NTG;
+  static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NTG, "shape");
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK == kPlain), "query groups");
   // masks: the step's [BQ queries x BK keys] mask tile is staged through LDS
   // with the Q and dO rows (16-byte chunks, rows padded by 16 bytes)
   static constexpr bool HASM = MK >= kMaskBool;
   static constexpr int MEB = MK == kMaskBool ? 1 : MK == kMaskAdd ? 2 : 4;
   static constexpr int MROWB = BK * MEB + 16;            // LDS row, bytes
   static constexpr int MCPR = BK * MEB / 16;             // 16-byte chunks per row
-  static constexpr int MPT = HASM ? (BQ * MCPR + NT - 1) / NT : 1;
+  static constexpr int MPT = HASM ? (BQ * MCPR + NTG - 1) / NTG : 1;
 
   struct __attribute__((aligned(16))) Buf {
     uint16_t q[BQ * KROW];
@@ -795,8 +801,11 @@ struct BwdDkdv {
     uint32_t mk[HASM ? BQ * MROWB / 4 : 4];   // mask tile (masked kernels)
   };
   struct __attribute__((aligned(16))) Smem {
-    Buf b[2];
+    Buf b[2 * KS];
   };
+  // query groups: group 1's dK and dV (per lane) for the merge
+  static constexpr int MERGE_BYTES = KS > 1 ? NWG * 2 * DB * 16 * 64 * 4 : 0;
+  static_assert(MERGE_BYTES <= (int)sizeof(Smem), "merged sums fit in LDS");
   struct Regs {
     u32x4 q0[PPT], q1[PPT], g0[PPT], g1[PPT];
     u32x4 m[MPT];
@@ -804,8 +813,11 @@ struct BwdDkdv {
   };
 
   static __device__ void run(const BwdParams& p, Smem& sm) {
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int l32 = lane % 32, hl = lane / 32;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid & 63;
+    const int l32 = tid & 31, hl = (tid >> 5) & 1;
+    const int grp = KS > 1 ? wave / NWG : 0;      // query group
+    const int gtid = KS > 1 ? tid % NTG : tid;    // thread index within the group
+    const int bb = KS > 1 ? 2 * grp : 0;          // the group's first LDS buffer
     int kt, bh;
     if (CAUSAL && SDPA_BWD_CAUSAL_LPT) {   // the first key tiles are seen by the most queries
       bwd_causal_rank_of_block(p.total, p.n_tiles, bh, kt);
@@ -818,7 +830,7 @@ struct BwdDkdv {
     const int nq = un.nq, nk = un.nk;
     const int rs_bytes = un.rs * 2;
     const int64_t qoff = un.qoff, kvoff = un.kvoff;
-    const int k0 = kt * BK, k0w = k0 + wave * 32;
+    const int k0 = kt * BK, k0w = k0 + (KS > 1 ? wave % NWG : wave) * 32;
     if (VARLEN && k0 >= nk) return;   // whole workgroup: past the sequence end
     const int ki = k0w + l32;
     const int nqt = (nq + BQ - 1) / BQ;
@@ -843,7 +855,7 @@ struct BwdDkdv {
     int pg[PPT], pl[PPT], ptl[PPT], pc[PPT];
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int t = tid + i * NT;
+      const int t = gtid + i * NTG;
       const int pr = t % (BQ / 2), c = t / (BQ / 2);
       pg[i] = 2 * pr;
       pc[i] = c * 8;
@@ -857,7 +869,7 @@ struct BwdDkdv {
       const __amdgpu_buffer_rsrc_t gv = rows_rsrc(p.dout + qoff, r0, nq, rs_bytes, D);
 #pragma unroll
       for (int t = 0; t < PPT; ++t)
-        if (PAIRS % NT == 0 || tid + t * NT < PAIRS) {
+        if (PAIRS % NTG == 0 || gtid + t * NTG < PAIRS) {
           r.q0[t] = ld16(qv, pg[t], pc[t], rs_bytes);
           r.q1[t] = ld16(qv, pg[t] + 1, pc[t], rs_bytes);
           r.g0[t] = ld16(gv, pg[t], pc[t], rs_bytes);
@@ -866,16 +878,16 @@ struct BwdDkdv {
       if (HASM) {
 #pragma unroll
         for (int t = 0; t < MPT; ++t) {
-          const int c = tid + t * NT;
-          if ((BQ * MCPR) % NT == 0 || c < BQ * MCPR) {
+          const int c = gtid + t * NTG;
+          if ((BQ * MCPR) % NTG == 0 || c < BQ * MCPR) {
             const int row = c / MCPR, cc = c % MCPR;
             const int off = (r0 + row) * p.am_rs * MEB + k0 * MEB + cc * 16;
             r.m[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(mrs, off, 0, 0));
           }
         }
       }
-      if (tid < BQ) {
-        const int row = r0 + tid;
+      if (gtid < BQ) {
+        const int row = r0 + gtid;
         const bool ok = row < nq;
         const int64_t li = un.l0 + (int64_t)row * un.ls;
         // masks: a row that saw no key (lse = -inf) has P = 0 everywhere
@@ -886,10 +898,10 @@ struct BwdDkdv {
       }
     };
     auto store = [&](int buf, const Regs& r) {
-      Buf& b = sm.b[buf];
+      Buf& b = sm.b[bb + buf];
 #pragma unroll
       for (int t = 0; t < PPT; ++t)
-        if (PAIRS % NT == 0 || tid + t * NT < PAIRS) {
+        if (PAIRS % NTG == 0 || gtid + t * NTG < PAIRS) {
           *reinterpret_cast<u32x4*>(&b.q[pl[t]]) = r.q0[t];
           *reinterpret_cast<u32x4*>(&b.q[pl[t] + KROW]) = r.q1[t];
           *reinterpret_cast<u32x4*>(&b.g[pl[t]]) = r.g0[t];
@@ -897,15 +909,15 @@ struct BwdDkdv {
           store_pair_t(&b.qt[ptl[t]], TW, r.q0[t], r.q1[t]);
           store_pair_t(&b.gt[ptl[t]], TW, r.g0[t], r.g1[t]);
         }
-      if (tid < BQ) {
-        b.nl[tid] = r.l2;
-        b.nd[tid] = r.dd;
+      if (gtid < BQ) {
+        b.nl[gtid] = r.l2;
+        b.nd[gtid] = r.dd;
       }
       if (HASM) {
 #pragma unroll
         for (int t = 0; t < MPT; ++t) {
-          const int c = tid + t * NT;
-          if ((BQ * MCPR) % NT == 0 || c < BQ * MCPR) {
+          const int c = gtid + t * NTG;
+          if ((BQ * MCPR) % NTG == 0 || c < BQ * MCPR) {
             const int row = c / MCPR, cc = c % MCPR;
             *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(b.mk) + row * MROWB + cc * 16) = r.m[t];
           }
@@ -939,7 +951,7 @@ struct BwdDkdv {
       poison_whole_lds(sm, tid, NT);
       __syncthreads();
     }
-    int i = next_tile(i0);
+    int i = KS > 1 ? i0 + grp : next_tile(i0);
     if (i < nqt) {
       Regs r0;
       load(r0, i);
@@ -948,16 +960,19 @@ struct BwdDkdv {
     __syncthreads();
 
     const int ql = l32 * KROW + hl * 8;
-    for (int step = 0; i < nqt; ++step) {
+    // query groups: every group makes the same number of steps (one
+    // barrier each); a group past its last tile only waits at them
+    const int nsteps = KS > 1 ? (nqt - i0 + KS - 1) / KS : 0;
+    for (int step = 0; KS > 1 ? step < nsteps : i < nqt; ++step) {
       const int buf = step & 1;
       Regs rn;
-      const int in_ = next_tile(i + 1);
+      const int in_ = KS > 1 ? i + KS : next_tile(i + 1);
       const bool nxt = in_ < nqt;
       if (nxt) load(rn, in_);
       const int qb = i * BQ;
-      const bool live = !(CAUSAL && qb + BQ - 1 < k0w);
+      const bool live = (KS == 1 || i < nqt) && !(CAUSAL && qb + BQ - 1 < k0w);
       if (live) {
-        const Buf& b = sm.b[buf];
+        const Buf& b = sm.b[bb + buf];
         const bool masked = CAUSAL && qb < k0w + 31;
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
@@ -1059,7 +1074,35 @@ struct BwdDkdv {
       i = in_;
     }
     if (SDPA_LDS_POISON) __syncthreads();
-    static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dK, dV rows fit in LDS");
+    if constexpr (KS > 1) {
+      // query groups: group 1 hands its dK and dV sums to group 0 through
+      // LDS (every read of the Q/dO buffers ended at the last step's
+      // barrier); the second barrier ends the reads before group 0 stages
+      // its output rows over the same LDS
+      float* mg = reinterpret_cast<float*>(&sm) + (wave % NWG) * 2 * DB * 16 * 64 + lane;
+      if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            mg[(db * 16 + r) * 64] = dk[db][r];
+            mg[((DB + db) * 16 + r) * 64] = dv[db][r];
+          }
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dk[db][r] += mg[(db * 16 + r) * 64];
+            dv[db][r] += mg[((DB + db) * 16 + r) * 64];
+          }
+      }
+      __syncthreads();
+      if (grp != 0) return;
+    }
+    static_assert(NWG * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dK, dV rows fit in LDS");
     if (GF32 || MK != kPlain) {
       store_rows<BF16, GF32, DB>(p.dk, kvoff, un.rs, ki, nk, hl, dk, p.scale);
       store_rows<BF16, GF32, DB>(p.dv, kvoff, un.rs, ki, nk, hl, dv, 1.f);
@@ -1135,11 +1178,12 @@ constexpr int kBwdKvMaskWavesPerSimd =
     : D == 64      ? SDPA_BWD_KVM_WAVES_D64
                    : kBwdKvWavesPerSimd<D>;
 
+// query groups (8 waves): one workgroup per CU, 256 VGPRs
 template <bool BF16, int D, int NW, int BQ, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
-          int MK>
-__global__ __launch_bounds__(NW * 64, (DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvMaskWavesPerSimd<D, MK>))
+          int MK, int KS = 1>
+__global__ __launch_bounds__(NW * 64, (KS > 1 ? 2 : DROP ? kBwdKvDropWavesPerSimd<D> : kBwdKvMaskWavesPerSimd<D, MK>))
 void bwd_dkdv_kernel(BwdParams p) {
-  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN, MK>;
+  using K = BwdDkdv<BF16, D, NW, BQ, CAUSAL, GF32, DROP, VARLEN, MK, KS>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -44,6 +44,35 @@ template <int D, int MK>
 constexpr int kBwdKvRows =
     MK != kPlain ? 32 : D == 32 ? SDPA_BWD_KV_ROWS_D32 : D == 64 ? SDPA_BWD_KV_ROWS_D64 : 32;
 
+// dK/dV with two query groups on grids of few key tiles: 8 waves over
+// 128 keys, in two groups of 4 that take alternate query tiles and add
+// their sums at the end, so that small grids hold twice the waves.  The
+// thresholds count tiles of 256 rows over the keys, as the forward's do
+// over the queries.  Plain and dropout kernels of 4-wave workgroups at
+// d = 32 and 64 (at d = 128 an 8-wave workgroup spills 15-42 VGPRs even at
+// 2 waves per SIMD).  Measured (f16, one box, A/B): B1 H16 N2048 d = 64
+// +17/20% plain and +13/16% with dropout (non-causal/causal), d = 32 with
+// dropout +13/19%; causal grids of 256 tiles +9...17%; non-causal grids
+// of 256 tiles -8...-10% at d = 32 with dropout, hence 128 there.
+#ifndef SDPA_BWD_SPLIT_TILES_D32
+#define SDPA_BWD_SPLIT_TILES_D32 128
+#endif
+#ifndef SDPA_BWD_SPLIT_TILES_D64
+#define SDPA_BWD_SPLIT_TILES_D64 128
+#endif
+#ifndef SDPA_BWD_SPLIT_TILES_D128
+#define SDPA_BWD_SPLIT_TILES_D128 128
+#endif
+#ifndef SDPA_BWD_SPLIT_TILES_CAUSAL
+#define SDPA_BWD_SPLIT_TILES_CAUSAL 256
+#endif
+template <int D>
+constexpr int64_t kBwdSplitTiles(bool causal) {
+  return causal ? SDPA_BWD_SPLIT_TILES_CAUSAL
+                : D == 32 ? SDPA_BWD_SPLIT_TILES_D32
+                          : (D == 64 ? SDPA_BWD_SPLIT_TILES_D64 : SDPA_BWD_SPLIT_TILES_D128);
+}
+
 template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN, int MK = kPlain>
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   using Q = BwdDq<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
@@ -56,8 +85,18 @@ hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
-                     dim3(p.total), dim3(kBwdWaves<D, MK, DROP> * 64), 0, a.stream, p);
+  constexpr int NWK = kBwdWaves<D, MK, DROP>;
+  if constexpr (MK == kPlain && NWK == 4 && D != 128) {
+    if (a.B * a.H * ((a.Nk + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
+      using KV2 = BwdDkdv<BF16, D, 2 * NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
+      static_assert(KV2::BK == KV::BK, "same key tiles");
+      hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, 2 * NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
+                         dim3(p.total), dim3(2 * NWK * 64), 0, a.stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
+                     dim3(p.total), dim3(NWK * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 

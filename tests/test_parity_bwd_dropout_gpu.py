@@ -7,6 +7,8 @@ and the forward's O inside D) and z dP / (1 - p) in place of dP.  The
 dK/dV kernel moves the keep bits across lanes; with q = k = 0 and dO the
 identity, dV[j, i] = z_ij / ((1 - p) |A_i|) exposes them bit for bit.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -132,6 +134,24 @@ def test_transposed_keep_bits_are_exact(causal):
         assert np.array_equal(dvn[0, h].T > 0, want), f"head {h}"
         kept = np.where(want, 1.0 / ((1.0 - float(np.float32(p))) * cnt[:, None]), 0.0)
         np.testing.assert_allclose(dvn[0, h].T, kept, rtol=2e-3)
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_dropout_one_group_dkdv_grid(d, causal):
+    """The small grids above run the dK/dV dropout kernel with two query
+    groups; 130 units of two key tiles (N = 300) run the one-group kernel,
+    checked on the first four units (their keep masks are those of units
+    0..3) against the oracle."""
+    B, H, n, p, seed = 1, 130, 300, 0.2, 0x5EED + d
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=23 + causal, cfg=114)
+    do = inputs.make_grad_out(w, seed=23, cfg=114)
+    sub = dataclasses.replace(w, H=4, q=w.q[:, :4].copy(), k=w.k[:, :4].copy(),
+                              v=w.v[:, :4].copy())
+    got = _run(w, do, p, seed, offset=2)
+    _check([g[:, :4] for g in got], _ref_and_bound(sub, do[:, :4].copy(), p, seed, 2),
+           f"one group d{d} causal={causal}")
 
 
 def test_bwd_dropout_deterministic_and_p_zero_is_plain():

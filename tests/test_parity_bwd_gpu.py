@@ -27,6 +27,7 @@ the test allows twice the bound for fp32 accumulation and exp2.  Note the
 bound is relative to the sum of magnitudes, not to the result: dQ and dK are
 sums whose terms cancel (every row of dS sums to zero).
 """
+import dataclasses
 import types
 
 import numpy as np
@@ -184,6 +185,24 @@ def test_bwd_full_workload_sampled_units(cfg):
                                 is_causal=w.is_causal, q64=f64(w.q), k64=f64(w.k), v64=f64(w.v))
     _check([g[bi, hi][None] for g in got], _ref_and_bound(sub, do[bi, hi][None], grad_f32=False),
            f"{w.name} full size, sampled units")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_one_group_dkdv_grid(dtype, causal):
+    """The small grids above run the dK/dV kernel with two query groups that
+    add their sums; 130 units of two key tiles (N = 300, d = 64) run the
+    one-group kernel, checked on four units against the oracle."""
+    B, H, n = 1, 130, 300
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, 64, dtype, "normal", causal, seed=21 + causal, cfg=47)
+    do = inputs.make_grad_out(w, seed=21, cfg=47)
+    sub = dataclasses.replace(w, H=4, q=w.q[:, :4].copy(), k=w.k[:, :4].copy(),
+                              v=w.v[:, :4].copy())
+    for grad_f32 in (True, False):
+        got = _run(w, do, grad_f32=grad_f32)
+        _check([g[:, :4] for g in got], _ref_and_bound(sub, do[:, :4].copy(), grad_f32=grad_f32),
+               f"one group {dtype} causal={causal} f32grad={grad_f32}")
 
 
 def test_bwd_deterministic():
