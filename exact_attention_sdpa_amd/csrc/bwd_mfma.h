@@ -410,21 +410,27 @@ __device__ __forceinline__ void store_rows_lds(void* base, int64_t off0, int64_t
 
 // ---- dQ: one wave per 32 query rows, key tiles of BN rows streamed
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP = false,
-          bool VARLEN = false, int MK = kPlain>
+          bool VARLEN = false, int MK = kPlain, int KS = 1>
 struct BwdDq {
-  static constexpr int BM = NW * 32;
+  // KS key groups: the workgroup's waves form KS groups of NWG waves over
+  // the same query rows; group g takes key tiles g, g + KS, ... and the
+  // groups' dQ partial sums are added at the end
+  static constexpr int NWG = NW / KS;
+  static constexpr int BM = NWG * 32;
   static constexpr int KB = BN / 32;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int NT = NW * 64;
+  static constexpr int NTG = NWG * 64;          // threads of a key group (staging)
   static constexpr int NC = D / 8;
   static constexpr int KROW = D + 8;            // row-major LDS row, elements
   static constexpr int TW = BN / 2 + 4;         // transposed LDS row, words
   static constexpr int PAIRS = (BN / 2) * NC;   // K: (2 rows x 16 bytes) tasks
   static constexpr int VCH = BN * NC;           // V: 16-byte tasks
-  static constexpr int PPT = (PAIRS + NT - 1) / NT;
-  static constexpr int VPT = (VCH + NT - 1) / NT;
+  static constexpr int PPT = (PAIRS + NTG - 1) / NTG;
+  static constexpr int VPT = (VCH + NTG - 1) / NTG;
   static_assert(BN % 32 == 0 && D % 32 == 0, "shape");
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK == kPlain), "key groups");
 
   struct __attribute__((aligned(16))) Buf {
     uint16_t k[BN * KROW];
@@ -432,8 +438,11 @@ struct BwdDq {
     uint32_t kt[D * TW];   // K^T (input type), keys in vt_key_pos order
   };
   struct __attribute__((aligned(16))) Smem {
-    Buf b[2];
+    Buf b[2 * KS];
   };
+  // key groups: group 1's dQ sums (per lane) for the merge
+  static constexpr int MERGE_BYTES = KS > 1 ? NWG * DB * 16 * 64 * 4 : 0;
+  static_assert(MERGE_BYTES <= (int)sizeof(Smem), "merged sums fit in LDS");
   struct Regs {
     u32x4 k0[PPT], k1[PPT], v[VPT];
   };
@@ -442,8 +451,11 @@ struct BwdDq {
   };
 
   static __device__ void run(const BwdParams& p, Smem& sm) {
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int l32 = lane % 32, hl = lane / 32;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid & 63;
+    const int l32 = tid & 31, hl = (tid >> 5) & 1;
+    const int grp = KS > 1 ? wave / NWG : 0;      // key group
+    const int gtid = KS > 1 ? tid % NTG : tid;    // thread index within the group
+    const int bb = KS > 1 ? 2 * grp : 0;          // the group's first LDS buffer
     int qt, bh;
     if (CAUSAL && SDPA_BWD_CAUSAL_LPT) {   // the last query tiles see the most keys
       int rank;
@@ -458,7 +470,7 @@ struct BwdDq {
     const int nq = un.nq, nk = un.nk;
     const int rs_bytes = un.rs * 2;
     const int64_t qoff = un.qoff, kvoff = un.kvoff;
-    const int q0 = qt * BM, q0w = q0 + wave * 32;
+    const int q0 = qt * BM, q0w = q0 + (KS > 1 ? wave % NWG : wave) * 32;
     if (VARLEN && q0 >= nq) return;   // whole workgroup: past the sequence end
     const int kend = CAUSAL ? min(nk, q0 + BM) : nk;
     const int ntiles = (kend + BN - 1) / BN;
@@ -514,7 +526,8 @@ struct BwdDq {
         }
       }
       dd = pair_sum(part);
-      if (hl == 0 && qok) p.dsum[li] = dd;
+      // (key groups: both groups hold D of the same rows; group 0 writes it)
+      if (hl == 0 && qok && grp == 0) p.dsum[li] = dd;
     } else {
       dd = qok ? p.dsum[li] : 0.f;
     }
@@ -531,7 +544,7 @@ struct BwdDq {
     Stage st;
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int t = tid + i * NT;
+      const int t = gtid + i * NTG;
       const int pr = t % (BN / 2), c = t / (BN / 2);
       st.kg[i] = 2 * pr;
       st.kl[i] = 2 * pr * KROW + c * 8;
@@ -539,38 +552,38 @@ struct BwdDq {
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int t = tid + i * NT;
+      const int t = gtid + i * NTG;
       st.vg[i] = t / NC;
       st.vl[i] = (t / NC) * KROW + (t % NC) * 8;
     }
-    auto col_of_pair = [&](int i) { return ((tid + i * NT) / (BN / 2)) * 8; };
-    auto col_of_v = [&](int i) { return ((tid + i * NT) % NC) * 8; };
+    auto col_of_pair = [&](int i) { return ((gtid + i * NTG) / (BN / 2)) * 8; };
+    auto col_of_v = [&](int i) { return ((gtid + i * NTG) % NC) * 8; };
 
     auto load = [&](Regs& r, int j) {
       const __amdgpu_buffer_rsrc_t kr = rows_rsrc(p.k + kvoff, j * BN, nk, rs_bytes, D);
       const __amdgpu_buffer_rsrc_t vr = rows_rsrc(p.v + kvoff, j * BN, nk, rs_bytes, D);
 #pragma unroll
       for (int i = 0; i < PPT; ++i)
-        if (PAIRS % NT == 0 || tid + i * NT < PAIRS) {
+        if (PAIRS % NTG == 0 || gtid + i * NTG < PAIRS) {
           r.k0[i] = ld16(kr, st.kg[i], col_of_pair(i), rs_bytes);
           r.k1[i] = ld16(kr, st.kg[i] + 1, col_of_pair(i), rs_bytes);
         }
 #pragma unroll
       for (int i = 0; i < VPT; ++i)
-        if (VCH % NT == 0 || tid + i * NT < VCH) r.v[i] = ld16(vr, st.vg[i], col_of_v(i), rs_bytes);
+        if (VCH % NTG == 0 || gtid + i * NTG < VCH) r.v[i] = ld16(vr, st.vg[i], col_of_v(i), rs_bytes);
     };
     auto store = [&](int buf, const Regs& r) {
-      Buf& b = sm.b[buf];
+      Buf& b = sm.b[bb + buf];
 #pragma unroll
       for (int i = 0; i < PPT; ++i)
-        if (PAIRS % NT == 0 || tid + i * NT < PAIRS) {
+        if (PAIRS % NTG == 0 || gtid + i * NTG < PAIRS) {
           *reinterpret_cast<u32x4*>(&b.k[st.kl[i]]) = r.k0[i];
           *reinterpret_cast<u32x4*>(&b.k[st.kl[i] + KROW]) = r.k1[i];
           store_pair_t(&b.kt[st.kt[i]], TW, r.k0[i], r.k1[i]);
         }
 #pragma unroll
       for (int i = 0; i < VPT; ++i)
-        if (VCH % NT == 0 || tid + i * NT < VCH) *reinterpret_cast<u32x4*>(&b.v[st.vl[i]]) = r.v[i];
+        if (VCH % NTG == 0 || gtid + i * NTG < VCH) *reinterpret_cast<u32x4*>(&b.v[st.vl[i]]) = r.v[i];
     };
 
     f32x16 acc[DB];
@@ -599,7 +612,7 @@ struct BwdDq {
       poison_whole_lds(sm, tid, NT);
       __syncthreads();
     }
-    int j = next_tile(0);
+    int j = KS > 1 ? grp : next_tile(0);
     if (j < ntiles) {
       Regs r0;
       load(r0, j);
@@ -608,16 +621,19 @@ struct BwdDq {
     __syncthreads();
 
     const int kl = l32 * KROW + hl * 8;
-    for (int step = 0; j < ntiles; ++step) {
+    // key groups: every group makes the same number of steps (one barrier
+    // each); a group past its last tile only waits at them
+    const int nsteps = KS > 1 ? (ntiles + KS - 1) / KS : 0;
+    for (int step = 0; KS > 1 ? step < nsteps : j < ntiles; ++step) {
       const int buf = step & 1;
       Regs rn;
-      const int jn = next_tile(j + 1);
+      const int jn = KS > 1 ? j + KS : next_tile(j + 1);
       const bool nxt = jn < ntiles;
       if (nxt) load(rn, jn);
       const int kb = j * BN;
-      const bool live = !(CAUSAL && kb > q0w + 31);
+      const bool live = (KS == 1 || j < ntiles) && !(CAUSAL && kb > q0w + 31);
       if (live) {
-        const Buf& b = sm.b[buf];
+        const Buf& b = sm.b[bb + buf];
         const bool masked = (kb + BN > nk) || (CAUSAL && kb + BN - 1 > q0w);
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) {
@@ -704,7 +720,28 @@ struct BwdDq {
     // (debug poisoning: the last refills end before any wave stages its
     // gradient rows in LDS)
     if (SDPA_LDS_POISON) __syncthreads();
-    static_assert(NW * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dQ rows fit in LDS");
+    if constexpr (KS > 1) {
+      // key groups: group 1 hands its dQ sums to group 0 through LDS (every
+      // read of the K/V buffers ended at the last step's barrier); the
+      // second barrier ends the reads before group 0 stages its rows there
+      float* mg = reinterpret_cast<float*>(&sm) + (wave % NWG) * DB * 16 * 64 + lane;
+      if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mg[(db * 16 + r) * 64] = acc[db][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += mg[(db * 16 + r) * 64];
+      }
+      __syncthreads();
+      if (grp != 0) return;
+    }
+    static_assert(NWG * 32 * (D + 8) * 2 <= (int)sizeof(Smem), "dQ rows fit in LDS");
     // (the masked kernels keep direct stores: through LDS they measured
     // 5% slower on a key-padding mask)
     if (GF32 || MK != kPlain)
@@ -1135,11 +1172,12 @@ constexpr int kBwdDqWavesPerSimd =
 template <int D>
 constexpr int kBwdDqDropWavesPerSimd = D == 32 ? 4 : D == 64 ? 3 : 2;
 
+// key groups (8 waves): one workgroup per CU, 256 VGPRs
 template <bool BF16, int D, int NW, int BN, bool CAUSAL, bool GF32, bool DROP, bool VARLEN,
-          int MK>
-__global__ __launch_bounds__(NW * 64, (DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D, GF32, MK>))
+          int MK, int KS = 1>
+__global__ __launch_bounds__(NW * 64, (KS > 1 ? 2 : DROP ? kBwdDqDropWavesPerSimd<D> : kBwdDqWavesPerSimd<D, GF32, MK>))
 void bwd_dq_kernel(BwdParams p) {
-  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN, MK>;
+  using K = BwdDq<BF16, D, NW, BN, CAUSAL, GF32, DROP, VARLEN, MK, KS>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }

@@ -44,16 +44,18 @@ template <int D, int MK>
 constexpr int kBwdKvRows =
     MK != kPlain ? 32 : D == 32 ? SDPA_BWD_KV_ROWS_D32 : D == 64 ? SDPA_BWD_KV_ROWS_D64 : 32;
 
-// dK/dV with two query groups on grids of few key tiles: 8 waves over
-// 128 keys, in two groups of 4 that take alternate query tiles and add
-// their sums at the end, so that small grids hold twice the waves.  The
+// dQ and dK/dV with two groups of waves on grids of few tiles: 8 waves
+// over 128 query rows (dQ) or keys (dK/dV), in two groups of 4 that take
+// alternate key (query) tiles and add their sums at the end, so that small
+// grids hold twice the waves.  The
 // thresholds count tiles of 256 rows over the keys, as the forward's do
 // over the queries.  Plain and dropout kernels of 4-wave workgroups at
 // d = 32 and 64 (at d = 128 an 8-wave workgroup spills 15-42 VGPRs even at
-// 2 waves per SIMD).  Measured (f16, one box, A/B): B1 H16 N2048 d = 64
-// +17/20% plain and +13/16% with dropout (non-causal/causal), d = 32 with
-// dropout +13/19%; causal grids of 256 tiles +9...17%; non-causal grids
-// of 256 tiles -8...-10% at d = 32 with dropout, hence 128 there.
+// 2 waves per SIMD).  Measured on the whole backward (f16, one box, A/B):
+// B1 H16 N2048 d = 64 +26/30% plain and +21/25% with dropout
+// (non-causal/causal), d = 32 with dropout +22/29%; causal grids of 256
+// tiles +17...32%.  Non-causal grids of 256 tiles lost 8-10% at d = 32
+// with dropout (dK/dV split alone), hence 128 there.
 #ifndef SDPA_BWD_SPLIT_TILES_D32
 #define SDPA_BWD_SPLIT_TILES_D32 128
 #endif
@@ -77,16 +79,29 @@ template <bool BF16, int D, bool CAUSAL, bool GF32, bool DROP, bool VARLEN, int 
 hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   using Q = BwdDq<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   using KV = BwdDkdv<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
+  constexpr int NWK = kBwdWaves<D, MK, DROP>;
+  constexpr bool kCanSplit = MK == kPlain && NWK == 4 && D != 128;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
-                     dim3(p.total), dim3(kBwdWaves<D, MK, DROP> * 64), 0, a.stream, p);
+  bool dq_done = false;
+  if constexpr (kCanSplit) {
+    // dQ with two key groups over the same 128 query rows
+    if (a.B * a.H * ((a.Nq + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
+      using Q2 = BwdDq<BF16, D, 2 * NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
+      static_assert(Q2::BM == Q::BM, "same query tiles");
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2 * NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
+                         dim3(p.total), dim3(2 * NWK * 64), 0, a.stream, p);
+      dq_done = true;
+    }
+  }
+  if (!dq_done)
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
+                       dim3(p.total), dim3(NWK * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
   p.total = (int)(a.B * a.H * p.n_tiles);
-  constexpr int NWK = kBwdWaves<D, MK, DROP>;
-  if constexpr (MK == kPlain && NWK == 4 && D != 128) {
+  if constexpr (kCanSplit) {
     if (a.B * a.H * ((a.Nk + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
       using KV2 = BwdDkdv<BF16, D, 2 * NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
       static_assert(KV2::BK == KV::BK, "same key tiles");

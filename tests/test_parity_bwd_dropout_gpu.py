@@ -138,11 +138,11 @@ def test_transposed_keep_bits_are_exact(causal):
 
 @pytest.mark.parametrize("d", [32, 64])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_dropout_one_group_dkdv_grid(d, causal):
-    """The small grids above run the dK/dV dropout kernel with two query
-    groups; 130 units of two key tiles (N = 300) run the one-group kernel,
-    checked on the first four units (their keep masks are those of units
-    0..3) against the oracle."""
+def test_bwd_dropout_one_group_grid(d, causal):
+    """The small grids above run the dQ and dK/dV dropout kernels with two
+    groups of waves; 130 units of two tiles (N = 300) run the one-group
+    kernels, checked on the first four units (their keep masks are those of
+    units 0..3) against the oracle."""
     B, H, n, p, seed = 1, 130, 300, 0.2, 0x5EED + d
     assert B * H * -(-n // 256) > 256
     w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=23 + causal, cfg=114)

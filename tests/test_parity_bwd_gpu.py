@@ -189,10 +189,10 @@ def test_bwd_full_workload_sampled_units(cfg):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_one_group_dkdv_grid(dtype, causal):
-    """The small grids above run the dK/dV kernel with two query groups that
-    add their sums; 130 units of two key tiles (N = 300, d = 64) run the
-    one-group kernel, checked on four units against the oracle."""
+def test_bwd_one_group_grid(dtype, causal):
+    """The small grids above run the dQ and dK/dV kernels with two groups of
+    waves that add their sums; 130 units of two tiles (N = 300, d = 64) run
+    the one-group kernels, checked on four units against the oracle."""
     B, H, n = 1, 130, 300
     assert B * H * -(-n // 256) > 256
     w = inputs.make_dense(B, H, n, n, 64, dtype, "normal", causal, seed=21 + causal, cfg=47)
