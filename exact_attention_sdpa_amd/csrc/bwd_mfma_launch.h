@@ -51,7 +51,7 @@ constexpr int kBwdKvRows =
 // thresholds count tiles of 256 rows over the keys, as the forward's do
 // over the queries.  Plain and dropout kernels of 4-wave workgroups at
 // d = 32 and 64 (at d = 128 an 8-wave workgroup spills 15-42 VGPRs even at
-// 2 waves per SIMD).  Measured on the whole backward (f16, one box, A/B):
+// 2 waves per SIMD).  Measured on the whole backward (f16, one MI355X, A/B):
 // B1 H16 N2048 d = 64 +26/30% plain and +21/25% with dropout
 // (non-causal/causal), d = 32 with dropout +22/29%; causal grids of 256
 // tiles +17...32%.  Non-causal grids of 256 tiles lost 8-10% at d = 32

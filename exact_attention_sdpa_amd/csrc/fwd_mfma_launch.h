@@ -65,7 +65,7 @@ template <> struct VarlenShape<128> : ShapeOf<SDPA_VARLEN_SHAPE_D128> {};
 // two groups of 4 that take alternate key tiles and merge their states at
 // the end.  Against the 256-row shape a workgroup's chain of key steps is
 // half as long and the grid has twice the waves, which pays where that grid
-// would leave most CUs with one workgroup or none (f16, one box: B1 H16
+// would leave most CUs with one workgroup or none (f16, one MI355X: B1 H16
 // N2048 +66/69% at d = 32, +15/21% at d = 64, +33/36% at d = 128,
 // non-causal/causal; 256 tiles of 256 rows: d = 32 +16%, causal d = 64 and
 // 128 +13...19%, but non-causal d = 64 and 128 -9...25%, as do larger
