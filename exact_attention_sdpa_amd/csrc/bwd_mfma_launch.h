@@ -80,11 +80,14 @@ hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   using Q = BwdDq<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   using KV = BwdDkdv<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   constexpr int NWK = kBwdWaves<D, MK, DROP>;
-  constexpr bool kCanSplit = MK == kPlain && NWK == 4 && D != 128;
+  // (d = 128: the dQ kernel's two groups fit 2 waves per SIMD, the dK/dV
+  // kernel's do not)
+  constexpr bool kCanSplitDq = MK == kPlain && NWK == 4;
+  constexpr bool kCanSplit = kCanSplitDq && D != 128;
   p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
   p.total = (int)(a.B * a.H * p.n_tiles);
   bool dq_done = false;
-  if constexpr (kCanSplit) {
+  if constexpr (kCanSplitDq) {
     // dQ with two key groups over the same 128 query rows
     if (a.B * a.H * ((a.Nq + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
       using Q2 = BwdDq<BF16, D, 2 * NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;

@@ -188,21 +188,23 @@ def test_bwd_full_workload_sampled_units(cfg):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_one_group_grid(dtype, causal):
-    """The small grids above run the dQ and dK/dV kernels with two groups of
-    waves that add their sums; 130 units of two tiles (N = 300, d = 64) run
-    the one-group kernels, checked on four units against the oracle."""
+def test_bwd_one_group_grid(dtype, d, causal):
+    """The small grids above run the dQ (d = 64, 128) and dK/dV (d = 64)
+    kernels with two groups of waves that add their sums; 130 units of two
+    tiles (N = 300) run the one-group kernels, checked on four units against
+    the oracle."""
     B, H, n = 1, 130, 300
     assert B * H * -(-n // 256) > 256
-    w = inputs.make_dense(B, H, n, n, 64, dtype, "normal", causal, seed=21 + causal, cfg=47)
+    w = inputs.make_dense(B, H, n, n, d, dtype, "normal", causal, seed=21 + causal, cfg=47)
     do = inputs.make_grad_out(w, seed=21, cfg=47)
     sub = dataclasses.replace(w, H=4, q=w.q[:, :4].copy(), k=w.k[:, :4].copy(),
                               v=w.v[:, :4].copy())
     for grad_f32 in (True, False):
         got = _run(w, do, grad_f32=grad_f32)
         _check([g[:, :4] for g in got], _ref_and_bound(sub, do[:, :4].copy(), grad_f32=grad_f32),
-               f"one group {dtype} causal={causal} f32grad={grad_f32}")
+               f"one group {dtype} d{d} causal={causal} f32grad={grad_f32}")
 
 
 def test_bwd_deterministic():
