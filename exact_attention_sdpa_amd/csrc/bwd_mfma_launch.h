@@ -49,9 +49,9 @@ constexpr int kBwdKvRows =
 // alternate key (query) tiles and add their sums at the end, so that small
 // grids hold twice the waves.  The
 // thresholds count tiles of 256 rows over the keys, as the forward's do
-// over the queries.  Plain and dropout kernels of 4-wave workgroups at
-// d = 32 and 64 (at d = 128 an 8-wave workgroup spills 15-42 VGPRs even at
-// 2 waves per SIMD).  Measured on the whole backward (f16, one MI355X, A/B):
+// over the queries.  Plain and dropout kernels (unmasked) at d = 32 and 64,
+// and dQ at d = 128 (there an 8-wave dK/dV workgroup spills 15-42 VGPRs
+// even at 2 waves per SIMD).  Measured on the whole backward (f16, one MI355X, A/B):
 // B1 H16 N2048 d = 64 +26/30% plain and +21/25% with dropout
 // (non-causal/causal), d = 32 with dropout +22/29%; causal grids of 256
 // tiles +17...32%.  Non-causal grids of 256 tiles lost 8-10% at d = 32
@@ -80,39 +80,44 @@ hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   using Q = BwdDq<BF16, D, kBwdWaves<D, MK, DROP>, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   using KV = BwdDkdv<BF16, D, kBwdWaves<D, MK, DROP>, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>;
   constexpr int NWK = kBwdWaves<D, MK, DROP>;
-  // (d = 128: the dQ kernel's two groups fit 2 waves per SIMD, the dK/dV
-  // kernel's do not)
-  constexpr bool kCanSplitDq = MK == kPlain && NWK == 4;
+  // the split kernels: 8 waves in two groups of 4 (128 rows or keys per
+  // workgroup; the 8-wave d = 32 kernels cover 256, so their split grid has
+  // twice the workgroups).  d = 128: the dQ kernel's two groups fit 2
+  // waves per SIMD, the dK/dV kernel's do not.
+  constexpr bool kCanSplitDq = MK == kPlain;
   constexpr bool kCanSplit = kCanSplitDq && D != 128;
-  p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
-  p.total = (int)(a.B * a.H * p.n_tiles);
   bool dq_done = false;
   if constexpr (kCanSplitDq) {
     // dQ with two key groups over the same 128 query rows
     if (a.B * a.H * ((a.Nq + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
-      using Q2 = BwdDq<BF16, D, 2 * NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
-      static_assert(Q2::BM == Q::BM, "same query tiles");
-      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 2 * NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
-                         dim3(p.total), dim3(2 * NWK * 64), 0, a.stream, p);
+      using Q2 = BwdDq<BF16, D, 8, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
+      p.n_tiles = (int)((a.Nq + Q2::BM - 1) / Q2::BM);
+      p.total = (int)(a.B * a.H * p.n_tiles);
+      hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, 8, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
+                         dim3(p.total), dim3(8 * 64), 0, a.stream, p);
       dq_done = true;
     }
   }
-  if (!dq_done)
+  if (!dq_done) {
+    p.n_tiles = (int)((a.Nq + Q::BM - 1) / Q::BM);
+    p.total = (int)(a.B * a.H * p.n_tiles);
     hipLaunchKernelGGL((bwd_dq_kernel<BF16, D, NWK, kBwdDqKeys<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
                        dim3(p.total), dim3(NWK * 64), 0, a.stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
-  p.total = (int)(a.B * a.H * p.n_tiles);
   if constexpr (kCanSplit) {
     if (a.B * a.H * ((a.Nk + 255) / 256) <= kBwdSplitTiles<D>(CAUSAL)) {
-      using KV2 = BwdDkdv<BF16, D, 2 * NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
-      static_assert(KV2::BK == KV::BK, "same key tiles");
-      hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, 2 * NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
-                         dim3(p.total), dim3(2 * NWK * 64), 0, a.stream, p);
+      using KV2 = BwdDkdv<BF16, D, 8, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>;
+      p.n_tiles = (int)((a.Nk + KV2::BK - 1) / KV2::BK);
+      p.total = (int)(a.B * a.H * p.n_tiles);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, 8, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK, 2>),
+                         dim3(p.total), dim3(8 * 64), 0, a.stream, p);
       return hipGetLastError();
     }
   }
+  p.n_tiles = (int)((a.Nk + KV::BK - 1) / KV::BK);
+  p.total = (int)(a.B * a.H * p.n_tiles);
   hipLaunchKernelGGL((bwd_dkdv_kernel<BF16, D, NWK, kBwdKvRows<D, MK>, CAUSAL, GF32, DROP, VARLEN, MK>),
                      dim3(p.total), dim3(NWK * 64), 0, a.stream, p);
   return hipGetLastError();

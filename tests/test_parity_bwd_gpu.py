@@ -188,11 +188,11 @@ def test_bwd_full_workload_sampled_units(cfg):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_one_group_grid(dtype, d, causal):
-    """The small grids above run the dQ (d = 64, 128) and dK/dV (d = 64)
-    kernels with two groups of waves that add their sums; 130 units of two
+    """The small grids above run the dQ and dK/dV kernels (dQ only at
+    d = 128) with two groups of waves that add their sums; 130 units of two
     tiles (N = 300) run the one-group kernels, checked on four units against
     the oracle."""
     B, H, n = 1, 130, 300
