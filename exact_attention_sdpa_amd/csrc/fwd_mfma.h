@@ -232,7 +232,9 @@ struct MfmaFwd {
   static constexpr int VPAIRS = (BN / 2) * NC;   // (2 rows x 16 bytes) V chunks
   static constexpr int KPT = (KCHUNKS + NTG - 1) / NTG;
   static constexpr int VPT = (VPAIRS + NTG - 1) / NTG;
-  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && (VAR == kPlain || VAR == kDropout)),
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 &&
+                            (VAR == kPlain || VAR == kDropout || VAR == kMaskBool ||
+                             VAR == kMaskAdd || VAR == kMaskAddF32)),
                 "key groups");
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(BN % 32 == 0 && BN <= 128, "key block");
@@ -1005,8 +1007,11 @@ struct MfmaFwd {
           const float* e = mg + qb * MITEMS * 64;
           const float m1 = e[(16 * DB) * 64], l1 = e[(16 * DB + 1) * 64];
           const float m = fmaxf(S.m[qb], m1);
-          const float a0 = __builtin_amdgcn_exp2f(S.m[qb] - m);
-          const float a1 = __builtin_amdgcn_exp2f(m1 - m);
+          // masks: a group in which the row saw no key has m = -inf and
+          // nothing to add (both: the row stays empty, m = -inf)
+          const float a0 = (MASK && S.m[qb] == -INFINITY) ? 0.f
+                                                          : __builtin_amdgcn_exp2f(S.m[qb] - m);
+          const float a1 = (MASK && m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
           S.m[qb] = m;
           S.l[qb] = S.l[qb] * a0 + l1 * a1;
 #pragma unroll

@@ -73,6 +73,41 @@ def test_full_mask(dtype, d, causal, kind):
            f"{dtype} d{d} causal={causal} {kind}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["bool", "add", "add_f32"])
+def test_masked_one_group_grid(d, causal, kind):
+    """The small grids above run the masked kernels with two key groups that
+    merge their states; 130 units of two query tiles (N = 300) run the
+    one-group ones, checked on sampled units (with their empty rows).  The
+    output is f32: mask biases put a row's weight on few keys, so |O| reaches
+    about 4.7, where one f16 rounding of the output alone is 2.3e-3, above
+    the max-abs bound; f32 leaves the kernel's own arithmetic measured."""
+    B, H, n = 1, 130, 300
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=d + causal, cfg=53)
+    mk = "bool" if kind == "bool" else "add"
+    mdt = "f32" if kind == "add_f32" else "f16"
+    m = inputs.make_attn_mask((B, H, n, n), mk, keep=0.8, seed=d + 5 * causal, cfg=54, dtype=mdt)
+    q, k, v = (G.to_device(x, "f16") for x in (w.q, w.k, w.v))
+    out, lse = sdpa.scaled_dot_product_attention(q, k, v, attn_mask=_mask_tensor(m, kind, mdt),
+                                                 is_causal=causal, scale=float(w.scale),
+                                                 out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    o, l = out.double().cpu().numpy(), lse.double().cpu().numpy()
+    for h in (0, 17, 64, H - 1):
+        sl = lambda x: x[:, h:h + 1]
+        m64, _ = _mask64(sl(m), kind, mdt)
+        ref, lref = oracle.sdpa_fwd_masked(sl(w.q64), sl(w.k64), sl(w.v64), m64, mk, w.scale,
+                                           causal)
+        what = f"one group d{d} causal={causal} {kind} head {h}"
+        dead = np.isneginf(lref)
+        assert np.array_equal(np.isneginf(sl(l)), dead), f"{what}: empty rows differ"
+        assert np.all(sl(o)[dead] == 0.0), f"{what}: empty rows not zero"
+        G.assert_parity(sl(o), ref, "f16", what, np.where(dead, 0.0, sl(l)),
+                        np.where(dead, 0.0, lref))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 260, 256), (2, 1, 1, 256), (1, 3, 260, 256),
                                    (2, 3, 1, 256), (260, 256), (256,)])
 @pytest.mark.parametrize("kind", ["bool", "add"])
