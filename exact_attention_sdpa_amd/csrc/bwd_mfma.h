@@ -430,7 +430,7 @@ struct BwdDq {
   static constexpr int PPT = (PAIRS + NTG - 1) / NTG;
   static constexpr int VPT = (VCH + NTG - 1) / NTG;
   static_assert(BN % 32 == 0 && D % 32 == 0, "shape");
-  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK == kPlain), "key groups");
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK != kBlockSparse), "key groups");
 
   struct __attribute__((aligned(16))) Buf {
     uint16_t k[BN * KROW];
@@ -819,7 +819,7 @@ struct BwdDkdv {
   static constexpr int PAIRS = (BQ / 2) * NC;   // Q and dO: (2 rows x 16 bytes) tasks
   static constexpr int PPT = (PAIRS + NTG - 1) / NTG;
   static_assert(BQ % 32 == 0 && D % 32 == 0 && BQ <= NTG, "shape");
-  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK == kPlain), "query groups");
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && MK != kBlockSparse), "query groups");
   // masks: the step's [BQ queries x BK keys] mask tile is staged through LDS
   // with the Q and dO rows (16-byte chunks, rows padded by 16 bytes)
   static constexpr bool HASM = MK >= kMaskBool;
@@ -1044,7 +1044,7 @@ struct BwdDkdv {
           // masks: add the bias in the units of s (the exponent is c s)
           if (MK >= kMaskBool) {
             // the lane's key column of the staged mask tile, its 16 rows
-            const char* mcol = reinterpret_cast<const char*>(b.mk) + (wave * 32 + l32) * MEB;
+            const char* mcol = reinterpret_cast<const char*>(b.mk) + (k0w - k0 + l32) * MEB;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int row = kk * 32 + 8 * (r / 4) + 4 * hl + (r % 4);

@@ -10,6 +10,7 @@ every visible pair (a masked pair's P is an exact 0).  Masks make such
 pairs common enough to matter: a key that only one row sees keeps a tiny P
 unaveraged.
 """
+import dataclasses
 import types
 
 import numpy as np
@@ -127,6 +128,27 @@ def test_bwd_masked_full_workload_sampled_units(cfg):
     msub = m[bi, [h % m.shape[1] for h in hi]][None]
     _check(sub, [g[bi, hi][None] for g in got], do[bi, hi][None], msub, kind, w.dtype,
            grad_f32=False)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["bool", "add_f32"])
+def test_bwd_masked_one_group_grid(d, causal, kind):
+    """The small grids above run the masked dQ and dK/dV kernels (dQ only at
+    d = 128) with two groups of waves; 130 units of two tiles (N = 300) run
+    the one-group ones, checked on four units against the oracle."""
+    B, H, n = 1, 130, 300
+    assert B * H * -(-n // 256) > 256
+    mk = "bool" if kind == "bool" else "add"
+    mdt = "f32" if kind == "add_f32" else "f16"
+    w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=d + causal, cfg=138)
+    do = inputs.make_grad_out(w, seed=d, cfg=138)
+    m = inputs.make_attn_mask((B, H, n, n), mk, keep=0.85, seed=d + 3 * causal, cfg=139,
+                              dtype=mdt)
+    got = _run(w, do, _mask_t(m, mk, mdt))
+    sub = dataclasses.replace(w, H=4, q=w.q[:, :4].copy(), k=w.k[:, :4].copy(),
+                              v=w.v[:, :4].copy())
+    _check(sub, [g[:, :4] for g in got], do[:, :4].copy(), m[:, :4].copy(), mk, mdt)
 
 
 @pytest.mark.parametrize("shape", [(2, 1, 1, 256), (1, 3, 200, 256), (200, 256)])
