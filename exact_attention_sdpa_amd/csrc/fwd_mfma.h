@@ -232,10 +232,7 @@ struct MfmaFwd {
   static constexpr int VPAIRS = (BN / 2) * NC;   // (2 rows x 16 bytes) V chunks
   static constexpr int KPT = (KCHUNKS + NTG - 1) / NTG;
   static constexpr int VPT = (VPAIRS + NTG - 1) / NTG;
-  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 &&
-                            (VAR == kPlain || VAR == kDropout || VAR == kMaskBool ||
-                             VAR == kMaskAdd || VAR == kMaskAddF32)),
-                "key groups");
+  static_assert(KS == 1 || (KS == 2 && NW % 2 == 0 && !BSP), "key groups");
   static_assert(D % 32 == 0 && D <= 128, "head dim");
   static_assert(BN % 32 == 0 && BN <= 128, "key block");
   // block-sparse: a workgroup's rows are exactly one mask row, and a key

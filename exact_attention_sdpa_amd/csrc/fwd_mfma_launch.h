@@ -325,6 +325,22 @@ hipError_t launch_mfma_masked_d(const FwdArgs& a) {
 template <bool BF16, int D>
 hipError_t launch_mfma_masked_drop_d(const FwdArgs& a) {
   if (a.cu != nullptr || a.amask == nullptr || !a.dropout) return hipErrorInvalidValue;
+  // key groups for grids of few query tiles, as for the plain launches
+  if (a.B * a.H * ((a.Nq + 255) / 256) <= kSplitTiles<D>(a.causal)) {
+#define SDPA_MSCASE(KIND, VAR)                                                                 \
+    if (a.amask_kind == KIND) {                                                               \
+      if (a.causal)                                                                           \
+        return a.out_f32 ? launch_mfma_inst<BF16, D, true, false, true, VAR, false, 2>(a)     \
+                         : launch_mfma_inst<BF16, D, true, false, false, VAR, false, 2>(a);   \
+      return a.out_f32 ? launch_mfma_inst<BF16, D, false, false, true, VAR, false, 2>(a)      \
+                       : launch_mfma_inst<BF16, D, false, false, false, VAR, false, 2>(a);    \
+    }
+    SDPA_MSCASE(SDPA_MASK_BOOL, kMaskBoolDrop)
+    SDPA_MSCASE(SDPA_MASK_ADD, kMaskAddDrop)
+    SDPA_MSCASE(SDPA_MASK_ADD_F32, kMaskAddF32Drop)
+#undef SDPA_MSCASE
+    return hipErrorInvalidValue;
+  }
   SDPA_MCASE(SDPA_MASK_BOOL, kMaskBoolDrop)
   SDPA_MCASE(SDPA_MASK_ADD, kMaskAddDrop)
   SDPA_MCASE(SDPA_MASK_ADD_F32, kMaskAddF32Drop)

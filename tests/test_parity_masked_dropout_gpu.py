@@ -71,6 +71,30 @@ def test_forward(dtype, d, causal, kind):
                     np.where(dead, 0.0, l), np.where(dead, 0.0, lref))
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_forward_one_group_grid(d, causal, kind):
+    """The small grids above run the kernels that split each workgroup's
+    keys over two wave groups; 130 units of two query tiles (N = 300) run
+    the one-group ones, checked on the first four units (their keep
+    decisions are those of units 0..3)."""
+    B, H, n = 1, 130, 300
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=d + causal, cfg=155)
+    mt, m64, mk = _mask(kind, "f16", (B, H, n, n), seed=d, cfg=155, keep=0.85)
+    out, lse = _fwd(w, mt, out_f32=True)
+    sl = lambda x: x[:, :4]
+    ref, lref = odrop.sdpa_fwd_masked_dropout(sl(w.q64), sl(w.k64), sl(w.v64), sl(m64), mk,
+                                              w.scale, causal, P_DROP, SEED, OFF)
+    o, l = sl(out.double().cpu().numpy()), sl(lse.double().cpu().numpy())
+    dead = np.isneginf(lref)
+    assert np.array_equal(np.isneginf(l), dead)
+    assert np.all(o[dead] == 0.0)
+    G.assert_parity(o, ref, "f16", f"one group d{d} causal={causal} {kind}",
+                    np.where(dead, 0.0, l), np.where(dead, 0.0, lref))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_mask_and_keep_decisions_are_exact(causal):
     """q = 0, V = identity, a boolean mask: O_ij = m_ij z_ij / (kappa |A_i|)."""
