@@ -84,7 +84,7 @@ hipError_t launch_bwd_tiles(const BwdArgs& a, BwdParams p) {
   // workgroup; the 8-wave d = 32 kernels cover 256, so their split grid has
   // twice the workgroups).  d = 128: the dQ kernel's two groups fit 2
   // waves per SIMD, the dK/dV kernel's do not.
-  constexpr bool kCanSplitDq = MK == kPlain || (!DROP && MK != kBlockSparse);
+  constexpr bool kCanSplitDq = MK != kBlockSparse;
   constexpr bool kCanSplit = kCanSplitDq && D != 128;
   bool dq_done = false;
   if constexpr (kCanSplitDq) {

@@ -15,6 +15,8 @@ pair's position) and divides kept weights by the keep probability.
 * Backward: the elementwise bound of tests/test_parity_bwd_dropout_gpu.py
   with P the masked softmax.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -138,7 +140,10 @@ E_LSE = 1e-4
 U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -24}
 
 
-def _bwd_check(w, do, mt, m64, mk, what):
+def _bwd_check(w, do, mt, m64, mk, what, first_heads=None):
+    """With first_heads = n (B = 1), the GPU runs every unit and the oracle
+    checks units 0..n-1 (whose keep decisions are those of units 0..n-1 of a
+    workload of n heads)."""
     q, k, v = (G.to_device(x, w.dtype) for x in (w.q, w.k, w.v))
     g = G.to_device(do, w.dtype)
     out, lse = sdpa.scaled_dot_product_attention(
@@ -151,6 +156,12 @@ def _bwd_check(w, do, mt, m64, mk, what):
         attn_mask=mt)
     torch.cuda.synchronize()
     got = [t.double().cpu().numpy() for t in got]
+    if first_heads is not None:
+        n = first_heads
+        got = [t[:, :n] for t in got]
+        do, m64 = do[:, :n], m64[:, :n]
+        w = dataclasses.replace(w, H=n, q=w.q[:, :n].copy(), k=w.k[:, :n].copy(),
+                                v=w.v[:, :n].copy())
     do64 = inputs.storage_to_f64(do, w.dtype)
     sc = float(w.scale)
     ref = ograd.sdpa_bwd_masked_dropout(w.q64, w.k64, w.v64, do64, m64, mk, sc, w.is_causal,
@@ -199,6 +210,21 @@ def test_backward(dtype, d, causal, kind):
     do = inputs.make_grad_out(w, seed=d, cfg=153)
     mt, m64, mk = _mask(kind, dtype, (B, H, Nq, Nk), seed=d, cfg=153)
     _bwd_check(w, do, mt, m64, mk, f"{dtype} d{d} causal={causal} {kind}")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("kind", ["bool", "add"])
+def test_backward_one_group_grid(d, causal, kind):
+    """The small grids above run the backward kernels split over two groups
+    of waves (dQ only at d = 128); 130 units of two tiles (N = 300) run the
+    one-group ones, checked on the first four units."""
+    B, H, n = 1, 130, 300
+    assert B * H * -(-n // 256) > 256
+    w = inputs.make_dense(B, H, n, n, d, "f16", "normal", causal, seed=d + causal, cfg=156)
+    do = inputs.make_grad_out(w, seed=d, cfg=156)
+    mt, m64, mk = _mask(kind, "f16", (B, H, n, n), seed=d, cfg=156, keep=0.85)
+    _bwd_check(w, do, mt, m64, mk, f"one group d{d} causal={causal} {kind}", first_heads=4)
 
 
 def test_backward_f32_mask_and_autograd():
