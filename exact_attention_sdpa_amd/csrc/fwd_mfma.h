@@ -815,8 +815,9 @@ struct MfmaFwd {
 
     // ---- which tile: XCD-contiguous ranges; causal: heaviest tiles first
     int qt, bh;
-    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles <= 16) {
-      // causal, short sequences: every head's heaviest query tiles first,
+    if (CAUSAL && !VARLEN && SDPA_CAUSAL_LPT && p.n_qtiles * BM <= 16 * 256) {
+      // causal, short sequences (at most 4096 rows): every head's heaviest
+      // query tiles first,
       // then the next heaviest of every head, ... (longest-processing-time
       // order, which shortens the tail when many heads have few tiles);
       // each XCD keeps its own eighth of the heads when the head count
